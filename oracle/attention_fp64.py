@@ -1,0 +1,250 @@
+"""Plain fp64 CPU oracle for exact scaled-dot-product attention (forward and backward).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or run this
+module: only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it.  It shares no code with the HIP kernels and never reads anything
+they produce except to compare against it.
+
+What it computes is the plain definition, written out and materialised (no tiling, no
+online softmax, no blocking):
+
+* Attention is ``softmax(Q @ K^T * softmax_scale) @ V`` with ``softmax_scale``
+  defaulting to ``1/sqrt(headdim)``  -- FlashAttention (Dao-AILab/flash-attention
+  README), section "How to use FlashAttention", the ``flash_attn_func`` docstring.
+* Layouts ``q: (batch, seqlen, nheads, headdim)``, ``k, v: (batch, seqlen, nheads_k,
+  headdim)``; query head ``h`` reads KV head ``h // (nheads // nheads_k)`` (6 query heads
+  over 2 KV heads: 0,1,2 -> 0 and 3,4,5 -> 1) -- same docstring, MQA/GQA paragraph.
+* The causal mask is aligned to the bottom-right corner of the score matrix: key ``j``
+  is kept for query ``i`` iff ``j <= i + seqlen_k - seqlen_q``; a query row whose mask
+  row is all zero produces an all-zero output -- same README, the
+  ``flash_attn_with_kvcache`` docstring and changelog entry 2.1.
+* The softmax log-sum-exp (LSE) is returned by the low-level ops -- the
+  kernels-community/flash-attn2 repository card, section "Low-level ops".  Its base is
+  the natural log of ``sum_j exp(scale * s_ij)``: the backward of the release notes
+  "v1.4 - FlashAttention Fork: 2.9.0 -> 2.9.1", section 4.1 (``scale_apply_exp2`` with
+  ``Scale_max=false``), multiplies the stored value by log2(e) before using it as an
+  exp2 offset, which fixes natural-log units.
+* The backward is the analytic gradient of the same definition: with
+  ``P = softmax(S)``, ``dV = P^T dO``, ``dP = dO V^T``, ``Dsum_i = sum_d dO_id O_id``
+  (which equals ``sum_j P_ij dP_ij``), ``dS = P * (dP - Dsum)``, ``dQ = scale dS K``,
+  ``dK = scale dS^T Q``.  For GQA the gradients of a KV head sum over the query heads
+  that read it.
+
+Readings taken where the pages are silent (each also listed in the design notes):
+
+* A fully masked query row gets ``O = 0`` (printed) and ``LSE = +inf`` (so that
+  ``exp(s - LSE) = 0`` when the backward recomputes probabilities); its gradients are 0.
+* Variable-length ("varlen") packed batches: sequence ``b`` occupies rows
+  ``[cu_seqlens[b], cu_seqlens[b+1])`` of the packed ``(total, nheads, headdim)`` arrays
+  and is attended independently; the LSE is laid out ``(nheads, total_q)``.  In padded
+  mode the LSE is ``(batch, nheads, seqlen_q)``.
+
+All arithmetic is numpy float64.  Inputs of any float dtype are upcast exactly.
+"""
+
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "causal_keep_mask",
+    "head_probabilities",
+    "head_forward",
+    "head_backward",
+    "forward",
+    "backward",
+]
+
+
+def kv_head_of(h: int, n_heads_q: int, n_heads_kv: int) -> int:
+    """KV head read by query head ``h``: contiguous groups of ``n_heads_q // n_heads_kv``
+    query heads share one KV head (flash_attn_func docstring, MQA/GQA paragraph)."""
+    if n_heads_q % n_heads_kv != 0:
+        raise ValueError("number of query heads must be divisible by number of KV heads")
+    return h // (n_heads_q // n_heads_kv)
+
+
+def causal_keep_mask(len_q: int, len_k: int, causal: bool) -> np.ndarray:
+    """Boolean (len_q, len_k) matrix, True where key j is kept for query i.
+
+    Bottom-right alignment: keep iff ``j <= i + len_k - len_q`` (flash_attn_with_kvcache
+    docstring; changelog entry 2.1 of the FlashAttention README)."""
+    i = np.arange(len_q)[:, None]
+    j = np.arange(len_k)[None, :]
+    if not causal:
+        return np.ones((len_q, len_k), dtype=bool)
+    return j <= i + (len_k - len_q)
+
+
+def head_probabilities(q: np.ndarray, k: np.ndarray, scale: float, causal: bool):
+    """Materialised softmax of one head.  Returns (P, LSE, keep) in float64.
+
+    ``S = scale * q k^T``; masked entries are excluded; rows with no kept key have
+    P = 0 and LSE = +inf."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    s = scale * (q @ k.T)
+    keep = causal_keep_mask(q.shape[0], k.shape[0], causal)
+    s = np.where(keep, s, -np.inf)
+    live = keep.any(axis=1)
+    m = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
+    e = np.where(keep, np.exp(s - m[:, None]), 0.0)
+    z = e.sum(axis=1)
+    p = np.zeros_like(e)
+    p[live] = e[live] / z[live, None]
+    lse = np.full(q.shape[0], np.inf)
+    lse[live] = m[live] + np.log(z[live])
+    return p, lse, keep
+
+
+def head_forward(q, k, v, scale: float, causal: bool):
+    """One head: O = P V (float64, (len_q, D)) and LSE ((len_q,))."""
+    p, lse, _ = head_probabilities(q, k, scale, causal)
+    o = p @ np.asarray(v, dtype=np.float64)
+    return o, lse
+
+
+def head_backward(q, k, v, do, scale: float, causal: bool):
+    """One head: analytic gradients (dq, dk, dv) of O = softmax(scale q k^T) v w.r.t.
+    q, k, v for the upstream gradient ``do``.  Probabilities are recomputed here from
+    the definition; nothing from a forward pass is reused."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    p, _, _ = head_probabilities(q, k, scale, causal)
+    o = p @ v
+    dv = p.T @ do
+    dp = do @ v.T
+    dsum = (do * o).sum(axis=1)
+    ds = p * (dp - dsum[:, None])
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def _sequences(batch: int, seqlen: int, cu_seqlens):
+    """List of (row_start, length) per sequence, padded or packed."""
+    if cu_seqlens is None:
+        return [(b * seqlen, seqlen) for b in range(batch)]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return [(int(cu[b]), int(cu[b + 1] - cu[b])) for b in range(len(cu) - 1)]
+
+
+def _check(q, k, v, cu_q, cu_k):
+    if (cu_q is None) != (cu_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    varlen = cu_q is not None
+    if varlen:
+        if q.ndim != 3 or k.ndim != 3 or v.ndim != 3:
+            raise ValueError("varlen inputs are (total, heads, headdim)")
+    elif q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("padded inputs are (batch, seqlen, heads, headdim)")
+    hq, hkv = q.shape[-2], k.shape[-2]
+    if hq % hkv != 0:
+        raise ValueError("number of query heads must be divisible by number of KV heads")
+    return varlen
+
+
+def _flat(x, varlen):
+    x = np.asarray(x)
+    return x if varlen else x.reshape((-1,) + x.shape[2:])
+
+
+def forward(q, k, v, scale=None, causal=False, cu_seqlens_q=None, cu_seqlens_k=None,
+            threads: int = 1, heads=None):
+    """Attention forward over a batch.
+
+    Padded: q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D) -> O (B, Sq, Hq, D), LSE (B, Hq, Sq).
+    Varlen: q (total_q, Hq, D), k/v (total_k, Hkv, D), cu_seqlens_* (B+1,) ->
+    O (total_q, Hq, D), LSE (Hq, total_q).  Returns float64 arrays.
+
+    ``heads`` optionally restricts the work to a list of (sequence, query head) pairs;
+    the other entries of O and LSE are left NaN (used to time a bounded sample)."""
+    varlen = _check(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    hq, hkv = q.shape[-2], k.shape[-2]
+    if varlen:
+        seq_q = _sequences(None, None, cu_seqlens_q)
+        seq_k = _sequences(None, None, cu_seqlens_k)
+    else:
+        seq_q = _sequences(q.shape[0], q.shape[1], None)
+        seq_k = _sequences(k.shape[0], k.shape[1], None)
+    qf, kf, vf = _flat(q, varlen), _flat(k, varlen), _flat(v, varlen)
+    o = np.full(qf.shape, np.nan, dtype=np.float64)
+    lse_flat = np.full((hq, qf.shape[0]), np.nan, dtype=np.float64)
+    work = heads if heads is not None else [(b, h) for b in range(len(seq_q)) for h in range(hq)]
+
+    def one(bh):
+        b, h = bh
+        (q0, lq), (k0, lk) = seq_q[b], seq_k[b]
+        g = kv_head_of(h, hq, hkv)
+        ob, lb = head_forward(qf[q0:q0 + lq, h], kf[k0:k0 + lk, g], vf[k0:k0 + lk, g], scale, causal)
+        o[q0:q0 + lq, h] = ob
+        lse_flat[h, q0:q0 + lq] = lb
+
+    _run(one, work, threads)
+    if varlen:
+        return o, lse_flat
+    B, Sq = q.shape[0], q.shape[1]
+    return o.reshape(q.shape), lse_flat.reshape(hq, B, Sq).transpose(1, 0, 2).copy()
+
+
+def backward(do, q, k, v, scale=None, causal=False, cu_seqlens_q=None, cu_seqlens_k=None,
+             threads: int = 1, heads=None):
+    """Attention backward over a batch: returns float64 (dq, dk, dv) in the layouts of
+    q, k, v.  dk/dv of a KV head sum the contributions of every query head that reads
+    it.  ``heads`` restricts the work as in :func:`forward` (then dk/dv hold partial
+    sums and dq is NaN outside the listed heads)."""
+    varlen = _check(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    hq, hkv = q.shape[-2], k.shape[-2]
+    if varlen:
+        seq_q = _sequences(None, None, cu_seqlens_q)
+        seq_k = _sequences(None, None, cu_seqlens_k)
+    else:
+        seq_q = _sequences(q.shape[0], q.shape[1], None)
+        seq_k = _sequences(k.shape[0], k.shape[1], None)
+    qf, kf, vf, dof = _flat(q, varlen), _flat(k, varlen), _flat(v, varlen), _flat(do, varlen)
+    dq = np.full(qf.shape, np.nan if heads is not None else 0.0, dtype=np.float64)
+    dk = np.zeros(kf.shape, dtype=np.float64)
+    dv = np.zeros(vf.shape, dtype=np.float64)
+    work = heads if heads is not None else [(b, h) for b in range(len(seq_q)) for h in range(hq)]
+    results = {}
+
+    def one(bh):
+        b, h = bh
+        (q0, lq), (k0, lk) = seq_q[b], seq_k[b]
+        g = kv_head_of(h, hq, hkv)
+        results[bh] = head_backward(qf[q0:q0 + lq, h], kf[k0:k0 + lk, g], vf[k0:k0 + lk, g],
+                                    dof[q0:q0 + lq, h], scale, causal)
+
+    _run(one, work, threads)
+    # Accumulate in a fixed order so the result does not depend on thread timing.
+    for (b, h) in work:
+        (q0, lq), (k0, lk) = seq_q[b], seq_k[b]
+        g = kv_head_of(h, hq, hkv)
+        dqh, dkh, dvh = results[(b, h)]
+        dq[q0:q0 + lq, h] = dqh
+        dk[k0:k0 + lk, g] += dkh
+        dv[k0:k0 + lk, g] += dvh
+    if varlen:
+        return dq, dk, dv
+    return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)
+
+
+def _run(fn, work, threads):
+    if threads <= 1 or len(work) <= 1:
+        for w in work:
+            fn(w)
+        return
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fn, work))
