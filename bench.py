@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+A step is one forward (fa_fwd) plus one backward (fa_bwd: preprocess, dK/dV main loop
+with dQ accumulation, dQ finalize) over the causal MHA workload B=2, H=16, S=4096,
+D=128, bf16 -- the reference workload that includes the backward.  Inputs are seeded
+synthetic N(0,1) draws, resident in HBM before timing starts.
+
+Prints ONE JSON line: throughput in algorithmic TFLOPS (forward 4*B*H*S*S*D/2 for causal,
+backward 2.5x that; masked work and recomputation are not counted), the roofline of the
+dominant kernel (the backward main loop) timed per launch with HIP events on the stream
+it runs on, the fp64 CPU oracle timed on a bounded sample of the same workload, and
+extra detail: the forward of the causal GQA workload B=2, Hq=32, Hkv=8, S=8192, D=128.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Case:
+    """Device-resident inputs and outputs of one workload."""
+
+    def __init__(self, n: int, with_bwd: bool):
+        import torch
+        from exact_tiled_attention_02_amd import fa, synth
+        self.w, x = synth.draw_config(n)
+        self.w.backward = with_bwd
+        d = {k: v.cuda() for k, v in x.items()}
+        if with_bwd and "do" not in d:
+            import numpy as np
+            rng = np.random.default_rng(1000 + n)
+            d["do"] = synth._cast(rng.standard_normal(tuple(d["q"].shape), dtype=np.float32), self.w.dtype).cuda()
+        self.d = d
+        self.out = torch.empty_like(d["q"])
+        self.lse = torch.empty(fa.lse_shape(d["q"]), dtype=torch.float32, device="cuda")
+        if with_bwd:
+            self.dq, self.dk, self.dv = (torch.empty_like(d[k]) for k in ("q", "k", "v"))
+            self.ws = fa.workspace_for(d["q"])
+        self.fwd_flops, self.bwd_flops = synth.flops(self.w)
+
+    def fwd(self):
+        from exact_tiled_attention_02_amd import fa
+        fa.fa_fwd(self.d["q"], self.d["k"], self.d["v"], self.out, self.lse, causal=self.w.causal,
+                  scale=self.w.softmax_scale)
+
+    def bwd_stage(self, stage):
+        from exact_tiled_attention_02_amd import fa
+        fa.fa_bwd_stage(stage, self.d["do"], self.d["q"], self.d["k"], self.d["v"], self.out, self.lse, self.dq,
+                        self.dk, self.dv, self.ws, causal=self.w.causal, scale=self.w.softmax_scale)
+
+    def step(self):
+        self.fwd()
+        self.bwd_stage(0)
+
+
+def time_launches(fn, n, pre=None, post=None):
+    """Average duration (s) of fn() over n launches, each bracketed by HIP events recorded
+    on torch's current stream -- the stream the library launches on."""
+    import torch
+    total = 0.0
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        if pre:
+            pre()
+        starts[i].record()
+        fn()
+        ends[i].record()
+        if post:
+            post()
+    torch.cuda.synchronize()
+    for s, e in zip(starts, ends):
+        total += s.elapsed_time(e) * 1e-3
+    return total / n
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload: whole
+    (batch, head) slices of forward + backward, until about target_s seconds of work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from exact_tiled_attention_02_amd import synth
+    from oracle import attention_fp64 as orc
+    w, x = synth.draw_config(5)
+    f = lambda t: t.to(dtype=__import__("torch").float64).numpy()
+    q, k, v, do = (f(x[n]) for n in ("q", "k", "v", "do"))
+    cores = min(16, os.cpu_count() or 1)
+    heads_all = [(b, h) for b in range(w.batch) for h in range(w.heads_q)]
+    per_head = synth.flops(w)
+    per_head = (per_head[0] + per_head[1]) / len(heads_all)
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while done < len(heads_all) and time.perf_counter() - t0 < target_s:
+            batch = heads_all[done:done + cores]
+            orc.forward(q, k, v, causal=True, threads=cores, heads=batch)
+            orc.backward(do, q, k, v, causal=True, threads=cores, heads=batch)
+            done += len(batch)
+    dt = time.perf_counter() - t0
+    return {"value": per_head * done / dt / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle, forward+backward of {done} of {len(heads_all)} (batch, head) slices of "
+                      f"B=2 H=16 S=4096 D=128 causal, {dt:.1f} s on {cores} threads (BLAS 1 thread each); "
+                      f"value = algorithmic FLOPs of the sample / wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-gqa", action="store_true", help="skip the S=8192 GQA forward detail")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "
+              f"see the design notes on sharding)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from exact_tiled_attention_02_amd import fa
+    fa.lib()
+    K, W = args.steps, args.warmup
+
+    c5 = Case(5, with_bwd=True)
+    log(f"[bench] workload {c5.w.name}: warmup {W}, steps {K}")
+    for _ in range(W):
+        c5.step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(K):
+        c5.step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    step_flops = c5.fwd_flops + c5.bwd_flops
+    value = step_flops / (ms * 1e-3) / 1e12
+    log(f"[bench] step {ms:.3f} ms -> {value:.1f} TFLOPS")
+
+    # per-kernel durations (HIP events on the launch stream)
+    t_fwd = time_launches(c5.fwd, K)
+    t_pre = time_launches(lambda: c5.bwd_stage(1), K)
+    t_main = time_launches(lambda: c5.bwd_stage(2), K, pre=lambda: c5.bwd_stage(1), post=lambda: c5.bwd_stage(3))
+    t_fin = time_launches(lambda: c5.bwd_stage(3), K)
+    B, S, H, D = c5.w.batch, c5.w.seqlen_q, c5.w.heads_q, c5.w.headdim
+    pre_bytes = B * S * H * (2 * D * 2 + D * 4 + 4)   # read O, dO (16-bit); write fp32 acc zeros + Dsum
+    fin_bytes = B * S * H * D * (4 + 2)               # read fp32 acc, write dQ
+    main_tflops = c5.bwd_flops / t_main / 1e12
+    detail = {
+        c5.w.name: {
+            "fwd_tflops": c5.fwd_flops / t_fwd / 1e12,
+            "fwd_pct_peak": 100 * c5.fwd_flops / t_fwd / 1e12 / PEAK_TFLOPS,
+            "bwd_tflops": c5.bwd_flops / (t_pre + t_main + t_fin) / 1e12,
+            "bwd_pct_peak": 100 * c5.bwd_flops / (t_pre + t_main + t_fin) / 1e12 / PEAK_TFLOPS,
+            "fwd_us": t_fwd * 1e6, "bwd_pre_us": t_pre * 1e6, "bwd_main_us": t_main * 1e6, "bwd_fin_us": t_fin * 1e6,
+            "bwd_pre_gbs": pre_bytes / t_pre / 1e9, "bwd_fin_gbs": fin_bytes / t_fin / 1e9,
+        }
+    }
+    del c5
+    torch.cuda.empty_cache()
+
+    if not args.skip_gqa:
+        c3 = Case(3, with_bwd=True)
+        for _ in range(W):
+            c3.fwd()
+        t3 = time_launches(c3.fwd, K)
+        c3.fwd()
+        t3p = time_launches(lambda: c3.bwd_stage(1), max(3, K // 4))
+        t3m = time_launches(lambda: c3.bwd_stage(2), max(3, K // 4), pre=lambda: c3.bwd_stage(1))
+        t3f = time_launches(lambda: c3.bwd_stage(3), max(3, K // 4))
+        detail[c3.w.name] = {
+            "fwd_tflops": c3.fwd_flops / t3 / 1e12, "fwd_pct_peak": 100 * c3.fwd_flops / t3 / 1e12 / PEAK_TFLOPS,
+            "fwd_us": t3 * 1e6,
+            "bwd_tflops_same_shape": c3.bwd_flops / (t3p + t3m + t3f) / 1e12,
+            "bwd_pct_peak_same_shape": 100 * c3.bwd_flops / (t3p + t3m + t3f) / 1e12 / PEAK_TFLOPS,
+        }
+        log(f"[bench] GQA S=8192 forward {t3 * 1e6:.1f} us -> {detail[c3.w.name]['fwd_tflops']:.1f} TFLOPS")
+        del c3
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 CPU oracle on a bounded sample")
+        cpu = cpu_baseline()
+
+    rec = {
+        "metric": "attention TFLOPS (fwd, fwd+bwd) & % of MI355X bf16 MFMA peak",
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fwdbwd_causal_mha_b2_h16_s4096_d128_bf16", "batch": 2, "heads_q": 16, "heads_kv": 16,
+                   "seqlen_q": 4096, "seqlen_k": 4096, "headdim": 128, "causal": True, "pct_peak": 100 * value /
+                   PEAK_TFLOPS},
+        "roofline": {"bound": "mfma", "achieved": main_tflops, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": main_tflops / PEAK_TFLOPS, "traffic": None,
+                     "kernel": "bwd_main_kernel<D=128, bf16, causal, padded>"},
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,392 @@
+// Backward kernels: preprocess, dK/dV main loop with dQ accumulation, dQ finalize.
+//
+// The probabilities are recomputed from the forward's LSE instead of being stored: the
+// backward of the release notes "v1.4 - FlashAttention Fork" (section 4.1) applies
+// exp2 with the stored per-row value multiplied by log2(e), i.e.
+// P = exp2(S * scale*log2(e) - LSE * log2(e)).  With that P the gradients are the
+// analytic ones of O = softmax(scale Q K^T) V:
+//   dV = P^T dO,  dP = dO V^T,  Dsum_i = sum_d dO_id O_id,  dS = P * (dP - Dsum),
+//   dK = scale dS^T Q,  dQ = scale dS K.
+// dK/dV of a KV head sum over the query heads that share it (MQA/GQA rule of the
+// flash_attn_func docstring); the causal mask is bottom-right aligned as in the forward.
+//
+// Kernels (all on the caller's stream, in order):
+//   1. preprocess: Dsum = rowsum(dO * O) in fp32 and zeroing of the fp32 dQ accumulator
+//      (memory-bound);
+//   2. main: one workgroup per (128-key block, KV head, sequence); each wavefront owns 32
+//      keys and keeps K, V (as MFMA operands) and its dK, dV accumulators in registers
+//      while it walks the query blocks that can see its keys and every query head of
+//      the group.  Per 32-row query block: S = Q K^T, P, dP = dO V^T, dS, then
+//      dV^T += dO^T P and dK^T += Q^T dS on MFMA; dS goes through LDS so that the four
+//      wavefronts together form dQ = dS K for the block, added to the fp32 accumulator
+//      with atomics;
+//   3. finalize: fp32 accumulator -> dQ in the input dtype.
+// The softmax scale is folded into dS once, so neither dK nor dQ is rescaled later.
+#include "fa_device.h"
+#include "fa_params.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdBN = 32 * kBwdWaves;  // keys per workgroup
+constexpr int kBwdBQ = 32;              // query rows per inner step
+
+// ---------------------------------------------------------------- 1. preprocess
+
+template <int D, bool BF16, bool VARLEN>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
+  constexpr int CH = D / 8;              // 16-byte chunks per (row, head)
+  constexpr int PAIRS = 256 / CH;        // (row, head) pairs per workgroup
+  const int tid = threadIdx.x;
+  const int pair_local = tid / CH;
+  const int ch = tid % CH;
+  const size_t pair = (size_t)blockIdx.x * PAIRS + pair_local;
+  size_t rows = (size_t)a.B * a.Sq;
+  if constexpr (VARLEN) rows = (size_t)a.cu_q[a.B];
+  const bool live = pair < rows * a.Hq;
+  float s = 0.f;
+  if (live) {
+    const size_t off = pair * D + ch * 8;
+    const u32x4 o = load16((const uint16_t*)a.out + off);
+    const u32x4 g = load16((const uint16_t*)a.dout + off);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      s += to_f32<BF16>(o[w] & 0xffff) * to_f32<BF16>(g[w] & 0xffff);
+      s += to_f32<BF16>(o[w] >> 16) * to_f32<BF16>(g[w] >> 16);
+    }
+    float* acc = a.dq_acc + off;
+    store16(acc, u32x4{0, 0, 0, 0});
+    store16(acc + 4, u32x4{0, 0, 0, 0});
+  }
+  // reduce over the CH lanes of this pair (CH is a power of two <= 32, lanes contiguous)
+#pragma unroll
+  for (int m = CH / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if (live && ch == 0) a.dsum[pair] = s;
+}
+
+// ---------------------------------------------------------------- 2. main loop
+
+template <int D>
+struct BwdTile {
+  static constexpr int KSTR = D + 32;   // K tile: transposed reads only
+  static constexpr int QSTR = D + 16;   // Q / dO tiles: row reads and transposed reads
+  static constexpr int SSTR = kBwdBN + 8;  // dS tile [query row][key]
+};
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int KSTR = BwdTile<D>::KSTR;
+  constexpr int QSTR = BwdTile<D>::QSTR;
+  constexpr int SSTR = BwdTile<D>::SSTR;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBwdBN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kBwdBQ * QSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[kBwdBQ * QSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t dSs[kBwdBQ * SSTR];
+  __shared__ float lse2_s[kBwdBQ];
+  __shared__ float dsum_s[kBwdBQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+
+  const int nkb = (a.Sk + kBwdBN - 1) / kBwdBN;
+  const int nbh = a.B * a.Hkv;
+  const int kb = blockIdx.x / nbh;
+  const int bh = blockIdx.x % nbh;
+  const int hk = bh % a.Hkv;
+  const int b = bh / a.Hkv;
+  (void)nkb;
+
+  int q_start, k_start, Lq, Lk;
+  if constexpr (VARLEN) {
+    q_start = a.cu_q[b];
+    Lq = a.cu_q[b + 1] - q_start;
+    k_start = a.cu_k[b];
+    Lk = a.cu_k[b + 1] - k_start;
+  } else {
+    q_start = b * a.Sq;
+    Lq = a.Sq;
+    k_start = b * a.Sk;
+    Lk = a.Sk;
+  }
+  const int k0 = kb * kBwdBN;
+  if (k0 >= Lk) return;  // uniform
+
+  const int G = a.Hq / a.Hkv;
+  const size_t q_rs = (size_t)a.Hq * D;
+  const size_t k_rs = (size_t)a.Hkv * D;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+  const int diag = Lk - Lq;
+  const float c = a.scale_log2;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  // K tile (all 128 keys) in LDS for dQ = dS K.
+  {
+    constexpr int CH = D / 8;
+    for (int cidx = tid; cidx < kBwdBN * CH; cidx += 256) {
+      const int r = cidx / CH, cc = cidx % CH;
+      const int key = k0 + r;
+      u32x4 kv = {0, 0, 0, 0};
+      if (key < Lk) kv = load16(kp + (size_t)key * k_rs + cc * 8);
+      store16(&Ks[r * KSTR + cc * 8], kv);
+    }
+  }
+  // This wavefront's keys as B operands: lane holds K[key][16 s + 8 lh .. +7].
+  const int my_key = k0 + wave * 32 + li;
+  const bool key_ok = my_key < Lk;
+  Frag8 kf[NS], vf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    kf[s].v = key_ok ? load16(kp + (size_t)my_key * k_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+    vf[s].v = key_ok ? load16(vp + (size_t)my_key * k_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+  }
+  f32x16 dkt[ND], dvt[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    dkt[d] = f32x16{};
+    dvt[d] = f32x16{};
+  }
+
+  // Query rows that can see a key of this block: i >= k0 - diag.
+  int qb_begin = 0;
+  if constexpr (CAUSAL) qb_begin = max(0, k0 - diag) / kBwdBQ;
+  const int qb_end = (Lq + kBwdBQ - 1) / kBwdBQ;
+
+  const int tr_row = 4 * lh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  for (int g = 0; g < G; ++g) {
+    const int h = hk * G + g;
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
+    const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * D;
+    for (int qb = qb_begin; qb < qb_end; ++qb) {
+      const int i0 = qb * kBwdBQ;
+      __syncthreads();  // previous step is done with Qs, dOs, dSs
+      {
+        constexpr int CH = D / 8;
+        for (int cidx = tid; cidx < kBwdBQ * CH; cidx += 256) {
+          const int r = cidx / CH, cc = cidx % CH;
+          const int row = i0 + r;
+          u32x4 qv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
+          if (row < Lq) {
+            qv = load16(qp + (size_t)row * q_rs + cc * 8);
+            gv = load16(dop + (size_t)row * q_rs + cc * 8);
+          }
+          store16(&Qs[r * QSTR + cc * 8], qv);
+          store16(&dOs[r * QSTR + cc * 8], gv);
+        }
+        if (tid < kBwdBQ) {
+          const int row = i0 + tid;
+          float l2 = INFINITY, ds = 0.f;
+          if (row < Lq) {
+            size_t li_idx;
+            if constexpr (VARLEN) {
+              li_idx = (size_t)h * a.cu_q[a.B] + q_start + row;
+            } else {
+              li_idx = ((size_t)b * a.Hq + h) * a.Sq + row;
+            }
+            l2 = a.lse[li_idx] * kLog2e;
+            ds = a.dsum[(size_t)(q_start + row) * a.Hq + h];
+          }
+          lse2_s[tid] = l2;
+          dsum_s[tid] = ds;
+        }
+      }
+      __syncthreads();
+
+      // S = Q K^T and dP = dO V^T (query rows x keys); lane = key, registers = rows.
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        Frag8 qa, ga;
+        qa.v = load16(&Qs[li * QSTR + st * 16 + lh * 8]);
+        ga.v = load16(&dOs[li * QSTR + st * 16 + lh * 8]);
+        s = mfma32x32x16<BF16>(qa, kf[st], s);
+        dp = mfma32x32x16<BF16>(ga, vf[st], dp);
+      }
+      // P and dS (scale folded in).
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int row = i0 + rl;
+        bool keep = key_ok && row < Lq;
+        if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
+        const float p = keep ? fast_exp2(fmaf(s[r], c, -lse2_s[rl])) : 0.f;
+        s[r] = p;
+        dp[r] = a.scale * p * (dp[r] - dsum_s[rl]);
+      }
+      Frag8 pf[2], dsf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r0 = 8 * t;
+        pf[t].v = u32x4{pack2<BF16>(s[r0 + 0], s[r0 + 1]), pack2<BF16>(s[r0 + 2], s[r0 + 3]),
+                        pack2<BF16>(s[r0 + 4], s[r0 + 5]), pack2<BF16>(s[r0 + 6], s[r0 + 7])};
+        dsf[t].v = u32x4{pack2<BF16>(dp[r0 + 0], dp[r0 + 1]), pack2<BF16>(dp[r0 + 2], dp[r0 + 3]),
+                         pack2<BF16>(dp[r0 + 4], dp[r0 + 5]), pack2<BF16>(dp[r0 + 6], dp[r0 + 7])};
+      }
+      // dS to LDS as [row][key] for the dQ product.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t two = dsf[t].v[w];
+          const int r = 8 * t + 2 * w;  // registers r and r+1 of this lane
+          const int rl0 = 8 * (r >> 2) + 4 * lh + (r & 3);
+          dSs[rl0 * SSTR + wave * 32 + li] = (uint16_t)(two & 0xffff);
+          dSs[(rl0 + 1) * SSTR + wave * 32 + li] = (uint16_t)(two >> 16);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const int off = (t * 16 + tr_row) * QSTR + d * 32 + tr_col;
+          const u32x2 g_lo = lds_read_tr16(&dOs[off]);
+          const u32x2 g_hi = lds_read_tr16(&dOs[off + 8 * QSTR]);
+          const u32x2 q_lo = lds_read_tr16(&Qs[off]);
+          const u32x2 q_hi = lds_read_tr16(&Qs[off + 8 * QSTR]);
+          Frag8 ga, qa;
+          ga.v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
+          qa.v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
+          dvt[d] = mfma32x32x16<BF16>(ga, pf[t], dvt[d]);
+          dkt[d] = mfma32x32x16<BF16>(qa, dsf[t], dkt[d]);
+        }
+      }
+      __syncthreads();  // dS of all four wavefronts is in LDS
+
+      // dQ[rows][d-block] = dS[rows][128 keys] K[128 keys][d-block]; d-blocks are dealt
+      // round-robin to the wavefronts.
+      for (int d = wave; d < ND; d += kBwdWaves) {
+        f32x16 dq = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < kBwdBN / 16; ++ks) {
+          Frag8 sa, kb2;
+          sa.v = load16(&dSs[li * SSTR + ks * 16 + lh * 8]);
+          const int krow = ks * 16 + 8 * lh + ((lane & 15) >> 2);
+          const int kcol = d * 32 + tr_col;
+          const u32x2 lo = lds_read_tr16(&Ks[krow * KSTR + kcol]);
+          const u32x2 hi = lds_read_tr16(&Ks[(krow + 4) * KSTR + kcol]);
+          kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+          dq = mfma32x32x16<BF16>(sa, kb2, dq);
+        }
+        // lane = column d*32 + li; registers = rows.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          if (row < Lq) {
+            float* dst = a.dq_acc + ((size_t)(q_start + row) * a.Hq + h) * D + d * 32 + li;
+            unsafeAtomicAdd(dst, dq[r]);
+          }
+        }
+      }
+    }
+  }
+
+  // dK, dV: lane = key, registers = head-dimension entries.
+  if (key_ok) {
+    uint16_t* dkp = (uint16_t*)a.dk + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
+    uint16_t* dvp = (uint16_t*)a.dv + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int col = d * 32 + 8 * gq + 4 * lh;
+        u32x2 wk, wv;
+        wk.x = pack2<BF16>(dkt[d][4 * gq + 0], dkt[d][4 * gq + 1]);
+        wk.y = pack2<BF16>(dkt[d][4 * gq + 2], dkt[d][4 * gq + 3]);
+        wv.x = pack2<BF16>(dvt[d][4 * gq + 0], dvt[d][4 * gq + 1]);
+        wv.y = pack2<BF16>(dvt[d][4 * gq + 2], dvt[d][4 * gq + 3]);
+        *(u32x2*)(dkp + col) = wk;
+        *(u32x2*)(dvp + col) = wv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 3. finalize
+
+template <bool BF16, bool VARLEN>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+  // 8 elements per thread
+  size_t rows = (size_t)a.B * a.Sq;
+  if constexpr (VARLEN) rows = (size_t)a.cu_q[a.B];
+  const size_t n8 = rows * a.Hq * a.D / 8;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
+    const u32x4 x0 = load16(a.dq_acc + i * 8);
+    const u32x4 x1 = load16(a.dq_acc + i * 8 + 4);
+    const float* f0 = (const float*)&x0;
+    const float* f1 = (const float*)&x1;
+    u32x4 o;
+    o.x = pack2<BF16>(f0[0], f0[1]);
+    o.y = pack2<BF16>(f0[2], f0[3]);
+    o.z = pack2<BF16>(f1[0], f1[1]);
+    o.w = pack2<BF16>(f1[2], f1[3]);
+    store16((uint16_t*)a.dq + i * 8, o);
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
+  const size_t rows = (size_t)a.B * a.Sq;  // bound on total_q in varlen mode
+  if (stages & 1) {
+    constexpr int PAIRS = 256 / (D / 8);
+    const size_t pairs = rows * a.Hq;
+    const dim3 grid((unsigned)((pairs + PAIRS - 1) / PAIRS));
+    hipLaunchKernelGGL((bwd_pre_kernel<D, BF16, VARLEN>), grid, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & 2) {
+    const int nkb = (a.Sk + kBwdBN - 1) / kBwdBN;
+    const dim3 grid((unsigned)nkb * a.B * a.Hkv);
+    hipLaunchKernelGGL((bwd_main_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & 4) {
+    const size_t n8 = rows * a.Hq * D / 8;
+    size_t blocks = (n8 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL((bwd_dq_kernel<BF16, VARLEN>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd_d(const BwdArgs& a, int st, hipStream_t stream) {
+  const bool varlen = a.cu_q != nullptr;
+  if (a.causal) {
+    return varlen ? launch_bwd_t<D, BF16, true, true>(a, st, stream) : launch_bwd_t<D, BF16, true, false>(a, st, stream);
+  }
+  return varlen ? launch_bwd_t<D, BF16, false, true>(a, st, stream)
+                : launch_bwd_t<D, BF16, false, false>(a, st, stream);
+}
+
+template <int D>
+hipError_t launch_bwd_dt(const BwdArgs& a, int st, hipStream_t stream) {
+  return a.bf16 ? launch_bwd_d<D, true>(a, st, stream) : launch_bwd_d<D, false>(a, st, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int stage_mask, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_bwd_dt<64>(a, stage_mask, stream);
+    case 128: return launch_bwd_dt<128>(a, stage_mask, stream);
+    case 256: return launch_bwd_dt<256>(a, stage_mask, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,80 @@
+// Device-side building blocks shared by the gfx950 attention kernels: operand types,
+// CDNA4 MFMA wrappers, LDS transpose reads, conversions and lane exchanges.
+//
+// MFMA v_mfma_f32_32x32x16_{bf16,f16} operand layout (lane l of a 64-wide wavefront,
+// h = l / 32, i = l % 32; verified on gfx950):
+//   A (32 x 16): lane holds A[i][8h .. 8h+7]
+//   B (16 x 32): lane holds B[8h .. 8h+7][i]
+//   C (32 x 32): lane holds C[8*(r/4) + 4h + (r%4)][i] in register r = 0..15
+// ds_read_b64_tr_b16, per group of 16 lanes: lane i receives element (i % 4) of the four
+// 8-byte chunks addressed by lanes (i / 4) + 4j, j = 0..3, of its group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+// 8 packed 16-bit values (one MFMA operand) carried type-agnostically.
+struct Frag8 {
+  u32x4 v;
+};
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32x32x16(const Frag8& a, const Frag8& b, const f32x16& c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v), __builtin_bit_cast(bf16x8, b.v), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a.v), __builtin_bit_cast(f16x8, b.v), c, 0,
+                                                  0, 0);
+  }
+}
+
+// Two fp32 -> one dword of two 16-bit values, round-to-nearest-even.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (BF16) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 t = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, t);
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 t = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, t);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float to_f32(uint16_t bits) {
+  if constexpr (BF16) {
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+  } else {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  }
+}
+
+// 8-byte transposed LDS read (see the layout note above).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_ptr) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(lds_ptr));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void store16(void* p, u32x4 x) { *(u32x4*)p = x; }
+
+}  // namespace fa

@@ -1,0 +1,283 @@
+// Forward kernel: exact attention, one workgroup per (query block, query head, sequence).
+//
+// Method (FlashAttention README, "How to use FlashAttention"; FlashAttention-2 abstract
+// as quoted on the flash-attention-2 snippet page; softmax details from the release
+// notes "v1.4 - FlashAttention Fork", section 4):
+//   * work is split over sequences, heads and 128-row query blocks; inside a workgroup
+//     each of the 4 wavefronts owns 32 query rows, so the softmax statistics of a row
+//     never leave its wavefront;
+//   * the query tile stays in registers; key/value tiles of 64 rows are staged through
+//     LDS and consumed by all four wavefronts;
+//   * per key tile: S^T = K Q^T on MFMA (fp32 accumulate), masking only on tiles that
+//     touch the causal diagonal or the sequence tail, a running row max m and row sum l,
+//     P = exp2(S * scale*log2(e) - m * scale*log2(e)) (one FMA + exp2), rescaling of the
+//     output accumulator by exp2((m_old - m_new) * scale*log2(e)) on every tile (exact;
+//     never skipped), then O^T += V^T P^T on MFMA with P rounded once to 16 bits;
+//   * a row max of -inf (nothing kept yet) is replaced by 0 so that no (-inf) - (-inf)
+//     appears;
+//   * epilogue: O = acc / l, LSE = m * scale + ln l; a row that kept no key writes O = 0
+//     and LSE = +inf.
+//
+// Orientation: computing S^T (keys x query rows) puts one query row in each lane (and
+// its twin lane l^32), so row reductions are in-lane plus one exchange with lane l^32,
+// the per-row rescale is a per-lane scalar, and the fp32 accumulator, converted to 16
+// bits, is already the B operand of the P V product.  V^T, the A operand of that
+// product, is read from the row-major V tile with ds_read_b64_tr_b16.
+#include "fa_device.h"
+#include "fa_params.h"
+
+namespace fa {
+namespace {
+
+constexpr int kFwdWaves = 4;
+constexpr int kFwdBM = 32 * kFwdWaves;  // query rows per workgroup
+constexpr int kFwdBN = 64;              // keys per tile
+
+template <int D>
+struct FwdTile {
+  // Row strides (in 16-bit elements) of the LDS tiles.  K rows are padded by 16 bytes so
+  // that the 16-byte reads of 16 consecutive key rows hit distinct banks; V rows by
+  // 64 bytes so that the transposed 8-byte reads of 4 consecutive rows do.
+  static constexpr int KSTR = D + 8;
+  static constexpr int VSTR = D + 32;
+};
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+  constexpr int NS = D / 16;  // 16-wide slices of the head dimension (QK^T depth)
+  constexpr int ND = D / 32;  // 32-wide blocks of the head dimension (output tiles)
+  constexpr int KSTR = FwdTile<D>::KSTR;
+  constexpr int VSTR = FwdTile<D>::VSTR;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kFwdBN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kFwdBN * VSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+
+  // Workgroup -> (query block, head, sequence).  Query blocks are visited from the last
+  // one down, so under a causal mask the longest key loops start first.
+  const int nqb = (a.Sq + kFwdBM - 1) / kFwdBM;
+  const int nbh = a.B * a.Hq;
+  const int lin = blockIdx.x;
+  const int qb = nqb - 1 - lin / nbh;
+  const int bh = lin % nbh;
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+
+  int q_start, k_start, Lq, Lk;
+  if constexpr (VARLEN) {
+    q_start = a.cu_q[b];
+    Lq = a.cu_q[b + 1] - q_start;
+    k_start = a.cu_k[b];
+    Lk = a.cu_k[b + 1] - k_start;
+  } else {
+    q_start = b * a.Sq;
+    Lq = a.Sq;
+    k_start = b * a.Sk;
+    Lk = a.Sk;
+  }
+  const int q0 = qb * kFwdBM;
+  if (q0 >= Lq) return;  // uniform over the workgroup
+
+  const int hk = h / (a.Hq / a.Hkv);
+  const size_t q_rs = (size_t)a.Hq * D;
+  const size_t k_rs = (size_t)a.Hkv * D;
+  const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+
+  // Key j is kept for row i iff j <= i + diag (bottom-right alignment).
+  const int diag = Lk - Lq;
+  int kend = Lk;
+  if constexpr (CAUSAL) kend = min(Lk, q0 + kFwdBM + diag);
+  const int nkb = kend > 0 ? (kend + kFwdBN - 1) / kFwdBN : 0;
+
+  const int my_row = q0 + wave * 32 + li;
+  const bool row_ok = my_row < Lq;
+  const int wave_row0 = q0 + wave * 32;
+
+  // Q^T operand: lane holds Q[my_row][16 s + 8 lh .. +7] for every slice s.
+  Frag8 qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    qf[s].v = row_ok ? load16(qp + (size_t)my_row * q_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float c = a.scale_log2;
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int k0 = kb * kFwdBN;
+    __syncthreads();  // every wavefront is done with the previous tile
+    {
+      constexpr int CH = D / 8;  // 16-byte chunks per row
+#pragma unroll
+      for (int cidx = tid; cidx < kFwdBN * CH; cidx += 256) {
+        const int r = cidx / CH;
+        const int cc = cidx % CH;
+        const int key = k0 + r;
+        u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+        if (key < Lk) {
+          kv = load16(kp + (size_t)key * k_rs + cc * 8);
+          vv = load16(vp + (size_t)key * k_rs + cc * 8);
+        }
+        store16(&Ks[r * KSTR + cc * 8], kv);
+        store16(&Vs[r * VSTR + cc * 8], vv);
+      }
+    }
+    __syncthreads();
+    // A wavefront whose rows keep no key of this tile has nothing to add.
+    if (CAUSAL && k0 > wave_row0 + 31 + diag) continue;
+
+    // S^T (keys x rows): two 32-key blocks.
+    f32x16 s[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      s[sub] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        Frag8 kf;
+        kf.v = load16(&Ks[(sub * 32 + li) * KSTR + st * 16 + lh * 8]);
+        s[sub] = mfma32x32x16<BF16>(kf, qf[st], s[sub]);
+      }
+    }
+
+    // Masked scores become -inf for the row max; their probabilities are forced to 0
+    // after the exp (exp2(-inf * 0) would be NaN for a zero scale).
+    const bool need_mask = (k0 + kFwdBN > Lk) || (CAUSAL && k0 + kFwdBN - 1 > wave_row0 + diag);
+    uint32_t keep_bits = 0xffffffffu;
+    if (need_mask) {
+      keep_bits = 0;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          bool keep = key < Lk;
+          if constexpr (CAUSAL) keep = keep && (key <= my_row + diag);
+          keep_bits |= (keep ? 1u : 0u) << (sub * 16 + r);
+          s[sub][r] = keep ? s[sub][r] : -INFINITY;
+        }
+      }
+    }
+
+    float mx = m_run;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+    mx = fmaxf(mx, xor32(mx));
+    const float m_use = (mx == -INFINITY) ? 0.f : mx;
+    const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
+    m_run = mx;
+    const float mc = m_use * c;
+
+    float ls = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(s[sub][r], c, -mc));
+        if (need_mask) p = ((keep_bits >> (sub * 16 + r)) & 1u) ? p : 0.f;
+        s[sub][r] = p;
+        ls += p;
+      }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+
+    // P^T as the B operand of O^T += V^T P^T: slice t covers keys 16t .. 16t+15; lane
+    // position p of half lh stands for key 16t + 8(p/4) + 4lh + p%4.
+    Frag8 pf[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int sub = t >> 1, r0 = (t & 1) * 8;
+      pf[t].v = u32x4{pack2<BF16>(s[sub][r0 + 0], s[sub][r0 + 1]), pack2<BF16>(s[sub][r0 + 2], s[sub][r0 + 3]),
+                      pack2<BF16>(s[sub][r0 + 4], s[sub][r0 + 5]), pack2<BF16>(s[sub][r0 + 6], s[sub][r0 + 7])};
+    }
+    const int tr_row = 4 * lh + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const uint16_t* base = &Vs[(t * 16 + tr_row) * VSTR + d * 32 + tr_col];
+        const u32x2 lo = lds_read_tr16(base);
+        const u32x2 hi = lds_read_tr16(base + 8 * VSTR);
+        Frag8 vf;
+        vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+        acc[d] = mfma32x32x16<BF16>(vf, pf[t], acc[d]);
+      }
+    }
+  }
+
+  // Epilogue.
+  const float l_tot = l_run + xor32(l_run);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = d * 32 + 8 * g + 4 * lh;
+        u32x2 w;
+        w.x = pack2<BF16>(acc[d][4 * g + 0] * inv, acc[d][4 * g + 1] * inv);
+        w.y = pack2<BF16>(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv);
+        *(u32x2*)(op + col) = w;
+      }
+    }
+    if (lh == 0) {
+      const float lse = l_tot > 0.f ? m_run * a.scale + __logf(l_tot) : INFINITY;
+      size_t idx;
+      if constexpr (VARLEN) {
+        idx = (size_t)h * a.cu_q[a.B] + q_start + my_row;
+      } else {
+        idx = ((size_t)b * a.Hq + h) * a.Sq + my_row;
+      }
+      a.lse[idx] = lse;
+    }
+  }
+}
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.Sq + kFwdBM - 1) / kFwdBM;
+  const dim3 grid((unsigned)nqb * a.B * a.Hq);
+  hipLaunchKernelGGL((fwd_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
+  const bool varlen = a.cu_q != nullptr;
+  if (a.causal) {
+    return varlen ? launch_fwd_t<D, BF16, true, true>(a, stream) : launch_fwd_t<D, BF16, true, false>(a, stream);
+  }
+  return varlen ? launch_fwd_t<D, BF16, false, true>(a, stream) : launch_fwd_t<D, BF16, false, false>(a, stream);
+}
+
+template <int D>
+hipError_t launch_fwd_dt(const FwdArgs& a, hipStream_t stream) {
+  return a.bf16 ? launch_fwd_d<D, true>(a, stream) : launch_fwd_d<D, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_fwd_dt<64>(a, stream);
+    case 128: return launch_fwd_dt<128>(a, stream);
+    case 256: return launch_fwd_dt<256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,190 @@
+"""Python binding of libfa.so (ctypes).  Argument marshalling only: every step of the
+attention computation runs in the HIP kernels behind the C ABI of include/fa.h.
+PyTorch supplies device memory and the current stream.
+
+The low-level entry points keep the C names (``fa_fwd``, ``fa_bwd``,
+``fa_bwd_workspace_bytes``); ``forward``/``backward`` additionally allocate their outputs.
+There is no fallback: if libfa.so is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1
+_DTYPE_CODE = {torch.float16: FA_DTYPE_FP16, torch.bfloat16: FA_DTYPE_BF16}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_tiled_attention_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, i, vp]
+        L.fa_fwd.restype = i
+        L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        L.fa_bwd_workspace_bytes.restype = sz
+        L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, i, vp, sz, vp]
+        L.fa_bwd.restype = i
+        L.fa_bwd_stage.argtypes = [i] + L.fa_bwd.argtypes
+        L.fa_bwd_stage.restype = i
+        L.fa_status_string.argtypes = [i]
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_last_error.argtypes = []
+        L.fa_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    """Map an fa_status to a Python exception (1, 2 -> ValueError; 3, 4 -> RuntimeError)."""
+    if status == FA_OK:
+        return
+    L = lib()
+    msg = f"{L.fa_status_string(status).decode()}: {L.fa_last_error().decode()}"
+    if status in (FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED):
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k):
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    if cu_seqlens_q is None:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("padded q/k/v are (batch, seqlen, heads, headdim)")
+        B, Sq, Hq, D = q.shape
+        Sk, Hkv = k.shape[1], k.shape[2]
+    else:
+        if q.dim() != 3 or k.dim() != 3:
+            raise ValueError("varlen q/k/v are (total, heads, headdim)")
+        if max_seqlen_q is None or max_seqlen_k is None:
+            raise ValueError("varlen calls need max_seqlen_q and max_seqlen_k")
+        for c in (cu_seqlens_q, cu_seqlens_k):
+            if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous() or not c.is_cuda:
+                raise ValueError("cu_seqlens must be contiguous 1-D int32 GPU tensors")
+        B = cu_seqlens_q.numel() - 1
+        if cu_seqlens_k.numel() != B + 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k differ in length")
+        Sq, Sk = int(max_seqlen_q), int(max_seqlen_k)
+        Hq, D = q.shape[1], q.shape[2]
+        Hkv = k.shape[1]
+    return B, Sq, Sk, Hq, Hkv, D
+
+
+def _dtype(*ts):
+    d = ts[0].dtype
+    if d not in _DTYPE_CODE:
+        raise ValueError(f"dtype {d} is not float16/bfloat16")
+    for t in ts:
+        if t.dtype != d:
+            raise ValueError("q, k, v (and dout, out) must share one dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if not t.is_cuda:
+            raise ValueError("tensors must live in GPU memory")
+    return _DTYPE_CODE[d]
+
+
+def fa_fwd(q, k, v, out, lse, causal: bool = False, scale: float | None = None, cu_seqlens_q=None,
+           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None) -> None:
+    """Enqueue the forward on ``stream`` (default: torch's current stream); writes out, lse."""
+    B, Sq, Sk, Hq, Hkv, D = _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    dt = _dtype(q, k, v, out)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, float(scale),
+                       int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), dt, _stream(stream)))
+
+
+def fa_bwd_workspace_bytes(B: int, Sq: int, Hq: int, D: int) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, Sq, Hq, D))
+
+
+def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: bool = False, scale: float | None = None,
+           cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None) -> None:
+    """Enqueue the backward; writes dq, dk, dv.  ``workspace``: a uint8 device tensor of
+    at least fa_bwd_workspace_bytes(B, Sq, Hq, D) bytes."""
+    fa_bwd_stage(0, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q, cu_seqlens_k,
+                 max_seqlen_q, max_seqlen_k, stream)
+
+
+def fa_bwd_stage(stage, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: bool = False,
+                 scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                 max_seqlen_k=None, stream=None) -> None:
+    """Enqueue one backward stage (1 preprocess, 2 main loop, 3 finalize); stage 0 runs
+    the whole backward (``fa_bwd``)."""
+    B, Sq, Sk, Hq, Hkv, D = _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    dt = _dtype(q, k, v, out, dout, dq, dk, dv)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    if not workspace.is_cuda:
+        raise ValueError("workspace must live in GPU memory")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    args = (_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, Sq, Sk,
+            Hq, Hkv, D, float(scale), int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), dt, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if stage == 0:
+        check(lib().fa_bwd(*args))
+    else:
+        check(lib().fa_bwd_stage(int(stage), *args))
+
+
+def lse_shape(q, cu_seqlens_q=None):
+    if cu_seqlens_q is None:
+        B, Sq, Hq, _ = q.shape
+        return (B, Hq, Sq)
+    return (q.shape[1], q.shape[0])
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None,
+            max_seqlen_q=None, max_seqlen_k=None, stream=None):
+    """Allocate (out, lse) and run :func:`fa_fwd`."""
+    out = torch.empty_like(q)
+    lse = torch.empty(lse_shape(q, cu_seqlens_q), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, out, lse, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, stream)
+    return out, lse
+
+
+def workspace_for(q, cu_seqlens_q=None, max_seqlen_q=None):
+    if cu_seqlens_q is None:
+        B, Sq, Hq, D = q.shape
+    else:
+        # every sequence is at most max_seqlen_q long, so B * max_seqlen_q >= total_q
+        B, Sq, Hq, D = cu_seqlens_q.numel() - 1, int(max_seqlen_q), q.shape[1], q.shape[2]
+    n = fa_bwd_workspace_bytes(B, Sq, Hq, D)
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def backward(dout, q, k, v, out, lse, causal: bool = False, scale: float | None = None, cu_seqlens_q=None,
+             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None):
+    """Allocate (dq, dk, dv) and the workspace, and run :func:`fa_bwd`."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = workspace_for(q, cu_seqlens_q, max_seqlen_q)
+    fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, ws, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+           max_seqlen_k, stream)
+    return dq, dk, dv

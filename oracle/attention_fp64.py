@@ -54,6 +54,7 @@ __all__ = [
     "causal_keep_mask",
     "head_probabilities",
     "head_forward",
+    "rows_forward",
     "head_backward",
     "forward",
     "backward",
@@ -105,6 +106,31 @@ def head_forward(q, k, v, scale: float, causal: bool):
     """One head: O = P V (float64, (len_q, D)) and LSE ((len_q,))."""
     p, lse, _ = head_probabilities(q, k, scale, causal)
     o = p @ np.asarray(v, dtype=np.float64)
+    return o, lse
+
+
+def rows_forward(q_rows, rows, k, v, scale: float, causal: bool, len_q: int):
+    """Output and LSE of selected query rows of one head: ``q_rows[n]`` is query row
+    ``rows[n]`` of a sequence of ``len_q`` queries (the row index fixes its causal
+    mask).  Same definition as :func:`head_forward`, restricted to those rows, so that
+    outputs of very long sequences can be checked one row at a time."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    len_k = k.shape[0]
+    s = scale * (q_rows @ k.T)
+    j = np.arange(len_k)[None, :]
+    keep = np.ones_like(s, dtype=bool) if not causal else (j <= rows[:, None] + (len_k - len_q))
+    s = np.where(keep, s, -np.inf)
+    live = keep.any(axis=1)
+    m = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
+    e = np.where(keep, np.exp(s - m[:, None]), 0.0)
+    z = e.sum(axis=1)
+    o = np.zeros((len(rows), v.shape[1]))
+    o[live] = (e[live] @ v) / z[live, None]
+    lse = np.full(len(rows), np.inf)
+    lse[live] = m[live] + np.log(z[live])
     return o, lse
 
 

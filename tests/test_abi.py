@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports every function include/fa.h declares, and rejects
+every invalid argument on the host with the documented status before launching
+anything (these calls return before any HIP call, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_02_amd import build, fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.LIB_PATH):
+        build.build()
+    return fa.lib()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libfa.so does not export {n}"
+
+
+def test_status_strings(L):
+    assert L.fa_status_string(0) == b"FA_OK"
+    assert L.fa_status_string(1) == b"FA_ERR_INVALID_ARGUMENT"
+    assert L.fa_status_string(4) == b"FA_ERR_HIP"
+    assert L.fa_status_string(99) == b"unknown fa_status"
+
+
+P = 0x10000  # a 16-byte aligned stand-in address; never dereferenced by these calls
+
+
+def _fwd(L, **over):
+    a = dict(q=P, k=P, v=P, out=P, lse=P, B=1, Sq=128, Sk=128, Hq=4, Hkv=2, D=128, scale=0.1, causal=1,
+             cu_q=None, cu_k=None, dtype=1, stream=None)
+    a.update(over)
+    return L.fa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hkv"], a["D"],
+                    a["scale"], a["causal"], a["cu_q"], a["cu_k"], a["dtype"], a["stream"])
+
+
+def _bwd(L, **over):
+    a = dict(do=P, q=P, k=P, v=P, out=P, lse=P, dq=P, dk=P, dv=P, B=1, Sq=128, Sk=128, Hq=4, Hkv=2, D=128,
+             scale=0.1, causal=1, cu_q=None, cu_k=None, dtype=1, ws=P, ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    return L.fa_bwd(a["do"], a["q"], a["k"], a["v"], a["out"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["Sq"],
+                    a["Sk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["cu_q"], a["cu_k"], a["dtype"],
+                    a["ws"], a["ws_bytes"], a["stream"])
+
+
+INVALID = [
+    (dict(Hq=6, Hkv=4), 1),                # heads not divisible
+    (dict(D=96), 2),                       # no kernel for this head dimension
+    (dict(D=512), 2),
+    (dict(D=0), 1),
+    (dict(dtype=7), 2),                    # unknown dtype
+    (dict(B=0), 1),
+    (dict(Sq=-1), 1),
+    (dict(Sk=0), 1),
+    (dict(Hkv=0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(scale=float("inf")), 1),
+    (dict(scale=-0.5), 1),
+    (dict(cu_q=P, cu_k=None), 1),         # only one cu_seqlens
+    (dict(cu_q=None, cu_k=P), 1),
+    (dict(cu_q=P + 2, cu_k=P), 1),         # misaligned cu_seqlens
+    (dict(q=None), 1),
+    (dict(v=P + 8), 1),                    # misaligned tensor
+    (dict(lse=None), 1),
+]
+
+
+@pytest.mark.parametrize("over,status", INVALID, ids=lambda x: str(x))
+def test_fwd_rejects(L, over, status):
+    assert _fwd(L, **over) == status
+    assert L.fa_last_error() != b""
+
+
+@pytest.mark.parametrize("over,status", INVALID + [
+    (dict(dq=None), 1), (dict(dk=P + 4), 1), (dict(do=None), 1),
+    (dict(ws=None), 3), (dict(ws_bytes=16), 3), (dict(ws=P + 8), 3),
+], ids=lambda x: str(x))
+def test_bwd_rejects(L, over, status):
+    assert _bwd(L, **over) == status
+
+
+def test_workspace_bytes(L):
+    n = L.fa_bwd_workspace_bytes(2, 4096, 16, 128)
+    assert n >= 2 * 4096 * 16 * 128 * 4 + 2 * 4096 * 16 * 4
+    assert n % 256 == 0
+    assert L.fa_bwd_workspace_bytes(0, 1, 1, 1) == 0
+
+
+def test_python_status_mapping(L):
+    fa.check(0)
+    for st, exc in ((1, ValueError), (2, ValueError), (3, RuntimeError), (4, RuntimeError)):
+        with pytest.raises(exc):
+            fa.check(st)
+
+
+def test_binding_rejects_host_tensors(L):
+    import torch
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q, q.clone(), torch.zeros(1, 2, 8), causal=False)
+
+
+@pytest.mark.parametrize("stage", [0, 4, -1])
+def test_bwd_stage_rejects_bad_stage(L, stage):
+    args = [P] * 9 + [1, 128, 128, 4, 2, 128, 0.1, 1, None, None, 1, P, 1 << 40, None]
+    assert L.fa_bwd_stage(stage, *args) == 1
+
+
+def test_bwd_stage_validates_like_fa_bwd(L):
+    args = [P] * 9 + [1, 128, 128, 6, 4, 128, 0.1, 1, None, None, 1, P, 1 << 40, None]
+    assert L.fa_bwd_stage(2, *args) == 1

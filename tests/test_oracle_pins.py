@@ -295,3 +295,17 @@ def test_dsum_identity():
     p, _, _ = orc.head_probabilities(q, k, 0.5, True)
     o = p @ v
     np.testing.assert_allclose((do * o).sum(axis=1), (p * (do @ v.T)).sum(axis=1), rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal,lq,lk", [(False, 9, 14), (True, 12, 12), (True, 10, 4), (True, 4, 10)])
+def test_rows_forward_matches_whole_head(causal, lq, lk):
+    """The row-sampled oracle equals the whole-head oracle on every row subset."""
+    rng = np.random.default_rng(15)
+    q, k, v = _rand(rng, lq, 8), _rand(rng, lk, 8), _rand(rng, lk, 8)
+    o, lse = orc.head_forward(q, k, v, 0.35, causal)
+    rows = rng.permutation(lq)[: max(1, lq // 2)]
+    o2, lse2 = orc.rows_forward(q[rows], rows, k, v, 0.35, causal, lq)
+    np.testing.assert_allclose(o2, o[rows], rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(np.isinf(lse2), np.isinf(lse[rows]))
+    fin = np.isfinite(lse2)
+    np.testing.assert_allclose(lse2[fin], lse[rows][fin], rtol=1e-14)
