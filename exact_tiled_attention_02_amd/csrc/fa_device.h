@@ -72,6 +72,50 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_ptr) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): lane l of the
+// wavefront writes lds_base + 16*l.  lds_base must be the same in every lane.
+__device__ __forceinline__ void lds_direct_load16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_base, 16, 0, 0);
+}
+
+// Wait until every outstanding memory operation of this wavefront has completed
+// (including direct global->LDS loads).
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Combine a value with the one held by lane l^32 (the other half of the wavefront).
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Layout of an unpadded K or V tile in LDS: row r holds D 16-bit elements as D/8 chunks
+// of 16 bytes, stored at physical chunk c ^ f(r) for logical chunk c.  The K pattern
+// spreads 16 consecutive rows of one chunk over all 64 banks (row reads of the MFMA A/B
+// operands); the V pattern spreads 4 consecutive rows x 4 consecutive chunks (the
+// transposed reads).  Each map is its own inverse.
+template <int D>
+struct TileSwizzle {
+  static constexpr int CH = D / 8;
+  __device__ static __forceinline__ int k(int r, int c) {
+    if constexpr (D == 64) return c ^ ((r >> 1) & 7);
+    else return c ^ (r & 15);
+  }
+  __device__ static __forceinline__ int v(int r, int c) {
+    if constexpr (D == 64) return c ^ (((r >> 1) & 1) << 2);
+    else return c ^ ((r & 3) << 2);
+  }
+  // element offset of logical chunk c of row r (K layout)
+  __device__ static __forceinline__ int k_elem(int r, int c) { return r * D + k(r, c) * 8; }
+  // element offset of logical element e of row r (V layout)
+  __device__ static __forceinline__ int v_elem(int r, int e) { return r * D + v(r, e >> 3) * 8 + (e & 7); }
+};
+
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }

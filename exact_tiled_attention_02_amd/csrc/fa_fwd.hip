@@ -6,8 +6,10 @@
 //   * work is split over sequences, heads and 128-row query blocks; inside a workgroup
 //     each of the 4 wavefronts owns 32 query rows, so the softmax statistics of a row
 //     never leave its wavefront;
-//   * the query tile stays in registers; key/value tiles of 64 rows are staged through
-//     LDS and consumed by all four wavefronts;
+//   * the query tile stays in registers; key/value tiles of 64 rows stream through LDS,
+//     double-buffered: the tile after the current one is fetched straight from global
+//     memory into LDS (global_load_lds_dwordx4, no register staging) while the current
+//     one is being multiplied, with one workgroup barrier per tile;
 //   * per key tile: S^T = K Q^T on MFMA (fp32 accumulate), masking only on tiles that
 //     touch the causal diagonal or the sequence tail, a running row max m and row sum l,
 //     P = exp2(S * scale*log2(e) - m * scale*log2(e)) (one FMA + exp2), rescaling of the
@@ -19,10 +21,15 @@
 //     and LSE = +inf.
 //
 // Orientation: computing S^T (keys x query rows) puts one query row in each lane (and
-// its twin lane l^32), so row reductions are in-lane plus one exchange with lane l^32,
-// the per-row rescale is a per-lane scalar, and the fp32 accumulator, converted to 16
-// bits, is already the B operand of the P V product.  V^T, the A operand of that
-// product, is read from the row-major V tile with ds_read_b64_tr_b16.
+// its twin lane l^32), so row reductions are in-lane plus one cross-half exchange
+// (v_permlane32_swap), the per-row rescale is a per-lane scalar, and the fp32
+// accumulator, converted to 16 bits, is already the B operand of the P V product.  V^T,
+// the A operand of that product, is read from the row-major V tile with
+// ds_read_b64_tr_b16.
+//
+// LDS tiles are unpadded and XOR-swizzled on 16-byte chunks (see TileSwizzle), which is
+// what a direct global->LDS load can produce and keeps both read patterns free of bank
+// conflicts.
 #include "fa_device.h"
 #include "fa_params.h"
 
@@ -33,23 +40,14 @@ constexpr int kFwdWaves = 4;
 constexpr int kFwdBM = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBN = 64;              // keys per tile
 
-template <int D>
-struct FwdTile {
-  // Row strides (in 16-bit elements) of the LDS tiles.  K rows are padded by 16 bytes so
-  // that the 16-byte reads of 16 consecutive key rows hit distinct banks; V rows by
-  // 64 bytes so that the transposed 8-byte reads of 4 consecutive rows do.
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = D + 32;
-};
-
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   constexpr int NS = D / 16;  // 16-wide slices of the head dimension (QK^T depth)
   constexpr int ND = D / 32;  // 32-wide blocks of the head dimension (output tiles)
-  constexpr int KSTR = FwdTile<D>::KSTR;
-  constexpr int VSTR = FwdTile<D>::VSTR;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kFwdBN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kFwdBN * VSTR];
+  constexpr int TILE = kFwdBN * D;  // elements per K or V tile
+  using Swz = TileSwizzle<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,6 +97,25 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const bool row_ok = my_row < Lq;
   const int wave_row0 = q0 + wave * 32;
 
+  // Direct global->LDS fetch of key/value tile kb into buffer buf.  Rows past the end of
+  // the sequence re-read its last row (finite data; those keys are masked to P = 0).
+  auto fetch = [&](int kb, int buf) {
+    const int k0 = kb * kFwdBN;
+#pragma unroll
+    for (int i = 0; i < TILE / 8 / 256; ++i) {
+      const int first = (i * kFwdWaves + wave) * 64;  // first chunk written by this instruction
+      const int chunk = first + lane;
+      const int r = chunk / Swz::CH;
+      const int p = chunk % Swz::CH;
+      const int key = min(k0 + r, Lk - 1);
+      const size_t src = (size_t)key * k_rs;
+      lds_direct_load16(kp + src + Swz::k(r, p) * 8, &Kt[buf][first * 8]);
+      lds_direct_load16(vp + src + Swz::v(r, p) * 8, &Vt[buf][first * 8]);
+    }
+  };
+
+  if (nkb > 0) fetch(0, 0);
+
   // Q^T operand: lane holds Q[my_row][16 s + 8 lh .. +7] for every slice s.
   Frag8 qf[NS];
 #pragma unroll
@@ -113,113 +130,113 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   float l_run = 0.f;
   const float c = a.scale_log2;
 
+  // Per-lane LDS element offsets of the MFMA operand reads (within a tile).
+  int koff[2][NS];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int st = 0; st < NS; ++st) koff[sub][st] = Swz::k_elem(sub * 32 + li, st * 2 + lh);
+  const int tr_row = 4 * lh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  wait_all_memory();
+  __syncthreads();
+
   for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
     const int k0 = kb * kFwdBN;
-    __syncthreads();  // every wavefront is done with the previous tile
-    {
-      constexpr int CH = D / 8;  // 16-byte chunks per row
-#pragma unroll
-      for (int cidx = tid; cidx < kFwdBN * CH; cidx += 256) {
-        const int r = cidx / CH;
-        const int cc = cidx % CH;
-        const int key = k0 + r;
-        u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (key < Lk) {
-          kv = load16(kp + (size_t)key * k_rs + cc * 8);
-          vv = load16(vp + (size_t)key * k_rs + cc * 8);
-        }
-        store16(&Ks[r * KSTR + cc * 8], kv);
-        store16(&Vs[r * VSTR + cc * 8], vv);
-      }
-    }
-    __syncthreads();
+    if (kb + 1 < nkb) fetch(kb + 1, cur ^ 1);
+
     // A wavefront whose rows keep no key of this tile has nothing to add.
-    if (CAUSAL && k0 > wave_row0 + 31 + diag) continue;
-
-    // S^T (keys x rows): two 32-key blocks.
-    f32x16 s[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      s[sub] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        Frag8 kf;
-        kf.v = load16(&Ks[(sub * 32 + li) * KSTR + st * 16 + lh * 8]);
-        s[sub] = mfma32x32x16<BF16>(kf, qf[st], s[sub]);
-      }
-    }
-
-    // Masked scores become -inf for the row max; their probabilities are forced to 0
-    // after the exp (exp2(-inf * 0) would be NaN for a zero scale).
-    const bool need_mask = (k0 + kFwdBN > Lk) || (CAUSAL && k0 + kFwdBN - 1 > wave_row0 + diag);
-    uint32_t keep_bits = 0xffffffffu;
-    if (need_mask) {
-      keep_bits = 0;
+    if (!(CAUSAL && k0 > wave_row0 + 31 + diag)) {
+      const uint16_t* K = Kt[cur];
+      const uint16_t* V = Vt[cur];
+      // S^T (keys x rows): two 32-key blocks.
+      f32x16 s[2];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
+        s[sub] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          Frag8 kf;
+          kf.v = load16(K + koff[sub][st]);
+          s[sub] = mfma32x32x16<BF16>(kf, qf[st], s[sub]);
+        }
+      }
+
+      // Masked scores become -inf for the row max; their probabilities are forced to 0
+      // after the exp (exp2(-inf * 0) would be NaN for a zero scale).
+      const bool need_mask = (k0 + kFwdBN > Lk) || (CAUSAL && k0 + kFwdBN - 1 > wave_row0 + diag);
+      uint32_t keep_bits = 0xffffffffu;
+      if (need_mask) {
+        keep_bits = 0;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            bool keep = key < Lk;
+            if constexpr (CAUSAL) keep = keep && (key <= my_row + diag);
+            keep_bits |= (keep ? 1u : 0u) << (sub * 16 + r);
+            s[sub][r] = keep ? s[sub][r] : -INFINITY;
+          }
+        }
+      }
+
+      float mx = m_run;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+      mx = pair_max(mx);
+      const float m_use = (mx == -INFINITY) ? 0.f : mx;
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
+      m_run = mx;
+      const float mc = m_use * c;
+
+      float ls = 0.f;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          bool keep = key < Lk;
-          if constexpr (CAUSAL) keep = keep && (key <= my_row + diag);
-          keep_bits |= (keep ? 1u : 0u) << (sub * 16 + r);
-          s[sub][r] = keep ? s[sub][r] : -INFINITY;
+          float p = fast_exp2(fmaf(s[sub][r], c, -mc));
+          if (need_mask) p = ((keep_bits >> (sub * 16 + r)) & 1u) ? p : 0.f;
+          s[sub][r] = p;
+          ls += p;
+        }
+      l_run = l_run * alpha + ls;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+
+      // P^T as the B operand of O^T += V^T P^T: slice t covers keys 16t .. 16t+15; lane
+      // position p of half lh stands for key 16t + 8(p/4) + 4lh + p%4.
+      Frag8 pf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int sub = t >> 1, r0 = (t & 1) * 8;
+        pf[t].v = u32x4{pack2<BF16>(s[sub][r0 + 0], s[sub][r0 + 1]), pack2<BF16>(s[sub][r0 + 2], s[sub][r0 + 3]),
+                        pack2<BF16>(s[sub][r0 + 4], s[sub][r0 + 5]), pack2<BF16>(s[sub][r0 + 6], s[sub][r0 + 7])};
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const int row = t * 16 + tr_row;
+          const int col = d * 32 + tr_col;
+          const u32x2 lo = lds_read_tr16(V + Swz::v_elem(row, col));
+          const u32x2 hi = lds_read_tr16(V + Swz::v_elem(row + 8, col));
+          Frag8 vf;
+          vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+          acc[d] = mfma32x32x16<BF16>(vf, pf[t], acc[d]);
         }
       }
     }
-
-    float mx = m_run;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_use = (mx == -INFINITY) ? 0.f : mx;
-    const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
-    m_run = mx;
-    const float mc = m_use * c;
-
-    float ls = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[sub][r], c, -mc));
-        if (need_mask) p = ((keep_bits >> (sub * 16 + r)) & 1u) ? p : 0.f;
-        s[sub][r] = p;
-        ls += p;
-      }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) acc[d] *= alpha;
-
-    // P^T as the B operand of O^T += V^T P^T: slice t covers keys 16t .. 16t+15; lane
-    // position p of half lh stands for key 16t + 8(p/4) + 4lh + p%4.
-    Frag8 pf[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int sub = t >> 1, r0 = (t & 1) * 8;
-      pf[t].v = u32x4{pack2<BF16>(s[sub][r0 + 0], s[sub][r0 + 1]), pack2<BF16>(s[sub][r0 + 2], s[sub][r0 + 3]),
-                      pack2<BF16>(s[sub][r0 + 4], s[sub][r0 + 5]), pack2<BF16>(s[sub][r0 + 6], s[sub][r0 + 7])};
-    }
-    const int tr_row = 4 * lh + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const uint16_t* base = &Vs[(t * 16 + tr_row) * VSTR + d * 32 + tr_col];
-        const u32x2 lo = lds_read_tr16(base);
-        const u32x2 hi = lds_read_tr16(base + 8 * VSTR);
-        Frag8 vf;
-        vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
-        acc[d] = mfma32x32x16<BF16>(vf, pf[t], acc[d]);
-      }
-    }
+    wait_all_memory();  // the prefetched tile has landed in LDS
+    __syncthreads();    // ... and every wavefront is done with the current one
   }
 
   // Epilogue.
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = pair_sum(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * D;
