@@ -1,6 +1,6 @@
 // Host side of libfa.so: argument validation, kernel choice and launch (C ABI of fa.h).
 // Nothing here synchronises the host or allocates device memory.
-#include "../../include/fa.h"
+#include "fa.h"
 
 #include <cmath>
 #include <cstdarg>

@@ -67,26 +67,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- 2. main loop
 
-template <int D>
-struct BwdTile {
-  static constexpr int KSTR = D + 32;   // K tile: transposed reads only
-  static constexpr int QSTR = D + 16;   // Q / dO tiles: row reads and transposed reads
-  static constexpr int SSTR = kBwdBN + 8;  // dS tile [query row][key]
-};
-
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr int KSTR = BwdTile<D>::KSTR;
-  constexpr int QSTR = BwdTile<D>::QSTR;
-  constexpr int SSTR = BwdTile<D>::SSTR;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBwdBN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kBwdBQ * QSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[kBwdBQ * QSTR];
+  constexpr int SSTR = kBwdBN + 8;  // dS tile [query row][key], padded
+  constexpr int QT = kBwdBQ * D;    // elements of a Q or dO tile
+  using Swz = DualSwizzle<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBwdBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][QT];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][QT];
   __shared__ __attribute__((aligned(16))) uint16_t dSs[kBwdBQ * SSTR];
-  __shared__ float lse2_s[kBwdBQ];
-  __shared__ float dsum_s[kBwdBQ];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][64];
+  __shared__ __attribute__((aligned(16))) float dsum_s[2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,13 +87,11 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   const int li = lane & 31;
   const int lh = lane >> 5;
 
-  const int nkb = (a.Sk + kBwdBN - 1) / kBwdBN;
   const int nbh = a.B * a.Hkv;
   const int kb = blockIdx.x / nbh;
   const int bh = blockIdx.x % nbh;
   const int hk = bh % a.Hkv;
   const int b = bh / a.Hkv;
-  (void)nkb;
 
   int q_start, k_start, Lq, Lk;
   if constexpr (VARLEN) {
@@ -125,18 +116,58 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   const int diag = Lk - Lq;
   const float c = a.scale_log2;
   constexpr float kLog2e = 1.4426950408889634f;
-
-  // K tile (all 128 keys) in LDS for dQ = dS K.
-  {
-    constexpr int CH = D / 8;
-    for (int cidx = tid; cidx < kBwdBN * CH; cidx += 256) {
-      const int r = cidx / CH, cc = cidx % CH;
-      const int key = k0 + r;
-      u32x4 kv = {0, 0, 0, 0};
-      if (key < Lk) kv = load16(kp + (size_t)key * k_rs + cc * 8);
-      store16(&Ks[r * KSTR + cc * 8], kv);
-    }
+  size_t lse_row0;  // index of row 0 of this sequence in the LSE of head 0
+  size_t lse_hs;    // LSE stride between heads
+  if constexpr (VARLEN) {
+    lse_hs = (size_t)a.cu_q[a.B];
+    lse_row0 = (size_t)q_start;
+  } else {
+    lse_hs = (size_t)a.Sq;
+    lse_row0 = (size_t)b * a.Hq * a.Sq;
   }
+
+  // Query rows that can see a key of this block: i >= k0 - diag.  The work is the flat
+  // list of (query head of the group, 32-row query block) steps.
+  int qb_begin = 0;
+  if constexpr (CAUSAL) qb_begin = max(0, k0 - diag) / kBwdBQ;
+  const int qb_end = (Lq + kBwdBQ - 1) / kBwdBQ;
+  const int nqs = max(0, qb_end - qb_begin);
+  const int nsteps = G * nqs;
+
+  // Direct global->LDS fetch of step it's Q, dO tiles and per-row LSE, Dsum.  Rows past
+  // the end of the sequence re-read its last row (they are masked to P = 0).
+  auto fetch = [&](int it, int buf) {
+    const int g = it / nqs;
+    const int h = hk * G + g;
+    const int i0 = (qb_begin + it % nqs) * kBwdBQ;
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
+    const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * D;
+#pragma unroll
+    for (int i = 0; i < QT / 8 / 256; ++i) {
+      const int first = (i * kBwdWaves + wave) * 64;
+      const int chunk = first + lane;
+      const int r = chunk / Swz::CH;
+      const int p = chunk % Swz::CH;
+      const size_t src = (size_t)min(i0 + r, Lq - 1) * q_rs + Swz::chunk(r, p) * 8;
+      lds_direct_load16(qp + src, &Qs[buf][first * 8]);
+      lds_direct_load16(dop + src, &dOs[buf][first * 8]);
+    }
+    const int row = min(i0 + (lane & 31), Lq - 1);
+    if (wave == 0) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, &lse_s[buf][0]);
+    if (wave == 1) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, &dsum_s[buf][0]);
+  };
+
+  if (nsteps > 0) fetch(0, 0);
+  // K tile (all 128 keys) in LDS for dQ = dS K.
+#pragma unroll
+  for (int i = 0; i < kBwdBN * D / 8 / 256; ++i) {
+    const int first = (i * kBwdWaves + wave) * 64;
+    const int chunk = first + lane;
+    const int r = chunk / Swz::CH;
+    const int p = chunk % Swz::CH;
+    lds_direct_load16(kp + (size_t)min(k0 + r, Lk - 1) * k_rs + Swz::chunk(r, p) * 8, &Ks[first * 8]);
+  }
+
   // This wavefront's keys as B operands: lane holds K[key][16 s + 8 lh .. +7].
   const int my_key = k0 + wave * 32 + li;
   const bool key_ok = my_key < Lk;
@@ -153,140 +184,111 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     dvt[d] = f32x16{};
   }
 
-  // Query rows that can see a key of this block: i >= k0 - diag.
-  int qb_begin = 0;
-  if constexpr (CAUSAL) qb_begin = max(0, k0 - diag) / kBwdBQ;
-  const int qb_end = (Lq + kBwdBQ - 1) / kBwdBQ;
-
   const int tr_row = 4 * lh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  for (int g = 0; g < G; ++g) {
-    const int h = hk * G + g;
-    const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
-    const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * D;
-    for (int qb = qb_begin; qb < qb_end; ++qb) {
-      const int i0 = qb * kBwdBQ;
-      __syncthreads();  // previous step is done with Qs, dOs, dSs
-      {
-        constexpr int CH = D / 8;
-        for (int cidx = tid; cidx < kBwdBQ * CH; cidx += 256) {
-          const int r = cidx / CH, cc = cidx % CH;
-          const int row = i0 + r;
-          u32x4 qv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
-          if (row < Lq) {
-            qv = load16(qp + (size_t)row * q_rs + cc * 8);
-            gv = load16(dop + (size_t)row * q_rs + cc * 8);
-          }
-          store16(&Qs[r * QSTR + cc * 8], qv);
-          store16(&dOs[r * QSTR + cc * 8], gv);
-        }
-        if (tid < kBwdBQ) {
-          const int row = i0 + tid;
-          float l2 = INFINITY, ds = 0.f;
-          if (row < Lq) {
-            size_t li_idx;
-            if constexpr (VARLEN) {
-              li_idx = (size_t)h * a.cu_q[a.B] + q_start + row;
-            } else {
-              li_idx = ((size_t)b * a.Hq + h) * a.Sq + row;
-            }
-            l2 = a.lse[li_idx] * kLog2e;
-            ds = a.dsum[(size_t)(q_start + row) * a.Hq + h];
-          }
-          lse2_s[tid] = l2;
-          dsum_s[tid] = ds;
-        }
-      }
-      __syncthreads();
+  wait_all_memory();
+  __syncthreads();
 
-      // S = Q K^T and dP = dO V^T (query rows x keys); lane = key, registers = rows.
-      f32x16 s = f32x16{}, dp = f32x16{};
+  for (int it = 0; it < nsteps; ++it) {
+    const int buf = it & 1;
+    const int h = hk * G + it / nqs;
+    const int i0 = (qb_begin + it % nqs) * kBwdBQ;
+    if (it + 1 < nsteps) fetch(it + 1, buf ^ 1);
+    const uint16_t* Q = Qs[buf];
+    const uint16_t* dO = dOs[buf];
+
+    // S = Q K^T and dP = dO V^T (query rows x keys); lane = key, registers = rows.
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        Frag8 qa, ga;
-        qa.v = load16(&Qs[li * QSTR + st * 16 + lh * 8]);
-        ga.v = load16(&dOs[li * QSTR + st * 16 + lh * 8]);
-        s = mfma32x32x16<BF16>(qa, kf[st], s);
-        dp = mfma32x32x16<BF16>(ga, vf[st], dp);
+    for (int st = 0; st < NS; ++st) {
+      Frag8 qa, ga;
+      const int off = Swz::row_elem(li, st * 2 + lh);
+      qa.v = load16(Q + off);
+      ga.v = load16(dO + off);
+      s = mfma32x32x16<BF16>(qa, kf[st], s);
+      dp = mfma32x32x16<BF16>(ga, vf[st], dp);
+    }
+    // P and dS (scale folded in).
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rl = 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int row = i0 + rl;
+      bool keep = key_ok && row < Lq;
+      if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
+      const float p = keep ? fast_exp2(fmaf(s[r], c, -lse_s[buf][rl] * kLog2e)) : 0.f;
+      s[r] = p;
+      dp[r] = a.scale * p * (dp[r] - dsum_s[buf][rl]);
+    }
+    Frag8 pf[2], dsf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = 8 * t;
+      pf[t].v = u32x4{pack2<BF16>(s[r0 + 0], s[r0 + 1]), pack2<BF16>(s[r0 + 2], s[r0 + 3]),
+                      pack2<BF16>(s[r0 + 4], s[r0 + 5]), pack2<BF16>(s[r0 + 6], s[r0 + 7])};
+      dsf[t].v = u32x4{pack2<BF16>(dp[r0 + 0], dp[r0 + 1]), pack2<BF16>(dp[r0 + 2], dp[r0 + 3]),
+                       pack2<BF16>(dp[r0 + 4], dp[r0 + 5]), pack2<BF16>(dp[r0 + 6], dp[r0 + 7])};
+    }
+    // dS to LDS as [row][key] for the dQ product.
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t two = dsf[t].v[w];
+        const int r = 8 * t + 2 * w;  // registers r and r+1 of this lane
+        const int rl0 = 8 * (r >> 2) + 4 * lh + (r & 3);
+        dSs[rl0 * SSTR + wave * 32 + li] = (uint16_t)(two & 0xffff);
+        dSs[(rl0 + 1) * SSTR + wave * 32 + li] = (uint16_t)(two >> 16);
       }
-      // P and dS (scale folded in).
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS.
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const int row = t * 16 + tr_row;
+        const int col = d * 32 + tr_col;
+        const int o_lo = Swz::elem(row, col), o_hi = Swz::elem(row + 8, col);
+        const u32x2 g_lo = lds_read_tr16(dO + o_lo);
+        const u32x2 g_hi = lds_read_tr16(dO + o_hi);
+        const u32x2 q_lo = lds_read_tr16(Q + o_lo);
+        const u32x2 q_hi = lds_read_tr16(Q + o_hi);
+        Frag8 ga, qa;
+        ga.v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
+        qa.v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
+        dvt[d] = mfma32x32x16<BF16>(ga, pf[t], dvt[d]);
+        dkt[d] = mfma32x32x16<BF16>(qa, dsf[t], dkt[d]);
+      }
+    }
+    __syncthreads();  // dS of all four wavefronts is in LDS
+
+    // dQ[rows][d-block] = dS[rows][128 keys] K[128 keys][d-block]; d-blocks are dealt
+    // round-robin to the wavefronts.
+    for (int d = wave; d < ND; d += kBwdWaves) {
+      f32x16 dq = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < kBwdBN / 16; ++ks) {
+        Frag8 sa, kb2;
+        sa.v = load16(&dSs[li * SSTR + ks * 16 + lh * 8]);
+        const int krow = ks * 16 + 8 * lh + ((lane & 15) >> 2);
+        const int kcol = d * 32 + tr_col;
+        const u32x2 lo = lds_read_tr16(&Ks[Swz::elem(krow, kcol)]);
+        const u32x2 hi = lds_read_tr16(&Ks[Swz::elem(krow + 4, kcol)]);
+        kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+        dq = mfma32x32x16<BF16>(sa, kb2, dq);
+      }
+      // lane = column d*32 + li; registers = rows.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rl = 8 * (r >> 2) + 4 * lh + (r & 3);
-        const int row = i0 + rl;
-        bool keep = key_ok && row < Lq;
-        if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
-        const float p = keep ? fast_exp2(fmaf(s[r], c, -lse2_s[rl])) : 0.f;
-        s[r] = p;
-        dp[r] = a.scale * p * (dp[r] - dsum_s[rl]);
-      }
-      Frag8 pf[2], dsf[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r0 = 8 * t;
-        pf[t].v = u32x4{pack2<BF16>(s[r0 + 0], s[r0 + 1]), pack2<BF16>(s[r0 + 2], s[r0 + 3]),
-                        pack2<BF16>(s[r0 + 4], s[r0 + 5]), pack2<BF16>(s[r0 + 6], s[r0 + 7])};
-        dsf[t].v = u32x4{pack2<BF16>(dp[r0 + 0], dp[r0 + 1]), pack2<BF16>(dp[r0 + 2], dp[r0 + 3]),
-                         pack2<BF16>(dp[r0 + 4], dp[r0 + 5]), pack2<BF16>(dp[r0 + 6], dp[r0 + 7])};
-      }
-      // dS to LDS as [row][key] for the dQ product.
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t two = dsf[t].v[w];
-          const int r = 8 * t + 2 * w;  // registers r and r+1 of this lane
-          const int rl0 = 8 * (r >> 2) + 4 * lh + (r & 3);
-          dSs[rl0 * SSTR + wave * 32 + li] = (uint16_t)(two & 0xffff);
-          dSs[(rl0 + 1) * SSTR + wave * 32 + li] = (uint16_t)(two >> 16);
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS.
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const int off = (t * 16 + tr_row) * QSTR + d * 32 + tr_col;
-          const u32x2 g_lo = lds_read_tr16(&dOs[off]);
-          const u32x2 g_hi = lds_read_tr16(&dOs[off + 8 * QSTR]);
-          const u32x2 q_lo = lds_read_tr16(&Qs[off]);
-          const u32x2 q_hi = lds_read_tr16(&Qs[off + 8 * QSTR]);
-          Frag8 ga, qa;
-          ga.v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
-          qa.v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
-          dvt[d] = mfma32x32x16<BF16>(ga, pf[t], dvt[d]);
-          dkt[d] = mfma32x32x16<BF16>(qa, dsf[t], dkt[d]);
-        }
-      }
-      __syncthreads();  // dS of all four wavefronts is in LDS
-
-      // dQ[rows][d-block] = dS[rows][128 keys] K[128 keys][d-block]; d-blocks are dealt
-      // round-robin to the wavefronts.
-      for (int d = wave; d < ND; d += kBwdWaves) {
-        f32x16 dq = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < kBwdBN / 16; ++ks) {
-          Frag8 sa, kb2;
-          sa.v = load16(&dSs[li * SSTR + ks * 16 + lh * 8]);
-          const int krow = ks * 16 + 8 * lh + ((lane & 15) >> 2);
-          const int kcol = d * 32 + tr_col;
-          const u32x2 lo = lds_read_tr16(&Ks[krow * KSTR + kcol]);
-          const u32x2 hi = lds_read_tr16(&Ks[(krow + 4) * KSTR + kcol]);
-          kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
-          dq = mfma32x32x16<BF16>(sa, kb2, dq);
-        }
-        // lane = column d*32 + li; registers = rows.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-          if (row < Lq) {
-            float* dst = a.dq_acc + ((size_t)(q_start + row) * a.Hq + h) * D + d * 32 + li;
-            unsafeAtomicAdd(dst, dq[r]);
-          }
+        const int row = i0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (row < Lq) {
+          float* dst = a.dq_acc + ((size_t)(q_start + row) * a.Hq + h) * D + d * 32 + li;
+          unsafeAtomicAdd(dst, dq[r]);
         }
       }
     }
+    wait_all_memory();  // the prefetched step has landed in LDS
+    __syncthreads();    // every wavefront is done with this step's tiles and dS
   }
 
   // dK, dV: lane = key, registers = head-dimension entries.
@@ -305,6 +307,300 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
         wv.y = pack2<BF16>(dvt[d][4 * gq + 2], dvt[d][4 * gq + 3]);
         *(u32x2*)(dkp + col) = wk;
         *(u32x2*)(dvp + col) = wv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 2b. main loop, 8 waves
+
+// Head dimensions up to 128: eight wavefronts per workgroup and 64-row query steps.
+// Wavefront w owns key group w % 4 (32 keys) and row half w / 4 (32 of the 64 rows), so
+// the two wavefronts of a key group accumulate partial dK, dV over different rows; the
+// partials are summed through LDS once, after the loop.  K and V operands are re-read
+// from LDS instead of being held in registers, which keeps a wavefront within 256
+// registers: two wavefronts per SIMD hide each other's latencies.
+constexpr int kW8Waves = 8;
+constexpr int kW8BQ = 64;
+
+template <int D>
+struct W8Lds {
+  static constexpr int SSTR = kBwdBN + 8;
+  static constexpr int KV = kBwdBN * D * 2;      // bytes of the K or V tile
+  static constexpr int QT = kW8BQ * D * 2;       // bytes of one Q or dO tile
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = K_OFF + KV;
+  static constexpr int Q_OFF = V_OFF + KV;       // 2 buffers
+  static constexpr int DO_OFF = Q_OFF + 2 * QT;  // 2 buffers
+  static constexpr int DS_OFF = DO_OFF + 2 * QT;
+  static constexpr int LSE_OFF = DS_OFF + kW8BQ * SSTR * 2;  // float[2][64]
+  static constexpr int DSUM_OFF = LSE_OFF + 2 * 64 * 4;
+  static constexpr int BYTES = DSUM_OFF + 2 * 64 * 4;
+  static constexpr int RED_BYTES = 4 * 2 * 32 * D * 4;  // fp32 dK, dV partials of 4 wavefronts
+  static_assert(RED_BYTES <= DS_OFF, "partial sums reuse the tile area");
+};
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  using L = W8Lds<D>;
+  constexpr int SSTR = L::SSTR;
+  using Swz = DualSwizzle<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
+  uint16_t* Ks = (uint16_t*)(smem + L::K_OFF);
+  uint16_t* Vs = (uint16_t*)(smem + L::V_OFF);
+  uint16_t* dSs = (uint16_t*)(smem + L::DS_OFF);
+  float* lse_s = (float*)(smem + L::LSE_OFF);
+  float* dsum_s = (float*)(smem + L::DSUM_OFF);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+  const int kg = wave & 3;   // key group
+  const int rh = wave >> 2;  // row half of the query step
+
+  const int nbh = a.B * a.Hkv;
+  const int kb = blockIdx.x / nbh;
+  const int bh = blockIdx.x % nbh;
+  const int hk = bh % a.Hkv;
+  const int b = bh / a.Hkv;
+
+  int q_start, k_start, Lq, Lk;
+  if constexpr (VARLEN) {
+    q_start = a.cu_q[b];
+    Lq = a.cu_q[b + 1] - q_start;
+    k_start = a.cu_k[b];
+    Lk = a.cu_k[b + 1] - k_start;
+  } else {
+    q_start = b * a.Sq;
+    Lq = a.Sq;
+    k_start = b * a.Sk;
+    Lk = a.Sk;
+  }
+  const int k0 = kb * kBwdBN;
+  if (k0 >= Lk) return;  // uniform
+
+  const int G = a.Hq / a.Hkv;
+  const size_t q_rs = (size_t)a.Hq * D;
+  const size_t k_rs = (size_t)a.Hkv * D;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+  const int diag = Lk - Lq;
+  const float c = a.scale_log2;
+  constexpr float kLog2e = 1.4426950408889634f;
+  size_t lse_row0, lse_hs;
+  if constexpr (VARLEN) {
+    lse_hs = (size_t)a.cu_q[a.B];
+    lse_row0 = (size_t)q_start;
+  } else {
+    lse_hs = (size_t)a.Sq;
+    lse_row0 = (size_t)b * a.Hq * a.Sq;
+  }
+
+  int qb_begin = 0;
+  if constexpr (CAUSAL) qb_begin = max(0, k0 - diag) / kW8BQ;
+  const int qb_end = (Lq + kW8BQ - 1) / kW8BQ;
+  const int nqs = max(0, qb_end - qb_begin);
+  const int nsteps = G * nqs;
+
+  auto fetch = [&](int it, int buf) {
+    const int h = hk * G + it / nqs;
+    const int i0 = (qb_begin + it % nqs) * kW8BQ;
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
+    const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * D;
+    uint16_t* Qd = (uint16_t*)(smem + L::Q_OFF + buf * L::QT);
+    uint16_t* dOd = (uint16_t*)(smem + L::DO_OFF + buf * L::QT);
+#pragma unroll
+    for (int i = 0; i < kW8BQ * D / 8 / 512; ++i) {
+      const int first = (i * kW8Waves + wave) * 64;
+      const int chunk = first + lane;
+      const int r = chunk / Swz::CH;
+      const int p = chunk % Swz::CH;
+      const size_t src = (size_t)min(i0 + r, Lq - 1) * q_rs + Swz::chunk(r, p) * 8;
+      lds_direct_load16(qp + src, Qd + first * 8);
+      lds_direct_load16(dop + src, dOd + first * 8);
+    }
+    const int row = min(i0 + lane, Lq - 1);
+    if (wave == 0) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, lse_s + buf * 64);
+    if (wave == 1) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, dsum_s + buf * 64);
+  };
+
+  if (nsteps > 0) fetch(0, 0);
+#pragma unroll
+  for (int i = 0; i < kBwdBN * D / 8 / 512; ++i) {
+    const int first = (i * kW8Waves + wave) * 64;
+    const int chunk = first + lane;
+    const int r = chunk / Swz::CH;
+    const int p = chunk % Swz::CH;
+    const size_t src = (size_t)min(k0 + r, Lk - 1) * k_rs + Swz::chunk(r, p) * 8;
+    lds_direct_load16(kp + src, Ks + first * 8);
+    lds_direct_load16(vp + src, Vs + first * 8);
+  }
+
+  const int my_key = k0 + kg * 32 + li;
+  const bool key_ok = my_key < Lk;
+  f32x16 dkt[ND], dvt[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    dkt[d] = f32x16{};
+    dvt[d] = f32x16{};
+  }
+  const int tr_row = 4 * lh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  wait_all_memory();
+  __syncthreads();
+
+  for (int it = 0; it < nsteps; ++it) {
+    const int buf = it & 1;
+    const int h = hk * G + it / nqs;
+    const int i0 = (qb_begin + it % nqs) * kW8BQ;
+    if (it + 1 < nsteps) fetch(it + 1, buf ^ 1);
+    const uint16_t* Q = (const uint16_t*)(smem + L::Q_OFF + buf * L::QT);
+    const uint16_t* dO = (const uint16_t*)(smem + L::DO_OFF + buf * L::QT);
+    const float* lse_b = lse_s + buf * 64 + rh * 32;
+    const float* dsum_b = dsum_s + buf * 64 + rh * 32;
+    const int wrow0 = i0 + rh * 32;  // first query row of this wavefront
+
+    // S = Q K^T, dP = dO V^T for this wavefront's 32 rows x 32 keys.
+    f32x16 s = f32x16{}, dp = f32x16{};
+    const bool live = !(CAUSAL && k0 + kg * 32 > wrow0 + 31 + diag);  // some key visible
+    if (live) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        Frag8 qa, ga, kf, vf;
+        const int qo = Swz::row_elem(rh * 32 + li, st * 2 + lh);
+        const int ko = Swz::row_elem(kg * 32 + li, st * 2 + lh);
+        qa.v = load16(Q + qo);
+        ga.v = load16(dO + qo);
+        kf.v = load16(Ks + ko);
+        vf.v = load16(Vs + ko);
+        s = mfma32x32x16<BF16>(qa, kf, s);
+        dp = mfma32x32x16<BF16>(ga, vf, dp);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rl = 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int row = wrow0 + rl;
+      bool keep = live && key_ok && row < Lq;
+      if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
+      const float p = keep ? fast_exp2(fmaf(s[r], c, -lse_b[rl] * kLog2e)) : 0.f;
+      s[r] = p;
+      dp[r] = a.scale * p * (dp[r] - dsum_b[rl]);
+    }
+    Frag8 pf[2], dsf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = 8 * t;
+      pf[t].v = u32x4{pack2<BF16>(s[r0 + 0], s[r0 + 1]), pack2<BF16>(s[r0 + 2], s[r0 + 3]),
+                      pack2<BF16>(s[r0 + 4], s[r0 + 5]), pack2<BF16>(s[r0 + 6], s[r0 + 7])};
+      dsf[t].v = u32x4{pack2<BF16>(dp[r0 + 0], dp[r0 + 1]), pack2<BF16>(dp[r0 + 2], dp[r0 + 3]),
+                       pack2<BF16>(dp[r0 + 4], dp[r0 + 5]), pack2<BF16>(dp[r0 + 6], dp[r0 + 7])};
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t two = dsf[t].v[w];
+        const int r = 8 * t + 2 * w;
+        const int rl0 = rh * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        dSs[rl0 * SSTR + kg * 32 + li] = (uint16_t)(two & 0xffff);
+        dSs[(rl0 + 1) * SSTR + kg * 32 + li] = (uint16_t)(two >> 16);
+      }
+    }
+    if (live) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const int row = rh * 32 + t * 16 + tr_row;
+          const int col = d * 32 + tr_col;
+          const int o_lo = Swz::elem(row, col), o_hi = Swz::elem(row + 8, col);
+          const u32x2 g_lo = lds_read_tr16(dO + o_lo);
+          const u32x2 g_hi = lds_read_tr16(dO + o_hi);
+          const u32x2 q_lo = lds_read_tr16(Q + o_lo);
+          const u32x2 q_hi = lds_read_tr16(Q + o_hi);
+          Frag8 ga, qa;
+          ga.v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
+          qa.v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
+          dvt[d] = mfma32x32x16<BF16>(ga, pf[t], dvt[d]);
+          dkt[d] = mfma32x32x16<BF16>(qa, dsf[t], dkt[d]);
+        }
+      }
+    }
+    __syncthreads();  // dS of all eight wavefronts is in LDS
+
+    // dQ[64 rows][D] = dS[64 rows][128 keys] K[128 keys][D]: 2 x ND tiles of 32 x 32.
+    for (int tile = wave; tile < 2 * ND; tile += kW8Waves) {
+      const int rq = tile & 1, d = tile >> 1;
+      const int qrow0 = i0 + rq * 32;
+      if (qrow0 >= Lq) continue;
+      if (CAUSAL && k0 > qrow0 + 31 + diag) continue;  // no key of the block visible
+      f32x16 dq = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < kBwdBN / 16; ++ks) {
+        Frag8 sa, kb2;
+        sa.v = load16(&dSs[(rq * 32 + li) * SSTR + ks * 16 + lh * 8]);
+        const int krow = ks * 16 + 8 * lh + ((lane & 15) >> 2);
+        const int kcol = d * 32 + tr_col;
+        const u32x2 lo = lds_read_tr16(Ks + Swz::elem(krow, kcol));
+        const u32x2 hi = lds_read_tr16(Ks + Swz::elem(krow + 4, kcol));
+        kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+        dq = mfma32x32x16<BF16>(sa, kb2, dq);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = qrow0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (row < Lq) {
+          float* dst = a.dq_acc + ((size_t)(q_start + row) * a.Hq + h) * D + d * 32 + li;
+          unsafeAtomicAdd(dst, dq[r]);
+        }
+      }
+    }
+    wait_all_memory();
+    __syncthreads();
+  }
+
+  // Sum the two row halves' partial dK, dV through LDS (the tile area is free now).
+  float* red = (float*)smem + (size_t)kg * (2 * 32 * D);
+  if (rh == 1) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        red[(d * 16 + r) * 64 + lane] = dkt[d][r];
+        red[32 * D + (d * 16 + r) * 64 + lane] = dvt[d][r];
+      }
+  }
+  __syncthreads();
+  if (rh == 0) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dkt[d][r] += red[(d * 16 + r) * 64 + lane];
+        dvt[d][r] += red[32 * D + (d * 16 + r) * 64 + lane];
+      }
+    if (key_ok) {
+      uint16_t* dkp = (uint16_t*)a.dk + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
+      uint16_t* dvp = (uint16_t*)a.dv + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = d * 32 + 8 * gq + 4 * lh;
+          u32x2 wk, wv;
+          wk.x = pack2<BF16>(dkt[d][4 * gq + 0], dkt[d][4 * gq + 1]);
+          wk.y = pack2<BF16>(dkt[d][4 * gq + 2], dkt[d][4 * gq + 3]);
+          wv.x = pack2<BF16>(dvt[d][4 * gq + 0], dvt[d][4 * gq + 1]);
+          wv.y = pack2<BF16>(dvt[d][4 * gq + 2], dvt[d][4 * gq + 3]);
+          *(u32x2*)(dkp + col) = wk;
+          *(u32x2*)(dvp + col) = wv;
+        }
       }
     }
   }
@@ -348,7 +644,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   if (stages & 2) {
     const int nkb = (a.Sk + kBwdBN - 1) / kBwdBN;
     const dim3 grid((unsigned)nkb * a.B * a.Hkv);
-    hipLaunchKernelGGL((bwd_main_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(256), 0, stream, a);
+    if constexpr (D <= 128) {
+      hipLaunchKernelGGL((bwd_main_w8_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(512), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((bwd_main_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(256), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

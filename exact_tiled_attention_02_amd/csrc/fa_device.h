@@ -78,6 +78,11 @@ __device__ __forceinline__ void lds_direct_load16(const void* gptr, void* lds_ba
   __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_base, 16, 0, 0);
 }
 
+// 4 bytes per lane straight into LDS (global_load_lds_dword): lane l writes lds_base + 4*l.
+__device__ __forceinline__ void lds_direct_load4(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_base, 4, 0, 0);
+}
+
 // Wait until every outstanding memory operation of this wavefront has completed
 // (including direct global->LDS loads).
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
@@ -114,6 +119,23 @@ struct TileSwizzle {
   __device__ static __forceinline__ int k_elem(int r, int c) { return r * D + k(r, c) * 8; }
   // element offset of logical element e of row r (V layout)
   __device__ static __forceinline__ int v_elem(int r, int e) { return r * D + v(r, e >> 3) * 8 + (e & 7); }
+};
+
+// One layout serving both read patterns on the same tile: 16-byte row reads of 16
+// consecutive rows (MFMA operands taken along the head dimension) and transposed 8-byte
+// reads of 4 consecutive rows x 4 consecutive chunks (operands taken along the rows).
+// f(r) is a bijection on 16 consecutive rows whose low two bits of r select the 4-chunk
+// group, so both patterns land on 16 distinct 4-bank groups.
+template <int D>
+struct DualSwizzle {
+  static constexpr int CH = D / 8;
+  __device__ static __forceinline__ int f(int r) {
+    if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return ((r & 3) << 2) | ((r >> 2) & 3);
+  }
+  __device__ static __forceinline__ int chunk(int r, int c) { return c ^ f(r); }
+  __device__ static __forceinline__ int row_elem(int r, int c) { return r * D + chunk(r, c) * 8; }
+  __device__ static __forceinline__ int elem(int r, int e) { return r * D + chunk(r, e >> 3) * 8 + (e & 7); }
 };
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
