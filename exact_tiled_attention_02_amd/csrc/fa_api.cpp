@@ -65,6 +65,16 @@ int hip_status(hipError_t e, const char* what) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Factor applied to raw scores before exp2: scale * log2(e), but at least 1e-30 so that
+// it is strictly positive.  The kernels then mask a score by setting it to -inf
+// (exp2(-inf * c) = 0 needs c > 0).  For scale = 0 the clamp changes nothing: every
+// |score * 1e-30| is far below half an ulp of 1, so each kept weight is exactly 1.0f, as
+// with a zero scale; the LSE and the gradients use the true scale.
+float exp2_scale(float scale) {
+  const float c = scale * kLog2e;
+  return c < 1e-30f ? 1e-30f : c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,7 +118,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   a.causal = causal ? 1 : 0;
   a.bf16 = dtype == FA_DTYPE_BF16;
   a.scale = scale;
-  a.scale_log2 = scale * kLog2e;
+  a.scale_log2 = exp2_scale(scale);
   return hip_status(fa::launch_fwd(a, stream), "fa_fwd launch");
 }
 
@@ -162,7 +172,7 @@ int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, con
   a.causal = causal ? 1 : 0;
   a.bf16 = dtype == FA_DTYPE_BF16;
   a.scale = scale;
-  a.scale_log2 = scale * kLog2e;
+  a.scale_log2 = exp2_scale(scale);
   return hip_status(fa::launch_bwd(a, stage_mask, stream), "fa_bwd launch");
 }
 

@@ -13,8 +13,9 @@
 //   * per key tile: S^T = K Q^T on MFMA (fp32 accumulate), masking only on tiles that
 //     touch the causal diagonal or the sequence tail, a running row max m and row sum l,
 //     P = exp2(S * scale*log2(e) - m * scale*log2(e)) (one FMA + exp2), rescaling of the
-//     output accumulator by exp2((m_old - m_new) * scale*log2(e)) on every tile (exact;
-//     never skipped), then O^T += V^T P^T on MFMA with P rounded once to 16 bits;
+//     output accumulator by exp2((m_old - m_new) * scale*log2(e)) on every tile (exact:
+//     only a multiplication by exactly 1.0f is left out), then O^T += V^T P^T on MFMA
+//     with P rounded once to 16 bits;
 //   * a row max of -inf (nothing kept yet) is replaced by 0 so that no (-inf) - (-inf)
 //     appears;
 //   * epilogue: O = acc / l, LSE = m * scale + ln l; a row that kept no key writes O = 0
@@ -27,9 +28,11 @@
 // the A operand of that product, is read from the row-major V tile with
 // ds_read_b64_tr_b16.
 //
-// LDS tiles are unpadded and XOR-swizzled on 16-byte chunks (see TileSwizzle), which is
+// LDS tiles are unpadded and XOR-swizzled on 16-byte chunks (see DualSwizzle), which is
 // what a direct global->LDS load can produce and keeps both read patterns free of bank
 // conflicts.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_params.h"
 
@@ -45,13 +48,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   constexpr int NS = D / 16;  // 16-wide slices of the head dimension (QK^T depth)
   constexpr int ND = D / 32;  // 32-wide blocks of the head dimension (output tiles)
   constexpr int TILE = kFwdBN * D;  // elements per K or V tile
-  using Swz = TileSwizzle<D>;
+  using Swz = DualSwizzle<D>;
   __shared__ __attribute__((aligned(16))) uint16_t Kt[2][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
   const int li = lane & 31;
   const int lh = lane >> 5;
 
@@ -97,20 +100,39 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const bool row_ok = my_row < Lq;
   const int wave_row0 = q0 + wave * 32;
 
-  // Direct global->LDS fetch of key/value tile kb into buffer buf.  Rows past the end of
-  // the sequence re-read its last row (finite data; those keys are masked to P = 0).
+  // Direct global->LDS fetch of key/value tile kb into buffer buf.  The per-lane source
+  // offsets do not depend on the tile; only a tile reaching past the end of the
+  // sequence needs its rows clamped (they re-read the last row: finite data, masked to
+  // P = 0).
+  constexpr int NI = TILE / 8 / 256;  // direct loads per wavefront per tensor
+  int foff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int chunk = (i * kFwdWaves + wave) * 64 + lane;
+    const int r = chunk / Swz::CH;
+    foff[i] = r * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
+  }
   auto fetch = [&](int kb, int buf) {
     const int k0 = kb * kFwdBN;
+    const uint16_t* kt = kp + (size_t)k0 * k_rs;
+    const uint16_t* vt = vp + (size_t)k0 * k_rs;
+    if (k0 + kFwdBN <= Lk) {
 #pragma unroll
-    for (int i = 0; i < TILE / 8 / 256; ++i) {
-      const int first = (i * kFwdWaves + wave) * 64;  // first chunk written by this instruction
-      const int chunk = first + lane;
-      const int r = chunk / Swz::CH;
-      const int p = chunk % Swz::CH;
-      const int key = min(k0 + r, Lk - 1);
-      const size_t src = (size_t)key * k_rs;
-      lds_direct_load16(kp + src + Swz::k(r, p) * 8, &Kt[buf][first * 8]);
-      lds_direct_load16(vp + src + Swz::v(r, p) * 8, &Vt[buf][first * 8]);
+      for (int i = 0; i < NI; ++i) {
+        const int first = (i * kFwdWaves + wave) * 64;
+        lds_direct_load16(kt + foff[i], &Kt[buf][first * 8]);
+        lds_direct_load16(vt + foff[i], &Vt[buf][first * 8]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int first = (i * kFwdWaves + wave) * 64;
+        const int chunk = first + lane;
+        const int r = chunk / Swz::CH;
+        const int off = min(r, Lk - 1 - k0) * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
+        lds_direct_load16(kt + off, &Kt[buf][first * 8]);
+        lds_direct_load16(vt + off, &Vt[buf][first * 8]);
+      }
     }
   };
 
@@ -130,25 +152,34 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   float l_run = 0.f;
   const float c = a.scale_log2;
 
-  // Per-lane LDS element offsets of the MFMA operand reads (within a tile).
-  int koff[2][NS];
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-    for (int st = 0; st < NS; ++st) koff[sub][st] = Swz::k_elem(sub * 32 + li, st * 2 + lh);
   const int tr_row = 4 * lh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  // Per-lane LDS offsets of the operand reads, fixed for the whole loop: row reads of K
+  // (key row li, chunk 2 st + lh) and transposed reads of V (rows tr_row and tr_row + 8
+  // of each 16-key slice, columns d*32 + tr_col); a slice or sub-block only adds a
+  // constant.
+  int koff[NS], voff[2][ND];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) koff[st] = Swz::row_elem(li, st * 2 + lh);
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int d = 0; d < ND; ++d) voff[hi][d] = Swz::elem(tr_row + 8 * hi, d * 32 + tr_col);
 
   wait_all_memory();
   __syncthreads();
 
-  for (int kb = 0; kb < nkb; ++kb) {
+  // One key tile.  MASK selects the variant for tiles that touch the causal diagonal or
+  // the sequence tail; interior tiles carry no masking code at all.
+  auto tile = [&](int kb, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int cur = kb & 1;
     const int k0 = kb * kFwdBN;
     if (kb + 1 < nkb) fetch(kb + 1, cur ^ 1);
 
     // A wavefront whose rows keep no key of this tile has nothing to add.
-    if (!(CAUSAL && k0 > wave_row0 + 31 + diag)) {
+    if (!(MASK && CAUSAL && k0 > wave_row0 + 31 + diag)) {
       const uint16_t* K = Kt[cur];
       const uint16_t* V = Vt[cur];
       // S^T (keys x rows): two 32-key blocks.
@@ -159,17 +190,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           Frag8 kf;
-          kf.v = load16(K + koff[sub][st]);
+          kf.v = load16(K + sub * 32 * D + koff[st]);
           s[sub] = mfma32x32x16<BF16>(kf, qf[st], s[sub]);
         }
       }
 
-      // Masked scores become -inf for the row max; their probabilities are forced to 0
-      // after the exp (exp2(-inf * 0) would be NaN for a zero scale).
-      const bool need_mask = (k0 + kFwdBN > Lk) || (CAUSAL && k0 + kFwdBN - 1 > wave_row0 + diag);
-      uint32_t keep_bits = 0xffffffffu;
-      if (need_mask) {
-        keep_bits = 0;
+      // Masked scores become -inf, so their probabilities are exp2(-inf) = 0 (the factor c
+      // is strictly positive).  Only tiles touching the diagonal or the tail need it.
+      if constexpr (MASK) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
@@ -177,7 +205,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
             bool keep = key < Lk;
             if constexpr (CAUSAL) keep = keep && (key <= my_row + diag);
-            keep_bits |= (keep ? 1u : 0u) << (sub * 16 + r);
             s[sub][r] = keep ? s[sub][r] : -INFINITY;
           }
         }
@@ -199,14 +226,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(s[sub][r], c, -mc));
-          if (need_mask) p = ((keep_bits >> (sub * 16 + r)) & 1u) ? p : 0.f;
+            const float p = fast_exp2(fmaf(s[sub][r], c, -mc));
           s[sub][r] = p;
           ls += p;
         }
       l_run = l_run * alpha + ls;
+      // Rescale the accumulator; when no row of the wavefront changed its maximum every
+      // factor is exactly 1.0f and the multiplication is skipped (bitwise identical).
+      if (__builtin_expect(__any(alpha != 1.f), 0)) {
 #pragma unroll
-      for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+        for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+      }
 
       // P^T as the B operand of O^T += V^T P^T: slice t covers keys 16t .. 16t+15; lane
       // position p of half lh stands for key 16t + 8(p/4) + 4lh + p%4.
@@ -221,10 +251,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       for (int t = 0; t < 4; ++t) {
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const int row = t * 16 + tr_row;
-          const int col = d * 32 + tr_col;
-          const u32x2 lo = lds_read_tr16(V + Swz::v_elem(row, col));
-          const u32x2 hi = lds_read_tr16(V + Swz::v_elem(row + 8, col));
+          const u32x2 lo = lds_read_tr16(V + t * 16 * D + voff[0][d]);
+          const u32x2 hi = lds_read_tr16(V + t * 16 * D + voff[1][d]);
           Frag8 vf;
           vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
           acc[d] = mfma32x32x16<BF16>(vf, pf[t], acc[d]);
@@ -233,7 +261,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
     wait_all_memory();  // the prefetched tile has landed in LDS
     __syncthreads();    // ... and every wavefront is done with the current one
-  }
+  };
+
+  // Leading tiles that no row of the workgroup masks, then the diagonal / tail tiles.
+  int n_full = Lk / kFwdBN;
+  if constexpr (CAUSAL) n_full = min(n_full, q0 + diag + 1 >= 0 ? (q0 + diag + 1) / kFwdBN : 0);
+  n_full = min(n_full, nkb);
+  for (int kb = 0; kb < n_full; ++kb) tile(kb, std::false_type{});
+  for (int kb = n_full; kb < nkb; ++kb) tile(kb, std::true_type{});
 
   // Epilogue.
   const float l_tot = pair_sum(l_run);
