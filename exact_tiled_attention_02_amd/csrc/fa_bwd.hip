@@ -22,6 +22,8 @@
 //      with atomics;
 //   3. finalize: fp32 accumulator -> dQ in the input dtype.
 // The softmax scale is folded into dS once, so neither dK nor dQ is rescaled later.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_params.h"
 
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
   const int li = lane & 31;
   const int lh = lane >> 5;
   const int kg = wave & 3;   // key group
@@ -406,22 +408,40 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
   const int nqs = max(0, qb_end - qb_begin);
   const int nsteps = G * nqs;
 
+  // Per-lane source offsets of the direct loads of a Q / dO tile (fixed for the loop).
+  constexpr int NQI = kW8BQ * D / 8 / 512;
+  int qoff[NQI];
+#pragma unroll
+  for (int i = 0; i < NQI; ++i) {
+    const int chunk = (i * kW8Waves + wave) * 64 + lane;
+    const int r = chunk / Swz::CH;
+    qoff[i] = r * (int)q_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
+  }
   auto fetch = [&](int it, int buf) {
     const int h = hk * G + it / nqs;
     const int i0 = (qb_begin + it % nqs) * kW8BQ;
-    const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
-    const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * D;
+    const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * D;
+    const uint16_t* qt = (const uint16_t*)a.q + base;
+    const uint16_t* dot = (const uint16_t*)a.dout + base;
     uint16_t* Qd = (uint16_t*)(smem + L::Q_OFF + buf * L::QT);
     uint16_t* dOd = (uint16_t*)(smem + L::DO_OFF + buf * L::QT);
+    if (i0 + kW8BQ <= Lq) {
 #pragma unroll
-    for (int i = 0; i < kW8BQ * D / 8 / 512; ++i) {
-      const int first = (i * kW8Waves + wave) * 64;
-      const int chunk = first + lane;
-      const int r = chunk / Swz::CH;
-      const int p = chunk % Swz::CH;
-      const size_t src = (size_t)min(i0 + r, Lq - 1) * q_rs + Swz::chunk(r, p) * 8;
-      lds_direct_load16(qp + src, Qd + first * 8);
-      lds_direct_load16(dop + src, dOd + first * 8);
+      for (int i = 0; i < NQI; ++i) {
+        const int first = (i * kW8Waves + wave) * 64;
+        lds_direct_load16(qt + qoff[i], Qd + first * 8);
+        lds_direct_load16(dot + qoff[i], dOd + first * 8);
+      }
+    } else {  // rows past the end re-read the last row (masked to P = 0)
+#pragma unroll
+      for (int i = 0; i < NQI; ++i) {
+        const int first = (i * kW8Waves + wave) * 64;
+        const int chunk = first + lane;
+        const int r = chunk / Swz::CH;
+        const int off = min(r, Lq - 1 - i0) * (int)q_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
+        lds_direct_load16(qt + off, Qd + first * 8);
+        lds_direct_load16(dot + off, dOd + first * 8);
+      }
     }
     const int row = min(i0 + lane, Lq - 1);
     if (wave == 0) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, lse_s + buf * 64);
@@ -450,11 +470,28 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
   }
   const int tr_row = 4 * lh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Per-lane LDS offsets, fixed for the loop.  Row reads (row li of a 32-row block, chunk
+  // 2 st + lh) have the same swizzle for Q, dO, K and V because every block starts at a
+  // multiple of 16 rows; transposed reads of Q / dO (rows tr_row, tr_row + 8 of a 16-row
+  // slice, columns d*32 + tr_col) and of K for dQ (rows 8 lh + (lane%16)/4 and +4 of a
+  // 16-key slice) add a constant per slice.
+  int roff[NS], qtr[2][ND], ktr[2];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) roff[st] = Swz::row_elem(li, st * 2 + lh);
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int d = 0; d < ND; ++d) qtr[hi][d] = Swz::elem(tr_row + 8 * hi, d * 32 + tr_col);
+  const int dq_d = wave >> 1;  // d-block of this wavefront's dQ tile (when it has one)
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) ktr[hi] = Swz::elem(8 * lh + ((lane & 15) >> 2) + 4 * hi, dq_d * 32 + tr_col);
 
   wait_all_memory();
   __syncthreads();
 
-  for (int it = 0; it < nsteps; ++it) {
+  // One query step.  mask: the step touches the causal diagonal or a sequence end (a
+  // uniform flag; the masking code sits behind a branch the other steps skip).
+  auto step = [&](int it, bool mask) {
     const int buf = it & 1;
     const int h = hk * G + it / nqs;
     const int i0 = (qb_begin + it % nqs) * kW8BQ;
@@ -465,32 +502,45 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
     const float* dsum_b = dsum_s + buf * 64 + rh * 32;
     const int wrow0 = i0 + rh * 32;  // first query row of this wavefront
 
-    // S = Q K^T, dP = dO V^T for this wavefront's 32 rows x 32 keys.
+    // S = Q K^T, dP = dO V^T for this wavefront's 32 rows x 32 keys (lane = key,
+    // registers = rows 8(r/4) + 4 lh + r%4).
+    bool live = true;
+    if constexpr (CAUSAL) live = !mask || k0 + kg * 32 <= wrow0 + 31 + diag;  // some key visible
     f32x16 s = f32x16{}, dp = f32x16{};
-    const bool live = !(CAUSAL && k0 + kg * 32 > wrow0 + 31 + diag);  // some key visible
     if (live) {
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         Frag8 qa, ga, kf, vf;
-        const int qo = Swz::row_elem(rh * 32 + li, st * 2 + lh);
-        const int ko = Swz::row_elem(kg * 32 + li, st * 2 + lh);
-        qa.v = load16(Q + qo);
-        ga.v = load16(dO + qo);
-        kf.v = load16(Ks + ko);
-        vf.v = load16(Vs + ko);
+        qa.v = load16(Q + rh * 32 * D + roff[st]);
+        ga.v = load16(dO + rh * 32 * D + roff[st]);
+        kf.v = load16(Ks + kg * 32 * D + roff[st]);
+        vf.v = load16(Vs + kg * 32 * D + roff[st]);
         s = mfma32x32x16<BF16>(qa, kf, s);
         dp = mfma32x32x16<BF16>(ga, vf, dp);
       }
     }
+    if (__builtin_expect(mask, 0)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rl = 8 * (r >> 2) + 4 * lh + (r & 3);
-      const int row = wrow0 + rl;
-      bool keep = live && key_ok && row < Lq;
-      if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
-      const float p = keep ? fast_exp2(fmaf(s[r], c, -lse_b[rl] * kLog2e)) : 0.f;
-      s[r] = p;
-      dp[r] = a.scale * p * (dp[r] - dsum_b[rl]);
+      for (int r = 0; r < 16; ++r) {
+        const int row = wrow0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        bool keep = live && key_ok && row < Lq;
+        if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
+        s[r] = keep ? s[r] : -INFINITY;  // exp2(-inf) = 0: c is strictly positive
+      }
+    }
+    // P = exp2(S c - LSE log2 e); dS = scale P (dP - Dsum).  Row statistics come in
+    // groups of four consecutive rows.
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 l4 = *(const f32x4*)(lse_b + 8 * g4 + 4 * lh);
+      const f32x4 d4 = *(const f32x4*)(dsum_b + 8 * g4 + 4 * lh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g4 + j;
+        const float p = fast_exp2(fmaf(s[r], c, -l4[j] * kLog2e));
+        s[r] = p;
+        dp[r] = a.scale * p * (dp[r] - d4[j]);
+      }
     }
     Frag8 pf[2], dsf[2];
 #pragma unroll
@@ -501,6 +551,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
       dsf[t].v = u32x4{pack2<BF16>(dp[r0 + 0], dp[r0 + 1]), pack2<BF16>(dp[r0 + 2], dp[r0 + 3]),
                        pack2<BF16>(dp[r0 + 4], dp[r0 + 5]), pack2<BF16>(dp[r0 + 6], dp[r0 + 7])};
     }
+    // dS to LDS as [row][key] for the dQ product.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -512,18 +563,17 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
         dSs[(rl0 + 1) * SSTR + kg * 32 + li] = (uint16_t)(two >> 16);
       }
     }
+    // dV^T += dO^T P and dK^T += Q^T dS.
     if (live) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const int row = rh * 32 + t * 16 + tr_row;
-          const int col = d * 32 + tr_col;
-          const int o_lo = Swz::elem(row, col), o_hi = Swz::elem(row + 8, col);
-          const u32x2 g_lo = lds_read_tr16(dO + o_lo);
-          const u32x2 g_hi = lds_read_tr16(dO + o_hi);
-          const u32x2 q_lo = lds_read_tr16(Q + o_lo);
-          const u32x2 q_hi = lds_read_tr16(Q + o_hi);
+          const int slice = (rh * 32 + t * 16) * D;
+          const u32x2 g_lo = lds_read_tr16(dO + slice + qtr[0][d]);
+          const u32x2 g_hi = lds_read_tr16(dO + slice + qtr[1][d]);
+          const u32x2 q_lo = lds_read_tr16(Q + slice + qtr[0][d]);
+          const u32x2 q_hi = lds_read_tr16(Q + slice + qtr[1][d]);
           Frag8 ga, qa;
           ga.v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
           qa.v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
@@ -534,35 +584,49 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
     }
     __syncthreads();  // dS of all eight wavefronts is in LDS
 
-    // dQ[64 rows][D] = dS[64 rows][128 keys] K[128 keys][D]: 2 x ND tiles of 32 x 32.
-    for (int tile = wave; tile < 2 * ND; tile += kW8Waves) {
-      const int rq = tile & 1, d = tile >> 1;
+    // dQ[64 rows][D] = dS[64 rows][128 keys] K[128 keys][D]: 2 x ND tiles of 32 x 32,
+    // tile w on wavefront w (row half w % 2, d-block w / 2).
+    if (wave < 2 * ND) {
+      const int rq = wave & 1;
       const int qrow0 = i0 + rq * 32;
-      if (qrow0 >= Lq) continue;
-      if (CAUSAL && k0 > qrow0 + 31 + diag) continue;  // no key of the block visible
-      f32x16 dq = f32x16{};
+      bool any = true;
+      if (mask) any = qrow0 < Lq && !(CAUSAL && k0 > qrow0 + 31 + diag);
+      if (any) {
+        f32x16 dq = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < kBwdBN / 16; ++ks) {
-        Frag8 sa, kb2;
-        sa.v = load16(&dSs[(rq * 32 + li) * SSTR + ks * 16 + lh * 8]);
-        const int krow = ks * 16 + 8 * lh + ((lane & 15) >> 2);
-        const int kcol = d * 32 + tr_col;
-        const u32x2 lo = lds_read_tr16(Ks + Swz::elem(krow, kcol));
-        const u32x2 hi = lds_read_tr16(Ks + Swz::elem(krow + 4, kcol));
-        kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
-        dq = mfma32x32x16<BF16>(sa, kb2, dq);
-      }
+        for (int ks = 0; ks < kBwdBN / 16; ++ks) {
+          Frag8 sa, kb2;
+          sa.v = load16(&dSs[(rq * 32 + li) * SSTR + ks * 16 + lh * 8]);
+          const u32x2 lo = lds_read_tr16(Ks + ks * 16 * D + ktr[0]);
+          const u32x2 hi = lds_read_tr16(Ks + ks * 16 * D + ktr[1]);
+          kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+          dq = mfma32x32x16<BF16>(sa, kb2, dq);
+        }
+        // lane = column dq_d*32 + li; registers = rows.
+        float* dst = a.dq_acc + ((size_t)(q_start + qrow0 + 4 * lh) * a.Hq + h) * D + dq_d * 32 + li;
+        const size_t rstride = (size_t)a.Hq * D;
+        if (__builtin_expect(qrow0 + 32 <= Lq, 1)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = qrow0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < Lq) {
-          float* dst = a.dq_acc + ((size_t)(q_start + row) * a.Hq + h) * D + d * 32 + li;
-          unsafeAtomicAdd(dst, dq[r]);
+          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * rstride, dq[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = 8 * (r >> 2) + (r & 3);  // row offset from qrow0 + 4 lh
+            if (qrow0 + 4 * lh + rr < Lq) unsafeAtomicAdd(dst + rr * rstride, dq[r]);
+          }
         }
       }
     }
     wait_all_memory();
     __syncthreads();
+  };
+
+  // Steps whose 64 rows see all 128 keys and lie inside both sequences need no mask.
+  for (int it = 0; it < nsteps; ++it) {
+    const int i0 = (qb_begin + it % nqs) * kW8BQ;
+    bool full = i0 + kW8BQ <= Lq && k0 + kBwdBN <= Lk;
+    if constexpr (CAUSAL) full = full && (k0 + kBwdBN - 1 <= i0 + diag);
+    step(it, !full);
   }
 
   // Sum the two row halves' partial dK, dV through LDS (the tile area is free now).

@@ -49,8 +49,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   constexpr int ND = D / 32;  // 32-wide blocks of the head dimension (output tiles)
   constexpr int TILE = kFwdBN * D;  // elements per K or V tile
   using Swz = DualSwizzle<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][TILE];
+  // Two buffers per tensor as distinct LDS objects, always addressed statically: the
+  // compiler can then tell that reads of one buffer do not touch the direct loads in
+  // flight into the other, and lets them overlap.
+  __shared__ __attribute__((aligned(16))) uint16_t K0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -112,7 +117,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const int r = chunk / Swz::CH;
     foff[i] = r * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
   }
-  auto fetch = [&](int kb, int buf) {
+  auto fetch = [&](int kb, auto buf_tag) {
+    uint16_t* Kd = decltype(buf_tag)::value ? K1 : K0;
+    uint16_t* Vd = decltype(buf_tag)::value ? V1 : V0;
     const int k0 = kb * kFwdBN;
     const uint16_t* kt = kp + (size_t)k0 * k_rs;
     const uint16_t* vt = vp + (size_t)k0 * k_rs;
@@ -120,8 +127,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int first = (i * kFwdWaves + wave) * 64;
-        lds_direct_load16(kt + foff[i], &Kt[buf][first * 8]);
-        lds_direct_load16(vt + foff[i], &Vt[buf][first * 8]);
+        lds_direct_load16(kt + foff[i], Kd + first * 8);
+        lds_direct_load16(vt + foff[i], Vd + first * 8);
       }
     } else {
 #pragma unroll
@@ -130,13 +137,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const int chunk = first + lane;
         const int r = chunk / Swz::CH;
         const int off = min(r, Lk - 1 - k0) * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
-        lds_direct_load16(kt + off, &Kt[buf][first * 8]);
-        lds_direct_load16(vt + off, &Vt[buf][first * 8]);
+        lds_direct_load16(kt + off, Kd + first * 8);
+        lds_direct_load16(vt + off, Vd + first * 8);
       }
     }
   };
 
-  if (nkb > 0) fetch(0, 0);
+  if (nkb > 0) fetch(0, std::false_type{});
 
   // Q^T operand: lane holds Q[my_row][16 s + 8 lh .. +7] for every slice s.
   Frag8 qf[NS];
@@ -172,16 +179,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   // One key tile.  MASK selects the variant for tiles that touch the causal diagonal or
   // the sequence tail; interior tiles carry no masking code at all.
-  auto tile = [&](int kb, auto mask_tag) {
+  auto tile = [&](int kb, auto mask_tag, auto buf_tag) {
+    constexpr bool BUF = decltype(buf_tag)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int cur = kb & 1;
     const int k0 = kb * kFwdBN;
-    if (kb + 1 < nkb) fetch(kb + 1, cur ^ 1);
+    if (kb + 1 < nkb) fetch(kb + 1, std::integral_constant<bool, !BUF>{});
 
     // A wavefront whose rows keep no key of this tile has nothing to add.
     if (!(MASK && CAUSAL && k0 > wave_row0 + 31 + diag)) {
-      const uint16_t* K = Kt[cur];
-      const uint16_t* V = Vt[cur];
+      const uint16_t* K = BUF ? K1 : K0;
+      const uint16_t* V = BUF ? V1 : V0;
       // S^T (keys x rows): two 32-key blocks.
       f32x16 s[2];
 #pragma unroll
@@ -267,8 +274,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   int n_full = Lk / kFwdBN;
   if constexpr (CAUSAL) n_full = min(n_full, q0 + diag + 1 >= 0 ? (q0 + diag + 1) / kFwdBN : 0);
   n_full = min(n_full, nkb);
-  for (int kb = 0; kb < n_full; ++kb) tile(kb, std::false_type{});
-  for (int kb = n_full; kb < nkb; ++kb) tile(kb, std::true_type{});
+  // Tile kb lives in buffer kb % 2; both loops advance in pairs so that every buffer is
+  // named statically (an odd interior tile count leaves one interior tile to the masked
+  // variant, which is correct for any tile).
+  using B0 = std::false_type;
+  using B1 = std::true_type;
+  n_full &= ~1;
+  int kb = 0;
+  for (; kb < n_full; kb += 2) {
+    tile(kb, std::false_type{}, B0{});
+    tile(kb + 1, std::false_type{}, B1{});
+  }
+  for (; kb + 2 <= nkb; kb += 2) {
+    tile(kb, std::true_type{}, B0{});
+    tile(kb + 1, std::true_type{}, B1{});
+  }
+  if (kb < nkb) tile(kb, std::true_type{}, B0{});
 
   // Epilogue.
   const float l_tot = pair_sum(l_run);
