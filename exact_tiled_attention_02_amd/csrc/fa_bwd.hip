@@ -325,36 +325,28 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
 constexpr int kW8Waves = 8;
 constexpr int kW8BQ = 64;
 
-template <int D>
-struct W8Lds {
-  static constexpr int SSTR = kBwdBN + 8;
-  static constexpr int KV = kBwdBN * D * 2;      // bytes of the K or V tile
-  static constexpr int QT = kW8BQ * D * 2;       // bytes of one Q or dO tile
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = K_OFF + KV;
-  static constexpr int Q_OFF = V_OFF + KV;       // 2 buffers
-  static constexpr int DO_OFF = Q_OFF + 2 * QT;  // 2 buffers
-  static constexpr int DS_OFF = DO_OFF + 2 * QT;
-  static constexpr int LSE_OFF = DS_OFF + kW8BQ * SSTR * 2;  // float[2][64]
-  static constexpr int DSUM_OFF = LSE_OFF + 2 * 64 * 4;
-  static constexpr int BYTES = DSUM_OFF + 2 * 64 * 4;
-  static constexpr int RED_BYTES = 4 * 2 * 32 * D * 4;  // fp32 dK, dV partials of 4 wavefronts
-  static_assert(RED_BYTES <= DS_OFF, "partial sums reuse the tile area");
-};
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  using L = W8Lds<D>;
-  constexpr int SSTR = L::SSTR;
+  constexpr int SSTR = kBwdBN + 8;  // dS tile [query row][key], padded
+  constexpr int QT = kW8BQ * D;      // elements of a Q or dO tile
   using Swz = DualSwizzle<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[L::BYTES];
-  uint16_t* Ks = (uint16_t*)(smem + L::K_OFF);
-  uint16_t* Vs = (uint16_t*)(smem + L::V_OFF);
-  uint16_t* dSs = (uint16_t*)(smem + L::DS_OFF);
-  float* lse_s = (float*)(smem + L::LSE_OFF);
-  float* dsum_s = (float*)(smem + L::DSUM_OFF);
+  // Double buffers for the query-side tiles.  The step body receives the buffer it reads
+  // and the one being filled as __restrict__ pointers, which tells the compiler that its
+  // LDS reads do not touch the direct loads in flight, so they overlap.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBwdBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBwdBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t dO0[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t dO1[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t dSs[kW8BQ * SSTR];
+  __shared__ __attribute__((aligned(16))) float lse0[64];
+  __shared__ __attribute__((aligned(16))) float lse1[64];
+  __shared__ __attribute__((aligned(16))) float dsum0[64];
+  __shared__ __attribute__((aligned(16))) float dsum1[64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -417,14 +409,13 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
     const int r = chunk / Swz::CH;
     qoff[i] = r * (int)q_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
   }
-  auto fetch = [&](int it, int buf) {
+  auto fetch = [&](int it, uint16_t* __restrict__ Qd, uint16_t* __restrict__ dOd, float* __restrict__ lsed,
+                   float* __restrict__ dsumd) {
     const int h = hk * G + it / nqs;
     const int i0 = (qb_begin + it % nqs) * kW8BQ;
     const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * D;
     const uint16_t* qt = (const uint16_t*)a.q + base;
     const uint16_t* dot = (const uint16_t*)a.dout + base;
-    uint16_t* Qd = (uint16_t*)(smem + L::Q_OFF + buf * L::QT);
-    uint16_t* dOd = (uint16_t*)(smem + L::DO_OFF + buf * L::QT);
     if (i0 + kW8BQ <= Lq) {
 #pragma unroll
       for (int i = 0; i < NQI; ++i) {
@@ -444,11 +435,11 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
       }
     }
     const int row = min(i0 + lane, Lq - 1);
-    if (wave == 0) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, lse_s + buf * 64);
-    if (wave == 1) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, dsum_s + buf * 64);
+    if (wave == 0) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, lsed);
+    if (wave == 1) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, dsumd);
   };
 
-  if (nsteps > 0) fetch(0, 0);
+  if (nsteps > 0) fetch(0, Q0, dO0, lse0, dsum0);
 #pragma unroll
   for (int i = 0; i < kBwdBN * D / 8 / 512; ++i) {
     const int first = (i * kW8Waves + wave) * 64;
@@ -491,15 +482,14 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
 
   // One query step.  mask: the step touches the causal diagonal or a sequence end (a
   // uniform flag; the masking code sits behind a branch the other steps skip).
-  auto step = [&](int it, bool mask) {
-    const int buf = it & 1;
+  auto step = [&](int it, bool mask, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
+                  const float* __restrict__ lse_c, const float* __restrict__ dsum_c, uint16_t* __restrict__ Qn,
+                  uint16_t* __restrict__ dOn, float* __restrict__ lse_n, float* __restrict__ dsum_n) {
     const int h = hk * G + it / nqs;
     const int i0 = (qb_begin + it % nqs) * kW8BQ;
-    if (it + 1 < nsteps) fetch(it + 1, buf ^ 1);
-    const uint16_t* Q = (const uint16_t*)(smem + L::Q_OFF + buf * L::QT);
-    const uint16_t* dO = (const uint16_t*)(smem + L::DO_OFF + buf * L::QT);
-    const float* lse_b = lse_s + buf * 64 + rh * 32;
-    const float* dsum_b = dsum_s + buf * 64 + rh * 32;
+    if (it + 1 < nsteps) fetch(it + 1, Qn, dOn, lse_n, dsum_n);
+    const float* lse_b = lse_c + rh * 32;
+    const float* dsum_b = dsum_c + rh * 32;
     const int wrow0 = i0 + rh * 32;  // first query row of this wavefront
 
     // S = Q K^T, dP = dO V^T for this wavefront's 32 rows x 32 keys (lane = key,
@@ -582,10 +572,11 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
         }
       }
     }
-    __syncthreads();  // dS of all eight wavefronts is in LDS
+    lds_barrier();  // dS of all eight wavefronts is in LDS (atomics stay in flight)
 
     // dQ[64 rows][D] = dS[64 rows][128 keys] K[128 keys][D]: 2 x ND tiles of 32 x 32,
     // tile w on wavefront w (row half w % 2, d-block w / 2).
+    bool sixteen = false;  // this wavefront issued exactly 16 atomics after the prefetch
     if (wave < 2 * ND) {
       const int rq = wave & 1;
       const int qrow0 = i0 + rq * 32;
@@ -608,6 +599,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
         if (__builtin_expect(qrow0 + 32 <= Lq, 1)) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * rstride, dq[r]);
+          sixteen = true;
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -617,27 +609,48 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
         }
       }
     }
-    wait_all_memory();
-    __syncthreads();
+    // The prefetch for the next step was issued before this step's atomics, so waiting
+    // until at most that many operations remain completes it without waiting for them.
+    if (sixteen) {
+      wait_vmcnt<16>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
   };
 
   // Steps whose 64 rows see all 128 keys and lie inside both sequences need no mask.
-  for (int it = 0; it < nsteps; ++it) {
+  // Step it reads buffer it % 2 and fills the other.
+  auto needs_mask = [&](int it) {
     const int i0 = (qb_begin + it % nqs) * kW8BQ;
     bool full = i0 + kW8BQ <= Lq && k0 + kBwdBN <= Lk;
     if constexpr (CAUSAL) full = full && (k0 + kBwdBN - 1 <= i0 + diag);
-    step(it, !full);
+    return !full;
+  };
+  for (int it = 0; it < nsteps; ++it) {
+    const bool odd = it & 1;
+    step(it, needs_mask(it), odd ? Q1 : Q0, odd ? dO1 : dO0, odd ? lse1 : lse0, odd ? dsum1 : dsum0,
+         odd ? Q0 : Q1, odd ? dO0 : dO1, odd ? lse0 : lse1, odd ? dsum0 : dsum1);
   }
 
-  // Sum the two row halves' partial dK, dV through LDS (the tile area is free now).
-  float* red = (float*)smem + (size_t)kg * (2 * 32 * D);
+  // Sum the two row halves' partial dK, dV through LDS; the tile buffers are free now
+  // and each key group takes 2 x 32 x D floats of them (one K or V tile, or two Q / dO
+  // buffers).
+  float* red_k;
+  float* red_v;
+  switch (kg) {
+    case 0: red_k = (float*)Ks; red_v = (float*)Ks + 32 * D; break;
+    case 1: red_k = (float*)Vs; red_v = (float*)Vs + 32 * D; break;
+    case 2: red_k = (float*)Q0; red_v = (float*)Q1; break;
+    default: red_k = (float*)dO0; red_v = (float*)dO1; break;
+  }
   if (rh == 1) {
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        red[(d * 16 + r) * 64 + lane] = dkt[d][r];
-        red[32 * D + (d * 16 + r) * 64 + lane] = dvt[d][r];
+        red_k[(d * 16 + r) * 64 + lane] = dkt[d][r];
+        red_v[(d * 16 + r) * 64 + lane] = dvt[d][r];
       }
   }
   __syncthreads();
@@ -646,8 +659,8 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
     for (int d = 0; d < ND; ++d)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        dkt[d][r] += red[(d * 16 + r) * 64 + lane];
-        dvt[d][r] += red[32 * D + (d * 16 + r) * 64 + lane];
+        dkt[d][r] += red_k[(d * 16 + r) * 64 + lane];
+        dvt[d][r] += red_v[(d * 16 + r) * 64 + lane];
       }
     if (key_ok) {
       uint16_t* dkp = (uint16_t*)a.dk + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;

@@ -87,6 +87,24 @@ __device__ __forceinline__ void lds_direct_load4(const void* gptr, void* lds_bas
 // (including direct global->LDS loads).
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N vector-memory operations of this wavefront are outstanding
+// (they complete in issue order), leaving LDS and export counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS traffic only: this wavefront's LDS operations are complete
+// before it arrives, and the compiler keeps memory accesses on their side of it.  Global
+// loads, stores and atomics in flight are not waited for (a __syncthreads() would wait
+// for all of them, including direct global->LDS loads); callers that need those wait
+// with wait_vmcnt first.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // Combine a value with the one held by lane l^32 (the other half of the wavefront).
 __device__ __forceinline__ float pair_max(float x) {
   const uint32_t b = __builtin_bit_cast(uint32_t, x);
