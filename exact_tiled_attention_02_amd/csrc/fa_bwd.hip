@@ -683,6 +683,302 @@ __global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- 2c. main loop, 256 keys
+
+// Head dimensions up to 128, 256 keys per workgroup: each dQ element then receives one
+// fp32 atomic per 256 keys.  The atomics execute at the memory side and bound the loop,
+// so halving them matters more than anything else here.  Eight wavefronts each own 32
+// keys for all 32 rows of a query step: S^T/dP and the dV, dK updates are per wavefront;
+// the four dQ tiles of a step (32 rows x 32 columns, contracted over all 256 keys) go to
+// wavefronts 0..ND-1, one per SIMD, so every SIMD carries the same MFMA load.  V stays in
+// registers as MFMA operands; K is in LDS (row reads for S, transposed reads for dQ).
+constexpr int kK2Keys = 256;
+constexpr int kK2Waves = 8;
+constexpr int kK2BQ = 32;
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int SSTR = kK2Keys + 8;  // dS tile [query row][key], padded
+  constexpr int QT = kK2BQ * D;      // elements of a Q or dO tile
+  using Swz = DualSwizzle<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kK2Keys * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t dO0[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t dO1[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t dSs[kK2BQ * SSTR];
+  __shared__ __attribute__((aligned(16))) float lse0[64];
+  __shared__ __attribute__((aligned(16))) float lse1[64];
+  __shared__ __attribute__((aligned(16))) float dsum0[64];
+  __shared__ __attribute__((aligned(16))) float dsum1[64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+
+  const int nbh = a.B * a.Hkv;
+  const int kb = blockIdx.x / nbh;
+  const int bh = blockIdx.x % nbh;
+  const int hk = bh % a.Hkv;
+  const int b = bh / a.Hkv;
+
+  int q_start, k_start, Lq, Lk;
+  if constexpr (VARLEN) {
+    q_start = a.cu_q[b];
+    Lq = a.cu_q[b + 1] - q_start;
+    k_start = a.cu_k[b];
+    Lk = a.cu_k[b + 1] - k_start;
+  } else {
+    q_start = b * a.Sq;
+    Lq = a.Sq;
+    k_start = b * a.Sk;
+    Lk = a.Sk;
+  }
+  const int k0 = kb * kK2Keys;
+  if (k0 >= Lk) return;  // uniform
+
+  const int G = a.Hq / a.Hkv;
+  const size_t q_rs = (size_t)a.Hq * D;
+  const size_t k_rs = (size_t)a.Hkv * D;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+  const int diag = Lk - Lq;
+  const float c = a.scale_log2;
+  constexpr float kLog2e = 1.4426950408889634f;
+  size_t lse_row0, lse_hs;
+  if constexpr (VARLEN) {
+    lse_hs = (size_t)a.cu_q[a.B];
+    lse_row0 = (size_t)q_start;
+  } else {
+    lse_hs = (size_t)a.Sq;
+    lse_row0 = (size_t)b * a.Hq * a.Sq;
+  }
+
+  int qb_begin = 0;
+  if constexpr (CAUSAL) qb_begin = max(0, k0 - diag) / kK2BQ;
+  const int qb_end = (Lq + kK2BQ - 1) / kK2BQ;
+  const int nqs = max(0, qb_end - qb_begin);
+  const int nsteps = G * nqs;
+
+  // Q / dO tile: QT/8 chunks, one direct load per lane for D = 128 (half the lanes
+  // for D = 64).
+  constexpr int QCH = QT / 8;
+  static_assert(QCH <= kK2Waves * 64 && QCH % 64 == 0, "one direct load per lane at most");
+  const int qchunk = wave * 64 + lane;
+  const bool qloader = wave * 64 < QCH;  // uniform per wavefront
+  const int qr = qchunk / Swz::CH;
+  const int qoff = qr * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8;
+  auto fetch = [&](int it, uint16_t* __restrict__ Qd, uint16_t* __restrict__ dOd, float* __restrict__ lsed,
+                   float* __restrict__ dsumd) {
+    const int h = hk * G + it / nqs;
+    const int i0 = (qb_begin + it % nqs) * kK2BQ;
+    const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * D;
+    const uint16_t* qt = (const uint16_t*)a.q + base;
+    const uint16_t* dot = (const uint16_t*)a.dout + base;
+    if (qloader) {
+      int off = qoff;
+      if (i0 + kK2BQ > Lq) off = min(qr, Lq - 1 - i0) * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8;
+      lds_direct_load16(qt + off, Qd + wave * 64 * 8);
+      lds_direct_load16(dot + off, dOd + wave * 64 * 8);
+    }
+    const int row = min(i0 + (lane & 31), Lq - 1);
+    if (wave == kK2Waves - 1) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, lsed);
+    if (wave == kK2Waves - 2) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, dsumd);
+  };
+
+  if (nsteps > 0) fetch(0, Q0, dO0, lse0, dsum0);
+#pragma unroll
+  for (int i = 0; i < kK2Keys * D / 8 / 512; ++i) {
+    const int first = (i * kK2Waves + wave) * 64;
+    const int chunk = first + lane;
+    const int r = chunk / Swz::CH;
+    const int p = chunk % Swz::CH;
+    lds_direct_load16(kp + (size_t)min(k0 + r, Lk - 1) * k_rs + Swz::chunk(r, p) * 8, Ks + first * 8);
+  }
+
+  // This wavefront's keys; V as B operands of dP = dO V^T.
+  const int my_key = k0 + wave * 32 + li;
+  const bool key_ok = my_key < Lk;
+  Frag8 vf[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+    vf[st].v = key_ok ? load16(vp + (size_t)my_key * k_rs + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+  f32x16 dkt[ND], dvt[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    dkt[d] = f32x16{};
+    dvt[d] = f32x16{};
+  }
+  const int tr_row = 4 * lh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Row reads (row li of a 32-row block, chunk 2 st + lh): offset li*D + ((2 st) ^ ry)*8.
+  const int ry = lh ^ Swz::f(li);
+  int ktr[2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) ktr[hi] = Swz::elem(8 * lh + ((lane & 15) >> 2) + 4 * hi, wave * 32 + tr_col);
+
+  wait_all_memory();
+  __syncthreads();
+
+  auto step = [&](int it, bool mask, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
+                  const float* __restrict__ lse_c, const float* __restrict__ dsum_c, uint16_t* __restrict__ Qn,
+                  uint16_t* __restrict__ dOn, float* __restrict__ lse_n, float* __restrict__ dsum_n) {
+    const int h = hk * G + it / nqs;
+    const int i0 = (qb_begin + it % nqs) * kK2BQ;
+    if (it + 1 < nsteps) fetch(it + 1, Qn, dOn, lse_n, dsum_n);
+
+    bool live = true;
+    if constexpr (CAUSAL) live = !mask || wave * 32 + k0 <= i0 + kK2BQ - 1 + diag;  // some key visible
+    f32x16 s = f32x16{}, dp = f32x16{};
+    if (live) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        Frag8 qa, ga, kf;
+        const int ro = li * D + ((st * 2) ^ ry) * 8;
+        qa.v = load16(Q + ro);
+        ga.v = load16(dO + ro);
+        kf.v = load16(Ks + wave * 32 * D + ro);
+        s = mfma32x32x16<BF16>(qa, kf, s);
+        dp = mfma32x32x16<BF16>(ga, vf[st], dp);
+      }
+    }
+    if (__builtin_expect(mask, 0)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        bool keep = live && key_ok && row < Lq;
+        if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
+        s[r] = keep ? s[r] : -INFINITY;  // exp2(-inf) = 0: c is strictly positive
+      }
+    }
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 l4 = *(const f32x4*)(lse_c + 8 * g4 + 4 * lh);
+      const f32x4 d4 = *(const f32x4*)(dsum_c + 8 * g4 + 4 * lh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g4 + j;
+        const float p = fast_exp2(fmaf(s[r], c, -l4[j] * kLog2e));
+        s[r] = p;
+        dp[r] = a.scale * p * (dp[r] - d4[j]);
+      }
+    }
+    Frag8 pf[2], dsf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = 8 * t;
+      pf[t].v = u32x4{pack2<BF16>(s[r0 + 0], s[r0 + 1]), pack2<BF16>(s[r0 + 2], s[r0 + 3]),
+                      pack2<BF16>(s[r0 + 4], s[r0 + 5]), pack2<BF16>(s[r0 + 6], s[r0 + 7])};
+      dsf[t].v = u32x4{pack2<BF16>(dp[r0 + 0], dp[r0 + 1]), pack2<BF16>(dp[r0 + 2], dp[r0 + 3]),
+                       pack2<BF16>(dp[r0 + 4], dp[r0 + 5]), pack2<BF16>(dp[r0 + 6], dp[r0 + 7])};
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t two = dsf[t].v[w];
+        const int r = 8 * t + 2 * w;
+        const int rl0 = 8 * (r >> 2) + 4 * lh + (r & 3);
+        dSs[rl0 * SSTR + wave * 32 + li] = (uint16_t)(two & 0xffff);
+        dSs[(rl0 + 1) * SSTR + wave * 32 + li] = (uint16_t)(two >> 16);
+      }
+    }
+    if (live) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const int o_lo = Swz::elem(t * 16 + tr_row, d * 32 + tr_col);
+          const int o_hi = Swz::elem(t * 16 + tr_row + 8, d * 32 + tr_col);
+          const u32x2 g_lo = lds_read_tr16(dO + o_lo);
+          const u32x2 g_hi = lds_read_tr16(dO + o_hi);
+          const u32x2 q_lo = lds_read_tr16(Q + o_lo);
+          const u32x2 q_hi = lds_read_tr16(Q + o_hi);
+          Frag8 ga, qa;
+          ga.v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
+          qa.v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
+          dvt[d] = mfma32x32x16<BF16>(ga, pf[t], dvt[d]);
+          dkt[d] = mfma32x32x16<BF16>(qa, dsf[t], dkt[d]);
+        }
+      }
+    }
+    lds_barrier();  // dS of all eight wavefronts is in LDS (atomics stay in flight)
+
+    // dQ[32 rows][d-block wave] = dS[32 rows][256 keys] K[256 keys][d-block].
+    bool sixteen = false;  // exactly 16 atomics issued after the prefetch
+    if (wave < ND) {
+      bool any = true;
+      if (mask) any = i0 < Lq && !(CAUSAL && k0 > i0 + kK2BQ - 1 + diag);
+      if (any) {
+        f32x16 dq = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < kK2Keys / 16; ++ks) {
+          Frag8 sa, kb2;
+          sa.v = load16(&dSs[li * SSTR + ks * 16 + lh * 8]);
+          const u32x2 lo = lds_read_tr16(Ks + ks * 16 * D + ktr[0]);
+          const u32x2 hi = lds_read_tr16(Ks + ks * 16 * D + ktr[1]);
+          kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+          dq = mfma32x32x16<BF16>(sa, kb2, dq);
+        }
+        float* dst = a.dq_acc + ((size_t)(q_start + i0 + 4 * lh) * a.Hq + h) * D + wave * 32 + li;
+        const size_t rstride = (size_t)a.Hq * D;
+        if (__builtin_expect(i0 + kK2BQ <= Lq, 1)) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * rstride, dq[r]);
+          sixteen = true;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = 8 * (r >> 2) + (r & 3);
+            if (i0 + 4 * lh + rr < Lq) unsafeAtomicAdd(dst + rr * rstride, dq[r]);
+          }
+        }
+      }
+    }
+    if (sixteen) {
+      wait_vmcnt<16>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+  };
+
+  auto needs_mask = [&](int it) {
+    const int i0 = (qb_begin + it % nqs) * kK2BQ;
+    bool full = i0 + kK2BQ <= Lq && k0 + kK2Keys <= Lk;
+    if constexpr (CAUSAL) full = full && (k0 + kK2Keys - 1 <= i0 + diag);
+    return !full;
+  };
+  for (int it = 0; it < nsteps; ++it) {
+    const bool odd = it & 1;
+    step(it, needs_mask(it), odd ? Q1 : Q0, odd ? dO1 : dO0, odd ? lse1 : lse0, odd ? dsum1 : dsum0,
+         odd ? Q0 : Q1, odd ? dO0 : dO1, odd ? lse0 : lse1, odd ? dsum0 : dsum1);
+  }
+
+  if (key_ok) {
+    uint16_t* dkp = (uint16_t*)a.dk + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
+    uint16_t* dvp = (uint16_t*)a.dv + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int col = d * 32 + 8 * gq + 4 * lh;
+        u32x2 wk, wv;
+        wk.x = pack2<BF16>(dkt[d][4 * gq + 0], dkt[d][4 * gq + 1]);
+        wk.y = pack2<BF16>(dkt[d][4 * gq + 2], dkt[d][4 * gq + 3]);
+        wv.x = pack2<BF16>(dvt[d][4 * gq + 0], dvt[d][4 * gq + 1]);
+        wv.y = pack2<BF16>(dvt[d][4 * gq + 2], dvt[d][4 * gq + 3]);
+        *(u32x2*)(dkp + col) = wk;
+        *(u32x2*)(dvp + col) = wv;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- 3. finalize
 
 template <bool BF16, bool VARLEN>
@@ -719,11 +1015,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
-    const int nkb = (a.Sk + kBwdBN - 1) / kBwdBN;
-    const dim3 grid((unsigned)nkb * a.B * a.Hkv);
     if constexpr (D <= 128) {
-      hipLaunchKernelGGL((bwd_main_w8_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(512), 0, stream, a);
+      const int nkb = (a.Sk + kK2Keys - 1) / kK2Keys;
+      const dim3 grid((unsigned)nkb * a.B * a.Hkv);
+      hipLaunchKernelGGL((bwd_main_k256_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(512), 0, stream, a);
     } else {
+      const int nkb = (a.Sk + kBwdBN - 1) / kBwdBN;
+      const dim3 grid((unsigned)nkb * a.B * a.Hkv);
       hipLaunchKernelGGL((bwd_main_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(256), 0, stream, a);
     }
     hipError_t e = hipGetLastError();
