@@ -92,6 +92,37 @@ def time_launches(fn, n, pre=None, post=None):
     return total / n
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_main_fwdbwd_b2_h16_s4096_d128_bf16.json")
+BWD_SOURCE = os.path.join(ROOT, "exact_tiled_attention_02_amd", "csrc", "fa_bwd.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the backward main loop from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading for a plain
+    copy of known size), or None when the kernel source has changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(BWD_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return 1024.0 * (rec["fetch_kib_per_launch"] * rec["copy_fetch_factor"] +
+                     rec["write_kib_per_launch"] * rec["copy_write_factor"])
+
+
+def copy_calibration(n_bytes: int = 512 << 20, reps: int = 3):
+    """A plain device-to-device copy of known size, for scaling the byte counters."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n_bytes, "reps": reps}), flush=True)
+
+
 def cpu_baseline(target_s: float = 12.0):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload: whole
     (batch, head) slices of forward + backward, until about target_s seconds of work."""
@@ -129,7 +160,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-gqa", action="store_true", help="skip the S=8192 GQA forward detail")
     ap.add_argument("--gqa-backward", action="store_true", help="also time the backward at the S=8192 GQA shape")
+    ap.add_argument("--copy-calibration", action="store_true", help="only run a 512 MiB device copy (counter scale)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "
               f"see the design notes on sharding)", file=sys.stderr)
@@ -227,7 +262,7 @@ def main():
                    "seqlen_q": 4096, "seqlen_k": 4096, "headdim": 128, "causal": True, "pct_peak": 100 * value /
                    PEAK_TFLOPS},
         "roofline": {"bound": "mfma", "achieved": main_tflops, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": main_tflops / PEAK_TFLOPS, "traffic": None,
+                     "frac": main_tflops / PEAK_TFLOPS, "traffic": measured_traffic(),
                      "kernel": "bwd_main_kernel<D=128, bf16, causal, padded>"},
         "cpu_baseline": cpu,
         "detail": detail,

@@ -13,13 +13,14 @@
 // Kernels (all on the caller's stream, in order):
 //   1. preprocess: Dsum = rowsum(dO * O) in fp32 and zeroing of the fp32 dQ accumulator
 //      (memory-bound);
-//   2. main: one workgroup per (128-key block, KV head, sequence); each wavefront owns 32
-//      keys and keeps K, V (as MFMA operands) and its dK, dV accumulators in registers
-//      while it walks the query blocks that can see its keys and every query head of
-//      the group.  Per 32-row query block: S = Q K^T, P, dP = dO V^T, dS, then
-//      dV^T += dO^T P and dK^T += Q^T dS on MFMA; dS goes through LDS so that the four
-//      wavefronts together form dQ = dS K for the block, added to the fp32 accumulator
-//      with atomics;
+//   2. main loop, one workgroup per (key block, KV head, sequence), walking the query
+//      blocks that can see its keys for every query head of the group, so dK and dV
+//      accumulate in registers with no atomics.  Per query step: S = Q K^T, P,
+//      dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS on MFMA; dS goes through
+//      LDS so that the workgroup forms dQ = dS K for the step's rows over all its keys,
+//      added to the fp32 accumulator with atomics.  Head dimensions up to 128 use 256
+//      keys per workgroup (8 wavefronts of 32 keys); D = 256 uses 128 keys (4
+//      wavefronts), which its register footprint requires;
 //   3. finalize: fp32 accumulator -> dQ in the input dtype.
 // The softmax scale is folded into dS once, so neither dK nor dQ is rescaled later.
 #include <type_traits>
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   if (live && ch == 0) a.dsum[pair] = s;
 }
 
-// ---------------------------------------------------------------- 2. main loop
+// ---------------------------------------------------------------- 2a. main loop, D = 256
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
@@ -314,376 +315,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- 2b. main loop, 8 waves
-
-// Head dimensions up to 128: eight wavefronts per workgroup and 64-row query steps.
-// Wavefront w owns key group w % 4 (32 keys) and row half w / 4 (32 of the 64 rows), so
-// the two wavefronts of a key group accumulate partial dK, dV over different rows; the
-// partials are summed through LDS once, after the loop.  K and V operands are re-read
-// from LDS instead of being held in registers, which keeps a wavefront within 256
-// registers: two wavefronts per SIMD hide each other's latencies.
-constexpr int kW8Waves = 8;
-constexpr int kW8BQ = 64;
-
-
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(512, 1) void bwd_main_w8_kernel(BwdArgs a) {
-  constexpr int NS = D / 16;
-  constexpr int ND = D / 32;
-  constexpr int SSTR = kBwdBN + 8;  // dS tile [query row][key], padded
-  constexpr int QT = kW8BQ * D;      // elements of a Q or dO tile
-  using Swz = DualSwizzle<D>;
-  // Double buffers for the query-side tiles.  The step body receives the buffer it reads
-  // and the one being filled as __restrict__ pointers, which tells the compiler that its
-  // LDS reads do not touch the direct loads in flight, so they overlap.
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBwdBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBwdBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[QT];
-  __shared__ __attribute__((aligned(16))) uint16_t Q1[QT];
-  __shared__ __attribute__((aligned(16))) uint16_t dO0[QT];
-  __shared__ __attribute__((aligned(16))) uint16_t dO1[QT];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[kW8BQ * SSTR];
-  __shared__ __attribute__((aligned(16))) float lse0[64];
-  __shared__ __attribute__((aligned(16))) float lse1[64];
-  __shared__ __attribute__((aligned(16))) float dsum0[64];
-  __shared__ __attribute__((aligned(16))) float dsum1[64];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
-  const int li = lane & 31;
-  const int lh = lane >> 5;
-  const int kg = wave & 3;   // key group
-  const int rh = wave >> 2;  // row half of the query step
-
-  const int nbh = a.B * a.Hkv;
-  const int kb = blockIdx.x / nbh;
-  const int bh = blockIdx.x % nbh;
-  const int hk = bh % a.Hkv;
-  const int b = bh / a.Hkv;
-
-  int q_start, k_start, Lq, Lk;
-  if constexpr (VARLEN) {
-    q_start = a.cu_q[b];
-    Lq = a.cu_q[b + 1] - q_start;
-    k_start = a.cu_k[b];
-    Lk = a.cu_k[b + 1] - k_start;
-  } else {
-    q_start = b * a.Sq;
-    Lq = a.Sq;
-    k_start = b * a.Sk;
-    Lk = a.Sk;
-  }
-  const int k0 = kb * kBwdBN;
-  if (k0 >= Lk) return;  // uniform
-
-  const int G = a.Hq / a.Hkv;
-  const size_t q_rs = (size_t)a.Hq * D;
-  const size_t k_rs = (size_t)a.Hkv * D;
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
-  const int diag = Lk - Lq;
-  const float c = a.scale_log2;
-  constexpr float kLog2e = 1.4426950408889634f;
-  size_t lse_row0, lse_hs;
-  if constexpr (VARLEN) {
-    lse_hs = (size_t)a.cu_q[a.B];
-    lse_row0 = (size_t)q_start;
-  } else {
-    lse_hs = (size_t)a.Sq;
-    lse_row0 = (size_t)b * a.Hq * a.Sq;
-  }
-
-  int qb_begin = 0;
-  if constexpr (CAUSAL) qb_begin = max(0, k0 - diag) / kW8BQ;
-  const int qb_end = (Lq + kW8BQ - 1) / kW8BQ;
-  const int nqs = max(0, qb_end - qb_begin);
-  const int nsteps = G * nqs;
-
-  // Per-lane source offsets of the direct loads of a Q / dO tile (fixed for the loop).
-  constexpr int NQI = kW8BQ * D / 8 / 512;
-  int qoff[NQI];
-#pragma unroll
-  for (int i = 0; i < NQI; ++i) {
-    const int chunk = (i * kW8Waves + wave) * 64 + lane;
-    const int r = chunk / Swz::CH;
-    qoff[i] = r * (int)q_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
-  }
-  auto fetch = [&](int it, uint16_t* __restrict__ Qd, uint16_t* __restrict__ dOd, float* __restrict__ lsed,
-                   float* __restrict__ dsumd) {
-    const int h = hk * G + it / nqs;
-    const int i0 = (qb_begin + it % nqs) * kW8BQ;
-    const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * D;
-    const uint16_t* qt = (const uint16_t*)a.q + base;
-    const uint16_t* dot = (const uint16_t*)a.dout + base;
-    if (i0 + kW8BQ <= Lq) {
-#pragma unroll
-      for (int i = 0; i < NQI; ++i) {
-        const int first = (i * kW8Waves + wave) * 64;
-        lds_direct_load16(qt + qoff[i], Qd + first * 8);
-        lds_direct_load16(dot + qoff[i], dOd + first * 8);
-      }
-    } else {  // rows past the end re-read the last row (masked to P = 0)
-#pragma unroll
-      for (int i = 0; i < NQI; ++i) {
-        const int first = (i * kW8Waves + wave) * 64;
-        const int chunk = first + lane;
-        const int r = chunk / Swz::CH;
-        const int off = min(r, Lq - 1 - i0) * (int)q_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
-        lds_direct_load16(qt + off, Qd + first * 8);
-        lds_direct_load16(dot + off, dOd + first * 8);
-      }
-    }
-    const int row = min(i0 + lane, Lq - 1);
-    if (wave == 0) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, lsed);
-    if (wave == 1) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, dsumd);
-  };
-
-  if (nsteps > 0) fetch(0, Q0, dO0, lse0, dsum0);
-#pragma unroll
-  for (int i = 0; i < kBwdBN * D / 8 / 512; ++i) {
-    const int first = (i * kW8Waves + wave) * 64;
-    const int chunk = first + lane;
-    const int r = chunk / Swz::CH;
-    const int p = chunk % Swz::CH;
-    const size_t src = (size_t)min(k0 + r, Lk - 1) * k_rs + Swz::chunk(r, p) * 8;
-    lds_direct_load16(kp + src, Ks + first * 8);
-    lds_direct_load16(vp + src, Vs + first * 8);
-  }
-
-  const int my_key = k0 + kg * 32 + li;
-  const bool key_ok = my_key < Lk;
-  f32x16 dkt[ND], dvt[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    dkt[d] = f32x16{};
-    dvt[d] = f32x16{};
-  }
-  const int tr_row = 4 * lh + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  // Per-lane LDS offsets, fixed for the loop.  Row reads (row li of a 32-row block, chunk
-  // 2 st + lh) have the same swizzle for Q, dO, K and V because every block starts at a
-  // multiple of 16 rows; transposed reads of Q / dO (rows tr_row, tr_row + 8 of a 16-row
-  // slice, columns d*32 + tr_col) and of K for dQ (rows 8 lh + (lane%16)/4 and +4 of a
-  // 16-key slice) add a constant per slice.
-  int roff[NS], qtr[2][ND], ktr[2];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) roff[st] = Swz::row_elem(li, st * 2 + lh);
-#pragma unroll
-  for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-    for (int d = 0; d < ND; ++d) qtr[hi][d] = Swz::elem(tr_row + 8 * hi, d * 32 + tr_col);
-  const int dq_d = wave >> 1;  // d-block of this wavefront's dQ tile (when it has one)
-#pragma unroll
-  for (int hi = 0; hi < 2; ++hi) ktr[hi] = Swz::elem(8 * lh + ((lane & 15) >> 2) + 4 * hi, dq_d * 32 + tr_col);
-
-  wait_all_memory();
-  __syncthreads();
-
-  // One query step.  mask: the step touches the causal diagonal or a sequence end (a
-  // uniform flag; the masking code sits behind a branch the other steps skip).
-  auto step = [&](int it, bool mask, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
-                  const float* __restrict__ lse_c, const float* __restrict__ dsum_c, uint16_t* __restrict__ Qn,
-                  uint16_t* __restrict__ dOn, float* __restrict__ lse_n, float* __restrict__ dsum_n) {
-    const int h = hk * G + it / nqs;
-    const int i0 = (qb_begin + it % nqs) * kW8BQ;
-    if (it + 1 < nsteps) fetch(it + 1, Qn, dOn, lse_n, dsum_n);
-    const float* lse_b = lse_c + rh * 32;
-    const float* dsum_b = dsum_c + rh * 32;
-    const int wrow0 = i0 + rh * 32;  // first query row of this wavefront
-
-    // S = Q K^T, dP = dO V^T for this wavefront's 32 rows x 32 keys (lane = key,
-    // registers = rows 8(r/4) + 4 lh + r%4).
-    bool live = true;
-    if constexpr (CAUSAL) live = !mask || k0 + kg * 32 <= wrow0 + 31 + diag;  // some key visible
-    f32x16 s = f32x16{}, dp = f32x16{};
-    if (live) {
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        Frag8 qa, ga, kf, vf;
-        qa.v = load16(Q + rh * 32 * D + roff[st]);
-        ga.v = load16(dO + rh * 32 * D + roff[st]);
-        kf.v = load16(Ks + kg * 32 * D + roff[st]);
-        vf.v = load16(Vs + kg * 32 * D + roff[st]);
-        s = mfma32x32x16<BF16>(qa, kf, s);
-        dp = mfma32x32x16<BF16>(ga, vf, dp);
-      }
-    }
-    if (__builtin_expect(mask, 0)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wrow0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        bool keep = live && key_ok && row < Lq;
-        if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
-        s[r] = keep ? s[r] : -INFINITY;  // exp2(-inf) = 0: c is strictly positive
-      }
-    }
-    // P = exp2(S c - LSE log2 e); dS = scale P (dP - Dsum).  Row statistics come in
-    // groups of four consecutive rows.
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 l4 = *(const f32x4*)(lse_b + 8 * g4 + 4 * lh);
-      const f32x4 d4 = *(const f32x4*)(dsum_b + 8 * g4 + 4 * lh);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * g4 + j;
-        const float p = fast_exp2(fmaf(s[r], c, -l4[j] * kLog2e));
-        s[r] = p;
-        dp[r] = a.scale * p * (dp[r] - d4[j]);
-      }
-    }
-    Frag8 pf[2], dsf[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r0 = 8 * t;
-      pf[t].v = u32x4{pack2<BF16>(s[r0 + 0], s[r0 + 1]), pack2<BF16>(s[r0 + 2], s[r0 + 3]),
-                      pack2<BF16>(s[r0 + 4], s[r0 + 5]), pack2<BF16>(s[r0 + 6], s[r0 + 7])};
-      dsf[t].v = u32x4{pack2<BF16>(dp[r0 + 0], dp[r0 + 1]), pack2<BF16>(dp[r0 + 2], dp[r0 + 3]),
-                       pack2<BF16>(dp[r0 + 4], dp[r0 + 5]), pack2<BF16>(dp[r0 + 6], dp[r0 + 7])};
-    }
-    // dS to LDS as [row][key] for the dQ product.
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t two = dsf[t].v[w];
-        const int r = 8 * t + 2 * w;
-        const int rl0 = rh * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        dSs[rl0 * SSTR + kg * 32 + li] = (uint16_t)(two & 0xffff);
-        dSs[(rl0 + 1) * SSTR + kg * 32 + li] = (uint16_t)(two >> 16);
-      }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS.
-    if (live) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const int slice = (rh * 32 + t * 16) * D;
-          const u32x2 g_lo = lds_read_tr16(dO + slice + qtr[0][d]);
-          const u32x2 g_hi = lds_read_tr16(dO + slice + qtr[1][d]);
-          const u32x2 q_lo = lds_read_tr16(Q + slice + qtr[0][d]);
-          const u32x2 q_hi = lds_read_tr16(Q + slice + qtr[1][d]);
-          Frag8 ga, qa;
-          ga.v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
-          qa.v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
-          dvt[d] = mfma32x32x16<BF16>(ga, pf[t], dvt[d]);
-          dkt[d] = mfma32x32x16<BF16>(qa, dsf[t], dkt[d]);
-        }
-      }
-    }
-    lds_barrier();  // dS of all eight wavefronts is in LDS (atomics stay in flight)
-
-    // dQ[64 rows][D] = dS[64 rows][128 keys] K[128 keys][D]: 2 x ND tiles of 32 x 32,
-    // tile w on wavefront w (row half w % 2, d-block w / 2).
-    bool sixteen = false;  // this wavefront issued exactly 16 atomics after the prefetch
-    if (wave < 2 * ND) {
-      const int rq = wave & 1;
-      const int qrow0 = i0 + rq * 32;
-      bool any = true;
-      if (mask) any = qrow0 < Lq && !(CAUSAL && k0 > qrow0 + 31 + diag);
-      if (any) {
-        f32x16 dq = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < kBwdBN / 16; ++ks) {
-          Frag8 sa, kb2;
-          sa.v = load16(&dSs[(rq * 32 + li) * SSTR + ks * 16 + lh * 8]);
-          const u32x2 lo = lds_read_tr16(Ks + ks * 16 * D + ktr[0]);
-          const u32x2 hi = lds_read_tr16(Ks + ks * 16 * D + ktr[1]);
-          kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
-          dq = mfma32x32x16<BF16>(sa, kb2, dq);
-        }
-        // lane = column dq_d*32 + li; registers = rows.
-        float* dst = a.dq_acc + ((size_t)(q_start + qrow0 + 4 * lh) * a.Hq + h) * D + dq_d * 32 + li;
-        const size_t rstride = (size_t)a.Hq * D;
-        if (__builtin_expect(qrow0 + 32 <= Lq, 1)) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * rstride, dq[r]);
-          sixteen = true;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = 8 * (r >> 2) + (r & 3);  // row offset from qrow0 + 4 lh
-            if (qrow0 + 4 * lh + rr < Lq) unsafeAtomicAdd(dst + rr * rstride, dq[r]);
-          }
-        }
-      }
-    }
-    // The prefetch for the next step was issued before this step's atomics, so waiting
-    // until at most that many operations remain completes it without waiting for them.
-    if (sixteen) {
-      wait_vmcnt<16>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();
-  };
-
-  // Steps whose 64 rows see all 128 keys and lie inside both sequences need no mask.
-  // Step it reads buffer it % 2 and fills the other.
-  auto needs_mask = [&](int it) {
-    const int i0 = (qb_begin + it % nqs) * kW8BQ;
-    bool full = i0 + kW8BQ <= Lq && k0 + kBwdBN <= Lk;
-    if constexpr (CAUSAL) full = full && (k0 + kBwdBN - 1 <= i0 + diag);
-    return !full;
-  };
-  for (int it = 0; it < nsteps; ++it) {
-    const bool odd = it & 1;
-    step(it, needs_mask(it), odd ? Q1 : Q0, odd ? dO1 : dO0, odd ? lse1 : lse0, odd ? dsum1 : dsum0,
-         odd ? Q0 : Q1, odd ? dO0 : dO1, odd ? lse0 : lse1, odd ? dsum0 : dsum1);
-  }
-
-  // Sum the two row halves' partial dK, dV through LDS; the tile buffers are free now
-  // and each key group takes 2 x 32 x D floats of them (one K or V tile, or two Q / dO
-  // buffers).
-  float* red_k;
-  float* red_v;
-  switch (kg) {
-    case 0: red_k = (float*)Ks; red_v = (float*)Ks + 32 * D; break;
-    case 1: red_k = (float*)Vs; red_v = (float*)Vs + 32 * D; break;
-    case 2: red_k = (float*)Q0; red_v = (float*)Q1; break;
-    default: red_k = (float*)dO0; red_v = (float*)dO1; break;
-  }
-  if (rh == 1) {
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        red_k[(d * 16 + r) * 64 + lane] = dkt[d][r];
-        red_v[(d * 16 + r) * 64 + lane] = dvt[d][r];
-      }
-  }
-  __syncthreads();
-  if (rh == 0) {
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dkt[d][r] += red_k[(d * 16 + r) * 64 + lane];
-        dvt[d][r] += red_v[(d * 16 + r) * 64 + lane];
-      }
-    if (key_ok) {
-      uint16_t* dkp = (uint16_t*)a.dk + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
-      uint16_t* dvp = (uint16_t*)a.dv + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int col = d * 32 + 8 * gq + 4 * lh;
-          u32x2 wk, wv;
-          wk.x = pack2<BF16>(dkt[d][4 * gq + 0], dkt[d][4 * gq + 1]);
-          wk.y = pack2<BF16>(dkt[d][4 * gq + 2], dkt[d][4 * gq + 3]);
-          wv.x = pack2<BF16>(dvt[d][4 * gq + 0], dvt[d][4 * gq + 1]);
-          wv.y = pack2<BF16>(dvt[d][4 * gq + 2], dvt[d][4 * gq + 3]);
-          *(u32x2*)(dkp + col) = wk;
-          *(u32x2*)(dvp + col) = wv;
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------- 2c. main loop, 256 keys
+// ---------------------------------------------------------------- 2b. main loop, D <= 128
 
 // Head dimensions up to 128, 256 keys per workgroup: each dQ element then receives one
 // fp32 atomic per 256 keys.  The atomics execute at the memory side and bound the loop,
@@ -817,6 +449,16 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   // Row reads (row li of a 32-row block, chunk 2 st + lh): offset li*D + ((2 st) ^ ry)*8.
   const int ry = lh ^ Swz::f(li);
+  // Transposed reads of Q / dO: row 16 t + tr_row + 8 hi, column 32 d + tr_col of a tile.
+  // With f = f(tr_row + 8 hi) the offset is trb[hi] + 32 (d ^ (f >> 2)) + 16 t D.
+  int trb[2], trx[2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    const int r = tr_row + 8 * hi;
+    const int f = Swz::f(r);
+    trb[hi] = r * D + (tr_col & 7) + 8 * ((tr_col >> 3) ^ (f & 3));
+    trx[hi] = f >> 2;
+  }
   int ktr[2];
 #pragma unroll
   for (int hi = 0; hi < 2; ++hi) ktr[hi] = Swz::elem(8 * lh + ((lane & 15) >> 2) + 4 * hi, wave * 32 + tr_col);
@@ -835,10 +477,11 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
     if constexpr (CAUSAL) live = !mask || wave * 32 + k0 <= i0 + kK2BQ - 1 + diag;  // some key visible
     f32x16 s = f32x16{}, dp = f32x16{};
     if (live) {
+      const int ryo = opaque(ry);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         Frag8 qa, ga, kf;
-        const int ro = li * D + ((st * 2) ^ ry) * 8;
+        const int ro = li * D + ((st * 2) ^ ryo) * 8;
         qa.v = load16(Q + ro);
         ga.v = load16(dO + ro);
         kf.v = load16(Ks + wave * 32 * D + ro);
@@ -888,12 +531,13 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
       }
     }
     if (live) {
+      const int b0 = opaque(trb[0]), b1 = opaque(trb[1]);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const int o_lo = Swz::elem(t * 16 + tr_row, d * 32 + tr_col);
-          const int o_hi = Swz::elem(t * 16 + tr_row + 8, d * 32 + tr_col);
+          const int o_lo = b0 + 32 * (d ^ trx[0]) + t * 16 * D;
+          const int o_hi = b1 + 32 * (d ^ trx[1]) + t * 16 * D;
           const u32x2 g_lo = lds_read_tr16(dO + o_lo);
           const u32x2 g_hi = lds_read_tr16(dO + o_hi);
           const u32x2 q_lo = lds_read_tr16(Q + o_lo);

@@ -117,28 +117,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-// Layout of an unpadded K or V tile in LDS: row r holds D 16-bit elements as D/8 chunks
-// of 16 bytes, stored at physical chunk c ^ f(r) for logical chunk c.  The K pattern
-// spreads 16 consecutive rows of one chunk over all 64 banks (row reads of the MFMA A/B
-// operands); the V pattern spreads 4 consecutive rows x 4 consecutive chunks (the
-// transposed reads).  Each map is its own inverse.
-template <int D>
-struct TileSwizzle {
-  static constexpr int CH = D / 8;
-  __device__ static __forceinline__ int k(int r, int c) {
-    if constexpr (D == 64) return c ^ ((r >> 1) & 7);
-    else return c ^ (r & 15);
-  }
-  __device__ static __forceinline__ int v(int r, int c) {
-    if constexpr (D == 64) return c ^ (((r >> 1) & 1) << 2);
-    else return c ^ ((r & 3) << 2);
-  }
-  // element offset of logical chunk c of row r (K layout)
-  __device__ static __forceinline__ int k_elem(int r, int c) { return r * D + k(r, c) * 8; }
-  // element offset of logical element e of row r (V layout)
-  __device__ static __forceinline__ int v_elem(int r, int e) { return r * D + v(r, e >> 3) * 8 + (e & 7); }
-};
-
 // One layout serving both read patterns on the same tile: 16-byte row reads of 16
 // consecutive rows (MFMA operands taken along the head dimension) and transposed 8-byte
 // reads of 4 consecutive rows x 4 consecutive chunks (operands taken along the rows).
@@ -156,7 +134,13 @@ struct DualSwizzle {
   __device__ static __forceinline__ int elem(int r, int e) { return r * D + chunk(r, e >> 3) * 8 + (e & 7); }
 };
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// Returns x unchanged but hides its value from the optimiser, so that expressions built
+// from it inside a loop are recomputed there instead of being hoisted into registers
+// that stay live across the whole loop (an empty asm statement; emits no instruction).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void store16(void* p, u32x4 x) { *(u32x4*)p = x; }
