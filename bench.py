@@ -196,6 +196,7 @@ def main():
     t_pre = time_launches(lambda: c5.bwd_stage(1), K)
     t_main = time_launches(lambda: c5.bwd_stage(2), K, pre=lambda: c5.bwd_stage(1), post=lambda: c5.bwd_stage(3))
     t_fin = time_launches(lambda: c5.bwd_stage(3), K)
+    t_det = time_launches(lambda: c5.bwd_stage("deterministic"), max(3, K // 4))
     B, S, H, D = c5.w.batch, c5.w.seqlen_q, c5.w.heads_q, c5.w.headdim
     pre_bytes = B * S * H * (2 * D * 2 + D * 4 + 4)   # read O, dO (16-bit); write fp32 acc zeros + Dsum
     fin_bytes = B * S * H * D * (4 + 2)               # read fp32 acc, write dQ
@@ -208,6 +209,7 @@ def main():
             "bwd_pct_peak": 100 * c5.bwd_flops / (t_pre + t_main + t_fin) / 1e12 / PEAK_TFLOPS,
             "fwd_us": t_fwd * 1e6, "bwd_pre_us": t_pre * 1e6, "bwd_main_us": t_main * 1e6, "bwd_fin_us": t_fin * 1e6,
             "bwd_pre_gbs": pre_bytes / t_pre / 1e9, "bwd_fin_gbs": fin_bytes / t_fin / 1e9,
+            "bwd_deterministic_us": t_det * 1e6, "bwd_deterministic_tflops": c5.bwd_flops / t_det / 1e12,
         }
     }
     del c5

@@ -173,6 +173,7 @@ int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, con
   a.bf16 = dtype == FA_DTYPE_BF16;
   a.scale = scale;
   a.scale_log2 = exp2_scale(scale);
+  a.zero_acc = (stage_mask & 8) == 0;  // only the atomic dQ path uses the accumulator
   return hip_status(fa::launch_bwd(a, stage_mask, stream), "fa_bwd launch");
 }
 
@@ -183,6 +184,14 @@ int fa_bwd(const void* dout, const void* q, const void* k, const void* v, const 
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, void* workspace,
            size_t workspace_bytes, hipStream_t stream) {
   return bwd_impl(7, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, cu_seqlens_q,
+                  cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_deterministic(const void* dout, const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, void* dq, void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv,
+                         int D, float scale, int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(1 | 8, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, cu_seqlens_q,
                   cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
 }
 

@@ -58,9 +58,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
       s += to_f32<BF16>(o[w] & 0xffff) * to_f32<BF16>(g[w] & 0xffff);
       s += to_f32<BF16>(o[w] >> 16) * to_f32<BF16>(g[w] >> 16);
     }
-    float* acc = a.dq_acc + off;
-    store16(acc, u32x4{0, 0, 0, 0});
-    store16(acc + 4, u32x4{0, 0, 0, 0});
+    if (a.zero_acc) {
+      float* acc = a.dq_acc + off;
+      store16(acc, u32x4{0, 0, 0, 0});
+      store16(acc + 4, u32x4{0, 0, 0, 0});
+    }
   }
   // reduce over the CH lanes of this pair (CH is a power of two <= 32, lanes contiguous)
 #pragma unroll
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- 2a. main loop, D = 256
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, bool DQ>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     }
     // dS to LDS as [row][key] for the dQ product.
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < (DQ ? 2 : 0); ++t) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t two = dsf[t].v[w];
@@ -263,11 +265,11 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
         dkt[d] = mfma32x32x16<BF16>(qa, dsf[t], dkt[d]);
       }
     }
-    __syncthreads();  // dS of all four wavefronts is in LDS
+    if constexpr (DQ) __syncthreads();  // dS of all four wavefronts is in LDS
 
     // dQ[rows][d-block] = dS[rows][128 keys] K[128 keys][d-block]; d-blocks are dealt
     // round-robin to the wavefronts.
-    for (int d = wave; d < ND; d += kBwdWaves) {
+    for (int d = wave; DQ && d < ND; d += kBwdWaves) {
       f32x16 dq = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < kBwdBN / 16; ++ks) {
@@ -328,7 +330,7 @@ constexpr int kK2Keys = 256;
 constexpr int kK2Waves = 8;
 constexpr int kK2BQ = 32;
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, bool DQ>
 __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
                        pack2<BF16>(dp[r0 + 4], dp[r0 + 5]), pack2<BF16>(dp[r0 + 6], dp[r0 + 7])};
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < (DQ ? 2 : 0); ++t) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t two = dsf[t].v[w];
@@ -550,11 +552,11 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
         }
       }
     }
-    lds_barrier();  // dS of all eight wavefronts is in LDS (atomics stay in flight)
+    if constexpr (DQ) lds_barrier();  // dS of all eight wavefronts is in LDS (atomics stay in flight)
 
     // dQ[32 rows][d-block wave] = dS[32 rows][256 keys] K[256 keys][d-block].
     bool sixteen = false;  // exactly 16 atomics issued after the prefetch
-    if (wave < ND) {
+    if (DQ && wave < ND) {
       bool any = true;
       if (mask) any = i0 < Lq && !(CAUSAL && k0 > i0 + kK2BQ - 1 + diag);
       if (any) {
@@ -623,6 +625,228 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- 2c. deterministic dQ pass
+
+// dQ without atomics (the deterministic backward): one workgroup per (128-row query
+// block, query head, sequence), walking its key tiles like the forward does, with P
+// recomputed from the LSE instead of a running softmax:
+//   S^T = K Q^T, dP^T = V dO^T, P = exp2(S c - LSE log2 e), dS = scale P (dP - Dsum),
+//   dQ^T += K^T dS^T.
+// Q and dO stay in registers as MFMA B operands; each lane holds one query row, so LSE
+// and Dsum are per-lane scalars; K and V tiles stream through LDS double-buffered by
+// direct loads; dQ accumulates in registers and is written once.  Every dQ element is
+// the same sum in the same order on every run.
+constexpr int kDqWaves = 4;
+constexpr int kDqBM = 32 * kDqWaves;
+constexpr int kDqBN = 64;
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int TILE = kDqBN * D;
+  using Swz = DualSwizzle<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+
+  const int nqb = (a.Sq + kDqBM - 1) / kDqBM;
+  const int nbh = a.B * a.Hq;
+  const int qb = nqb - 1 - blockIdx.x / nbh;  // longest key loops first
+  const int bh = blockIdx.x % nbh;
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+
+  int q_start, k_start, Lq, Lk;
+  if constexpr (VARLEN) {
+    q_start = a.cu_q[b];
+    Lq = a.cu_q[b + 1] - q_start;
+    k_start = a.cu_k[b];
+    Lk = a.cu_k[b + 1] - k_start;
+  } else {
+    q_start = b * a.Sq;
+    Lq = a.Sq;
+    k_start = b * a.Sk;
+    Lk = a.Sk;
+  }
+  const int q0 = qb * kDqBM;
+  if (q0 >= Lq) return;  // uniform
+
+  const int hk = h / (a.Hq / a.Hkv);
+  const size_t q_rs = (size_t)a.Hq * D;
+  const size_t k_rs = (size_t)a.Hkv * D;
+  const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
+  const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * D;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+
+  const int diag = Lk - Lq;
+  int kend = Lk;
+  if constexpr (CAUSAL) kend = min(Lk, q0 + kDqBM + diag);
+  const int nkb = kend > 0 ? (kend + kDqBN - 1) / kDqBN : 0;
+  const int my_row = q0 + wave * 32 + li;
+  const bool row_ok = my_row < Lq;
+  const int wave_row0 = q0 + wave * 32;
+
+  constexpr int NI = TILE / 8 / 256;
+  int foff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int chunk = (i * kDqWaves + wave) * 64 + lane;
+    const int r = chunk / Swz::CH;
+    foff[i] = r * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
+  }
+  auto fetch = [&](int kb, uint16_t* __restrict__ Kd, uint16_t* __restrict__ Vd) {
+    const int k0 = kb * kDqBN;
+    const uint16_t* kt = kp + (size_t)k0 * k_rs;
+    const uint16_t* vt = vp + (size_t)k0 * k_rs;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int first = (i * kDqWaves + wave) * 64;
+      int off = foff[i];
+      if (k0 + kDqBN > Lk) {
+        const int chunk = first + lane;
+        const int r = chunk / Swz::CH;
+        off = min(r, Lk - 1 - k0) * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
+      }
+      lds_direct_load16(kt + off, Kd + first * 8);
+      lds_direct_load16(vt + off, Vd + first * 8);
+    }
+  };
+  if (nkb > 0) fetch(0, K0, V0);
+
+  Frag8 qf[NS], gf[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    qf[st].v = row_ok ? load16(qp + (size_t)my_row * q_rs + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+    gf[st].v = row_ok ? load16(dop + (size_t)my_row * q_rs + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+  }
+  constexpr float kLog2e = 1.4426950408889634f;
+  float lse2 = INFINITY, dsum = 0.f;
+  if (row_ok) {
+    size_t li_idx;
+    if constexpr (VARLEN) {
+      li_idx = (size_t)h * a.cu_q[a.B] + q_start + my_row;
+    } else {
+      li_idx = ((size_t)b * a.Hq + h) * a.Sq + my_row;
+    }
+    lse2 = a.lse[li_idx] * kLog2e;
+    dsum = a.dsum[(size_t)(q_start + my_row) * a.Hq + h];
+  }
+  const float c = a.scale_log2;
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
+  const int tr_row = 4 * lh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int ry = lh ^ Swz::f(li);  // row reads: li*D + ((2 st) ^ ry)*8
+  int trb[2], trx[2];               // transposed reads: trb[hi] + 32 (d ^ trx[hi]) + 16 t D
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    const int r = tr_row + 8 * hi;
+    const int f = Swz::f(r);
+    trb[hi] = r * D + (tr_col & 7) + 8 * ((tr_col >> 3) ^ (f & 3));
+    trx[hi] = f >> 2;
+  }
+
+  wait_all_memory();
+  __syncthreads();
+
+  auto tile = [&](int kb, bool mask, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                  uint16_t* __restrict__ Kn, uint16_t* __restrict__ Vn) {
+    const int k0 = kb * kDqBN;
+    if (kb + 1 < nkb) fetch(kb + 1, Kn, Vn);
+    if (!(CAUSAL && k0 > wave_row0 + 31 + diag)) {  // some key of the tile is visible
+      f32x16 s[2], dp[2];
+      const int ryo = opaque(ry);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        s[sub] = f32x16{};
+        dp[sub] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          const int ro = (sub * 32 + li) * D + ((st * 2) ^ ryo) * 8;
+          Frag8 kf, vf;
+          kf.v = load16(K + ro);
+          vf.v = load16(V + ro);
+          s[sub] = mfma32x32x16<BF16>(kf, qf[st], s[sub]);
+          dp[sub] = mfma32x32x16<BF16>(vf, gf[st], dp[sub]);
+        }
+      }
+      if (__builtin_expect(mask, 0)) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            bool keep = key < Lk;
+            if constexpr (CAUSAL) keep = keep && (key <= my_row + diag);
+            s[sub][r] = keep ? s[sub][r] : -INFINITY;
+          }
+      }
+      Frag8 df[4];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[sub][r], c, -lse2));
+          s[sub][r] = a.scale * p * (dp[sub][r] - dsum);
+        }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int sub = t >> 1, r0 = (t & 1) * 8;
+        df[t].v = u32x4{pack2<BF16>(s[sub][r0 + 0], s[sub][r0 + 1]), pack2<BF16>(s[sub][r0 + 2], s[sub][r0 + 3]),
+                        pack2<BF16>(s[sub][r0 + 4], s[sub][r0 + 5]), pack2<BF16>(s[sub][r0 + 6], s[sub][r0 + 7])};
+      }
+      const int b0 = opaque(trb[0]), b1 = opaque(trb[1]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const u32x2 lo = lds_read_tr16(K + b0 + 32 * (d ^ trx[0]) + t * 16 * D);
+          const u32x2 hi = lds_read_tr16(K + b1 + 32 * (d ^ trx[1]) + t * 16 * D);
+          Frag8 kt;
+          kt.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+          acc[d] = mfma32x32x16<BF16>(kt, df[t], acc[d]);
+        }
+      }
+    }
+    wait_all_memory();
+    __syncthreads();
+  };
+
+  int n_full = Lk / kDqBN;
+  if constexpr (CAUSAL) n_full = min(n_full, q0 + diag + 1 >= 0 ? (q0 + diag + 1) / kDqBN : 0);
+  n_full = min(n_full, nkb);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bool odd = kb & 1;
+    tile(kb, kb >= n_full, odd ? K1 : K0, odd ? V1 : V0, odd ? K0 : K1, odd ? V0 : V1);
+  }
+
+  if (row_ok) {
+    uint16_t* gp = (uint16_t*)a.dq + (size_t)(q_start + my_row) * q_rs + (size_t)h * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = d * 32 + 8 * g + 4 * lh;
+        u32x2 w;
+        w.x = pack2<BF16>(acc[d][4 * g + 0], acc[d][4 * g + 1]);
+        w.y = pack2<BF16>(acc[d][4 * g + 2], acc[d][4 * g + 3]);
+        *(u32x2*)(gp + col) = w;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- 3. finalize
 
 template <bool BF16, bool VARLEN>
@@ -658,18 +882,34 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stages & 2) {
+  if (stages & (2 | 8)) {
+    const bool det = (stages & 8) != 0;
     if constexpr (D <= 128) {
       const int nkb = (a.Sk + kK2Keys - 1) / kK2Keys;
       const dim3 grid((unsigned)nkb * a.B * a.Hkv);
-      hipLaunchKernelGGL((bwd_main_k256_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(512), 0, stream, a);
+      if (det) {
+        hipLaunchKernelGGL((bwd_main_k256_kernel<D, BF16, CAUSAL, VARLEN, false>), grid, dim3(512), 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((bwd_main_k256_kernel<D, BF16, CAUSAL, VARLEN, true>), grid, dim3(512), 0, stream, a);
+      }
     } else {
       const int nkb = (a.Sk + kBwdBN - 1) / kBwdBN;
       const dim3 grid((unsigned)nkb * a.B * a.Hkv);
-      hipLaunchKernelGGL((bwd_main_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(256), 0, stream, a);
+      if (det) {
+        hipLaunchKernelGGL((bwd_main_kernel<D, BF16, CAUSAL, VARLEN, false>), grid, dim3(256), 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((bwd_main_kernel<D, BF16, CAUSAL, VARLEN, true>), grid, dim3(256), 0, stream, a);
+      }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (det) {
+      const int nqb = (a.Sq + kDqBM - 1) / kDqBM;
+      const dim3 grid((unsigned)nqb * a.B * a.Hq);
+      hipLaunchKernelGGL((bwd_dq_pass_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(256), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (stages & 4) {
     const size_t n8 = rows * a.Hq * D / 8;

@@ -41,11 +41,13 @@ struct BwdArgs {
   int bf16;
   float scale;
   float scale_log2;
+  int zero_acc;  // preprocess also zeroes dq_acc (the atomic path needs it)
 };
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-// stage_mask bit 0: preprocess, bit 1: main loop, bit 2: finalize.
+// stage_mask bit 0: preprocess, bit 1: main loop with dQ atomics, bit 2: finalize,
+// bit 3: deterministic dQ (main loop without dQ, then a separate dQ pass writing dq).
 hipError_t launch_bwd(const BwdArgs& a, int stage_mask, hipStream_t stream);
 
 }  // namespace fa

@@ -38,6 +38,8 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_workspace_bytes.restype = sz
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, i, vp, sz, vp]
         L.fa_bwd.restype = i
+        L.fa_bwd_deterministic.argtypes = L.fa_bwd.argtypes
+        L.fa_bwd_deterministic.restype = i
         L.fa_bwd_stage.argtypes = [i] + L.fa_bwd.argtypes
         L.fa_bwd_stage.restype = i
         L.fa_status_string.argtypes = [i]
@@ -150,8 +152,18 @@ def fa_bwd_stage(stage, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: 
             workspace.numel() * workspace.element_size(), _stream(stream))
     if stage == 0:
         check(lib().fa_bwd(*args))
+    elif stage == "deterministic":
+        check(lib().fa_bwd_deterministic(*args))
     else:
         check(lib().fa_bwd_stage(int(stage), *args))
+
+
+def fa_bwd_deterministic(dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: bool = False,
+                         scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                         max_seqlen_k=None, stream=None) -> None:
+    """Enqueue the deterministic backward (dQ by a separate pass, no atomics)."""
+    fa_bwd_stage("deterministic", dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q,
+                 cu_seqlens_k, max_seqlen_q, max_seqlen_k, stream)
 
 
 def lse_shape(q, cu_seqlens_q=None):
@@ -181,10 +193,12 @@ def workspace_for(q, cu_seqlens_q=None, max_seqlen_q=None):
 
 
 def backward(dout, q, k, v, out, lse, causal: bool = False, scale: float | None = None, cu_seqlens_q=None,
-             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None):
-    """Allocate (dq, dk, dv) and the workspace, and run :func:`fa_bwd`."""
+             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None, deterministic: bool = False):
+    """Allocate (dq, dk, dv) and the workspace, and run :func:`fa_bwd` (or
+    :func:`fa_bwd_deterministic`)."""
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = workspace_for(q, cu_seqlens_q, max_seqlen_q)
-    fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, ws, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-           max_seqlen_k, stream)
+    run = fa_bwd_deterministic if deterministic else fa_bwd
+    run(dout, q, k, v, out, lse, dq, dk, dv, ws, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+        max_seqlen_k, stream)
     return dq, dk, dv

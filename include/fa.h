@@ -62,7 +62,7 @@ typedef enum fa_dtype { FA_DTYPE_FP16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
 
 /*
  * Forward.  Writes out and lse (layouts above).  `scale` multiplies Q K^T before the
- * softmax (callers usually pass 1/sqrt(D)); it must be finite.  `causal` != 0 applies
+ * softmax (callers usually pass 1/sqrt(D)); it must be finite and >= 0.  `causal` != 0 applies
  * the bottom-right-aligned causal mask.  Rows of a varlen sequence beyond its length are
  * neither read nor written.
  */
@@ -93,6 +93,20 @@ int fa_bwd(const void* dout, const void* q, const void* k, const void* v,
            int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, int causal,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
            int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Deterministic backward: same arguments, results and workspace as fa_bwd, but dQ is
+ * formed by a separate pass over the key blocks of each query block instead of fp32
+ * atomics, so dq, dk and dv are bitwise identical from run to run (the pages' README
+ * offers a deterministic backward: changelog entry 2.4 and the `deterministic`
+ * argument of the flash_attn_func docstring).  It recomputes the scores and dP once more,
+ * so it is slower than fa_bwd.
+ */
+int fa_bwd_deterministic(const void* dout, const void* q, const void* k, const void* v,
+                         const void* out, const float* lse, void* dq, void* dk, void* dv,
+                         int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, int causal,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                         int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One stage of fa_bwd, for callers that schedule or time the stages themselves.

@@ -16,7 +16,7 @@ def rel_fro(got, ref):
     return float(np.linalg.norm(got - ref) / n) if n > 0 else float(np.linalg.norm(got))
 
 
-def run_fwd_bwd(w, x, poison=True):
+def run_fwd_bwd(w, x, poison=True, deterministic=False):
     d = dev(x)
     kw = {}
     if w.varlen:
@@ -31,8 +31,8 @@ def run_fwd_bwd(w, x, poison=True):
         dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
     ws = fa.workspace_for(d["q"], d.get("cu_seqlens_q"), w.seqlen_q if w.varlen else None)
     ws.fill_(0xFF)  # the workspace's contents on entry must not matter
-    fa.fa_bwd(d["do"], d["q"], d["k"], d["v"], out, lse, dq, dk, dv, ws, causal=w.causal, scale=w.softmax_scale,
-              **kw)
+    run = fa.fa_bwd_deterministic if deterministic else fa.fa_bwd
+    run(d["do"], d["q"], d["k"], d["v"], out, lse, dq, dk, dv, ws, causal=w.causal, scale=w.softmax_scale, **kw)
     torch.cuda.synchronize()
     return out, lse, dq, dk, dv
 
@@ -69,11 +69,11 @@ def W(name, B, Hq, Hkv, Sq, Sk, D, dtype, causal, seed=0, lengths=None, scale=No
     return synth.Workload(name, B, Hq, Hkv, Sq, Sk, D, dtype, causal, backward=True, seed=seed, scale=scale)
 
 
-def _full(w):
+def _full(w, deterministic=False):
     x = synth.make_inputs(w)
-    say(f"bwd {w.name} B={w.batch} Hq={w.heads_q} Hkv={w.heads_kv} Sq={w.seqlen_q} Sk={w.seqlen_k} D={w.headdim} "
-        f"{w.dtype} causal={w.causal} varlen={w.varlen}")
-    _, _, dq, dk, dv = run_fwd_bwd(w, x)
+    say(f"bwd{' det' if deterministic else ''} {w.name} B={w.batch} Hq={w.heads_q} Hkv={w.heads_kv} Sq={w.seqlen_q} "
+        f"Sk={w.seqlen_k} D={w.headdim} {w.dtype} causal={w.causal} varlen={w.varlen}")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x, deterministic=deterministic)
     return check_grads(w, x, dq, dk, dv)
 
 
@@ -114,3 +114,31 @@ def test_varlen_ragged(D, causal):
 
 def test_gqa_long():
     print(_full(W("bwd_gqa_1k", 1, 8, 2, 1024, 1024, 128, "bf16", True, seed=9)))
+
+
+# ---------------------------------------------------------------- deterministic backward
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES[:3], ids=lambda s: "x".join(map(str, s)))
+def test_deterministic_sweep(D, causal, shape):
+    B, Hq, Hkv, Sq, Sk = shape
+    print(_full(W(f"bwd_det_d{D}_c{int(causal)}", B, Hq, Hkv, Sq, Sk, D, "bf16", causal, seed=D + Sq + 2),
+                deterministic=True))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_deterministic_varlen_fp16(causal):
+    lq = [1, 129, 0, 300, 64, 17]
+    lk = [5, 129, 3, 250, 64, 200]
+    print(_full(W(f"bwd_det_varlen_c{int(causal)}", None, 4, 2, None, None, 128, "fp16", causal, seed=9,
+                  lengths=(lq, lk)), deterministic=True))
+
+
+def test_deterministic_is_bitwise_repeatable_and_matches_workload5():
+    w, x = synth.draw_config(5)
+    say(f"bwd det {w.name}")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x, deterministic=True)
+    _, _, dq2, dk2, dv2 = run_fwd_bwd(w, x, deterministic=True)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    print("workload 5 deterministic rel-Frobenius:", check_grads(w, x, dq, dk, dv, heads=[(0, 0), (1, 15)]))
