@@ -123,6 +123,71 @@ def copy_calibration(n_bytes: int = 512 << 20, reps: int = 3):
     print(json.dumps({"copy_bytes_per_launch": n_bytes, "reps": reps}), flush=True)
 
 
+def sweep(steps: int, warmup: int):
+    """The benchmark grid of the FlashAttention README's A100 section ("Performance"):
+    head dimension 64 or 128 with hidden size 2048 (32 or 16 heads), sequence lengths
+    512 .. 16k, batch 16k / seqlen, forward + backward, causal and not; reproduced on one
+    MI355X with synthetic bf16 inputs.  Prints one JSON line per point, with a plain
+    PyTorch attention (bf16 matmul, fp32 softmax, materialised scores) timed beside it as
+    the README's comparison point."""
+    import torch
+    from exact_tiled_attention_02_amd import fa, synth
+    for D in (64, 128):
+        H = 2048 // D
+        for causal in (False, True):
+            for S in (512, 1024, 2048, 4096, 8192, 16384):
+                B = 16384 // S
+                w = synth.Workload(f"sweep_d{D}_s{S}", B, H, H, S, S, D, "bf16", causal, backward=True, seed=S + D)
+                x = {k: v.cuda() for k, v in synth.make_inputs(w).items()}
+                out = torch.empty_like(x["q"])
+                lse = torch.empty(fa.lse_shape(x["q"]), dtype=torch.float32, device="cuda")
+                dq, dk, dv = (torch.empty_like(x[k]) for k in ("q", "k", "v"))
+                ws = fa.workspace_for(x["q"])
+                fwd = lambda: fa.fa_fwd(x["q"], x["k"], x["v"], out, lse, causal=causal)
+                bwd = lambda: fa.fa_bwd(x["do"], x["q"], x["k"], x["v"], out, lse, dq, dk, dv, ws, causal=causal)
+                for _ in range(warmup):
+                    fwd()
+                    bwd()
+                tf = time_launches(fwd, steps)
+                tb = time_launches(bwd, steps)
+                ff, fb = synth.flops(w)
+
+                # plain PyTorch attention, (B, H, S, D) layout, forward and backward written
+                # out (no autograd; every right-hand matmul operand made contiguous)
+                qt, kt, vt, dot = (x[n].transpose(1, 2).contiguous() for n in ("q", "k", "v", "do"))
+                scale = 1.0 / D ** 0.5
+
+                def torch_fb():
+                    s_ = torch.matmul(qt, kt.transpose(-1, -2).contiguous()).float() * scale
+                    if causal:
+                        s_ = s_.masked_fill(torch.ones(S, S, dtype=torch.bool, device="cuda").triu(1), float("-inf"))
+                    p_ = torch.softmax(s_, dim=-1)
+                    p16 = p_.to(qt.dtype)
+                    torch.matmul(p16, vt)                                   # O
+                    torch.matmul(p16.transpose(-1, -2).contiguous(), dot)   # dV
+                    dp_ = torch.matmul(dot, vt.transpose(-1, -2).contiguous()).float()
+                    ds_ = (p_ * (dp_ - (dp_ * p_).sum(-1, keepdim=True)) * scale).to(qt.dtype)
+                    torch.matmul(ds_, kt)                                   # dQ
+                    torch.matmul(ds_.transpose(-1, -2).contiguous(), qt)    # dK
+
+                t_torch = None
+                if S <= 8192:  # the materialised scores need B*H*S*S*(4+4+2+2+4) bytes
+                    torch_fb()
+                    t_torch = time_launches(torch_fb, max(2, steps // 4))
+                del qt, kt, vt, dot
+                torch.cuda.empty_cache()
+                rec = {"workload": w.name, "batch": B, "heads": H, "seqlen": S, "headdim": D, "causal": causal,
+                       "fwd_tflops": ff / tf / 1e12, "bwd_tflops": fb / tb / 1e12,
+                       "fwdbwd_tflops": (ff + fb) / (tf + tb) / 1e12,
+                       "fwdbwd_pct_peak": 100 * (ff + fb) / (tf + tb) / 1e12 / PEAK_TFLOPS,
+                       "fwd_us": tf * 1e6, "bwd_us": tb * 1e6,
+                       "torch_fwdbwd_us": None if t_torch is None else t_torch * 1e6,
+                       "speedup_vs_torch": None if t_torch is None else t_torch / (tf + tb)}
+                print(json.dumps(rec), flush=True)
+                del x, out, lse, dq, dk, dv, ws
+                torch.cuda.empty_cache()
+
+
 def cpu_baseline(target_s: float = 12.0):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload: whole
     (batch, head) slices of forward + backward, until about target_s seconds of work."""
@@ -161,9 +226,13 @@ def main():
     ap.add_argument("--skip-gqa", action="store_true", help="skip the S=8192 GQA forward detail")
     ap.add_argument("--gqa-backward", action="store_true", help="also time the backward at the S=8192 GQA shape")
     ap.add_argument("--copy-calibration", action="store_true", help="only run a 512 MiB device copy (counter scale)")
+    ap.add_argument("--sweep", action="store_true", help="only run the head-dim / seqlen sweep (one JSON line each)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.sweep:
+        sweep(args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "

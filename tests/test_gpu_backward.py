@@ -142,3 +142,12 @@ def test_deterministic_is_bitwise_repeatable_and_matches_workload5():
     _, _, dq2, dk2, dv2 = run_fwd_bwd(w, x, deterministic=True)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
     print("workload 5 deterministic rel-Frobenius:", check_grads(w, x, dq, dk, dv, heads=[(0, 0), (1, 15)]))
+
+
+def test_sweep_point_d64_s2048_sampled_heads():
+    """A sweep point (hidden 2048 as 32 heads of 64, batch 16k / seqlen)."""
+    w = W("sweep_d64_s2048", 8, 32, 32, 2048, 2048, 64, "bf16", True, seed=2112)
+    x = synth.make_inputs(w)
+    say(f"bwd {w.name}")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x)
+    print(check_grads(w, x, dq, dk, dv, heads=[(0, 0), (7, 31)]))

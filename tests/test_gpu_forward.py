@@ -136,3 +136,13 @@ def test_forward_is_bitwise_deterministic():
     o1, l1, _ = run_forward(w, x)
     o2, l2, _ = run_forward(w, x)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_sweep_point_d64_s16k_sampled():
+    """The longest point of the head-dim / seqlen sweep: B=1, 32 heads, S=16384, D=64."""
+    w = W("sweep_d64_s16k", 1, 32, 32, 16384, 16384, 64, "bf16", True, seed=16448)
+    x = synth.make_inputs(w)
+    say(f"fwd {w.name}")
+    o, lse, _ = run_forward(w, x)
+    assert torch.isfinite(o).all().item()
+    check_forward_sampled(w, x, o, lse, [(0, 0), (0, 31)], seed=16)
