@@ -9,6 +9,6 @@ mapping, closed forms, invariants, finite-difference gradients, an fp64 library
 cross-check); none is "parity unpinned".
 """
 from .attention_fp64 import (  # noqa: F401
-    kv_head_of, causal_keep_mask, head_probabilities, head_forward, rows_forward, head_backward,
-    forward, backward,
+    kv_head_of, causal_keep_mask, keep_mask, alibi_bias, head_probabilities, head_forward, rows_forward,
+    head_backward, forward, backward, gather_kvcache, forward_kvcache,
 )

@@ -29,6 +29,20 @@ online softmax, no blocking):
   (which equals ``sum_j P_ij dP_ij``), ``dS = P * (dP - Dsum)``, ``dQ = scale dS K``,
   ``dK = scale dS^T Q``.  For GQA the gradients of a KV head sum over the query heads
   that read it.
+* Sliding-window (local) attention, ``window = (left, right)`` with -1 meaning unbounded
+  on that side: query ``i`` keeps keys ``j`` with
+  ``i + seqlen_k - seqlen_q - left <= j <= i + seqlen_k - seqlen_q + right`` -- the
+  ``flash_attn_func`` docstring (window paragraph) and changelog entry 2.3.  With
+  ``causal`` both conditions must hold (the window is intersected with the causal mask).
+* ALiBi: the bias ``-slope_h * |i + seqlen_k - seqlen_q - j|`` is added to the scaled
+  score of query ``i`` and key ``j`` of query head ``h`` before the softmax -- the
+  ``alibi_slopes`` argument of the same docstring.  Slopes are given per query head, or
+  per (sequence, query head).  The returned LSE is that of the biased scores.
+* KV cache (``flash_attn_with_kvcache`` docstring, read-only use): sequence ``b`` reads
+  cache entry ``cache_batch_idx[b]`` (default ``b``), its first ``cache_seqlens[b]`` rows
+  (default: all), and, with a block table, key row ``j`` lives in physical block
+  ``block_table[b, j // page]`` at row ``j % page``.  Masks and biases use
+  ``seqlen_k = cache_seqlens[b]``.
 
 Readings taken where the pages are silent (each also listed in the design notes):
 
@@ -52,6 +66,10 @@ import numpy as np
 __all__ = [
     "kv_head_of",
     "causal_keep_mask",
+    "keep_mask",
+    "alibi_bias",
+    "gather_kvcache",
+    "forward_kvcache",
     "head_probabilities",
     "head_forward",
     "rows_forward",
@@ -81,15 +99,38 @@ def causal_keep_mask(len_q: int, len_k: int, causal: bool) -> np.ndarray:
     return j <= i + (len_k - len_q)
 
 
-def head_probabilities(q: np.ndarray, k: np.ndarray, scale: float, causal: bool):
-    """Materialised softmax of one head.  Returns (P, LSE, keep) in float64.
+def keep_mask(len_q: int, len_k: int, causal: bool, window=(-1, -1), rows=None) -> np.ndarray:
+    """Boolean (len(rows), len_k) matrix, True where key j is kept for query row i.
 
-    ``S = scale * q k^T``; masked entries are excluded; rows with no kept key have
+    ``rows`` are the query indices (default ``0 .. len_q-1``).  The causal condition is
+    that of :func:`causal_keep_mask`; the window keeps
+    ``i + len_k - len_q - left <= j <= i + len_k - len_q + right`` (a negative bound is
+    unbounded) -- ``flash_attn_func`` docstring, window paragraph."""
+    i = (np.arange(len_q) if rows is None else np.asarray(rows, dtype=np.int64))[:, None]
+    j = np.arange(len_k)[None, :]
+    diag = i + (len_k - len_q)
+    keep = np.ones((i.shape[0], len_k), dtype=bool)
+    if causal:
+        keep &= j <= diag
+    left, right = window
+    if left >= 0:
+        keep &= j >= diag - left
+    if right >= 0:
+        keep &= j <= diag + right
+    return keep
+
+
+def alibi_bias(len_q: int, len_k: int, slope: float, rows=None) -> np.ndarray:
+    """(len(rows), len_k) float64 bias ``-slope * |i + len_k - len_q - j|`` added to the
+    scaled scores (``alibi_slopes`` argument of the ``flash_attn_func`` docstring)."""
+    i = (np.arange(len_q) if rows is None else np.asarray(rows, dtype=np.int64))[:, None]
+    j = np.arange(len_k)[None, :]
+    return -float(slope) * np.abs(i + (len_k - len_q) - j).astype(np.float64)
+
+
+def _softmax_rows(s: np.ndarray, keep: np.ndarray):
+    """Masked row softmax of the score matrix ``s``: (P, LSE); rows with no kept key get
     P = 0 and LSE = +inf."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    s = scale * (q @ k.T)
-    keep = causal_keep_mask(q.shape[0], k.shape[0], causal)
     s = np.where(keep, s, -np.inf)
     live = keep.any(axis=1)
     m = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
@@ -97,22 +138,39 @@ def head_probabilities(q: np.ndarray, k: np.ndarray, scale: float, causal: bool)
     z = e.sum(axis=1)
     p = np.zeros_like(e)
     p[live] = e[live] / z[live, None]
-    lse = np.full(q.shape[0], np.inf)
+    lse = np.full(s.shape[0], np.inf)
     lse[live] = m[live] + np.log(z[live])
+    return p, lse
+
+
+def head_probabilities(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, window=(-1, -1),
+                       alibi_slope=None):
+    """Materialised softmax of one head.  Returns (P, LSE, keep) in float64.
+
+    ``S = scale * q k^T`` (plus the ALiBi bias when ``alibi_slope`` is given); masked
+    entries are excluded; rows with no kept key have P = 0 and LSE = +inf."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    s = scale * (q @ k.T)
+    if alibi_slope is not None:
+        s = s + alibi_bias(q.shape[0], k.shape[0], alibi_slope)
+    keep = keep_mask(q.shape[0], k.shape[0], causal, window)
+    p, lse = _softmax_rows(s, keep)
     return p, lse, keep
 
 
-def head_forward(q, k, v, scale: float, causal: bool):
+def head_forward(q, k, v, scale: float, causal: bool, window=(-1, -1), alibi_slope=None):
     """One head: O = P V (float64, (len_q, D)) and LSE ((len_q,))."""
-    p, lse, _ = head_probabilities(q, k, scale, causal)
+    p, lse, _ = head_probabilities(q, k, scale, causal, window, alibi_slope)
     o = p @ np.asarray(v, dtype=np.float64)
     return o, lse
 
 
-def rows_forward(q_rows, rows, k, v, scale: float, causal: bool, len_q: int):
+def rows_forward(q_rows, rows, k, v, scale: float, causal: bool, len_q: int, window=(-1, -1),
+                 alibi_slope=None):
     """Output and LSE of selected query rows of one head: ``q_rows[n]`` is query row
-    ``rows[n]`` of a sequence of ``len_q`` queries (the row index fixes its causal
-    mask).  Same definition as :func:`head_forward`, restricted to those rows, so that
+    ``rows[n]`` of a sequence of ``len_q`` queries (the row index fixes its mask and
+    bias).  Same definition as :func:`head_forward`, restricted to those rows, so that
     outputs of very long sequences can be checked one row at a time."""
     q_rows = np.asarray(q_rows, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -120,29 +178,23 @@ def rows_forward(q_rows, rows, k, v, scale: float, causal: bool, len_q: int):
     rows = np.asarray(rows, dtype=np.int64)
     len_k = k.shape[0]
     s = scale * (q_rows @ k.T)
-    j = np.arange(len_k)[None, :]
-    keep = np.ones_like(s, dtype=bool) if not causal else (j <= rows[:, None] + (len_k - len_q))
-    s = np.where(keep, s, -np.inf)
-    live = keep.any(axis=1)
-    m = np.where(live, s.max(axis=1, initial=-np.inf), 0.0)
-    e = np.where(keep, np.exp(s - m[:, None]), 0.0)
-    z = e.sum(axis=1)
-    o = np.zeros((len(rows), v.shape[1]))
-    o[live] = (e[live] @ v) / z[live, None]
-    lse = np.full(len(rows), np.inf)
-    lse[live] = m[live] + np.log(z[live])
-    return o, lse
+    if alibi_slope is not None:
+        s = s + alibi_bias(len_q, len_k, alibi_slope, rows)
+    keep = keep_mask(len_q, len_k, causal, window, rows)
+    p, lse = _softmax_rows(s, keep)
+    return p @ v, lse
 
 
-def head_backward(q, k, v, do, scale: float, causal: bool):
-    """One head: analytic gradients (dq, dk, dv) of O = softmax(scale q k^T) v w.r.t.
-    q, k, v for the upstream gradient ``do``.  Probabilities are recomputed here from
-    the definition; nothing from a forward pass is reused."""
+def head_backward(q, k, v, do, scale: float, causal: bool, window=(-1, -1), alibi_slope=None):
+    """One head: analytic gradients (dq, dk, dv) of O = softmax(scale q k^T + bias) v
+    w.r.t. q, k, v for the upstream gradient ``do`` (the bias does not depend on q, k, v,
+    so the formulas are those of the unbiased case with the biased P).  Probabilities are
+    recomputed here from the definition; nothing from a forward pass is reused."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    p, _, _ = head_probabilities(q, k, scale, causal)
+    p, _, _ = head_probabilities(q, k, scale, causal, window, alibi_slope)
     o = p @ v
     dv = p.T @ do
     dp = do @ v.T
@@ -181,8 +233,16 @@ def _flat(x, varlen):
     return x if varlen else x.reshape((-1,) + x.shape[2:])
 
 
+def _slope(alibi_slopes, b, h):
+    """Slope of (sequence b, query head h) from an (Hq,) or (B, Hq) array, or None."""
+    if alibi_slopes is None:
+        return None
+    a = np.asarray(alibi_slopes, dtype=np.float64)
+    return float(a[h] if a.ndim == 1 else a[b, h])
+
+
 def forward(q, k, v, scale=None, causal=False, cu_seqlens_q=None, cu_seqlens_k=None,
-            threads: int = 1, heads=None):
+            threads: int = 1, heads=None, window=(-1, -1), alibi_slopes=None):
     """Attention forward over a batch.
 
     Padded: q (B, Sq, Hq, D), k/v (B, Sk, Hkv, D) -> O (B, Sq, Hq, D), LSE (B, Hq, Sq).
@@ -190,7 +250,8 @@ def forward(q, k, v, scale=None, causal=False, cu_seqlens_q=None, cu_seqlens_k=N
     O (total_q, Hq, D), LSE (Hq, total_q).  Returns float64 arrays.
 
     ``heads`` optionally restricts the work to a list of (sequence, query head) pairs;
-    the other entries of O and LSE are left NaN (used to time a bounded sample)."""
+    the other entries of O and LSE are left NaN (used to time a bounded sample).
+    ``window`` = (left, right) sliding window; ``alibi_slopes`` (Hq,) or (B, Hq)."""
     varlen = _check(q, k, v, cu_seqlens_q, cu_seqlens_k)
     D = q.shape[-1]
     if scale is None:
@@ -211,7 +272,8 @@ def forward(q, k, v, scale=None, causal=False, cu_seqlens_q=None, cu_seqlens_k=N
         b, h = bh
         (q0, lq), (k0, lk) = seq_q[b], seq_k[b]
         g = kv_head_of(h, hq, hkv)
-        ob, lb = head_forward(qf[q0:q0 + lq, h], kf[k0:k0 + lk, g], vf[k0:k0 + lk, g], scale, causal)
+        ob, lb = head_forward(qf[q0:q0 + lq, h], kf[k0:k0 + lk, g], vf[k0:k0 + lk, g], scale, causal,
+                              window, _slope(alibi_slopes, b, h))
         o[q0:q0 + lq, h] = ob
         lse_flat[h, q0:q0 + lq] = lb
 
@@ -223,7 +285,7 @@ def forward(q, k, v, scale=None, causal=False, cu_seqlens_q=None, cu_seqlens_k=N
 
 
 def backward(do, q, k, v, scale=None, causal=False, cu_seqlens_q=None, cu_seqlens_k=None,
-             threads: int = 1, heads=None):
+             threads: int = 1, heads=None, window=(-1, -1), alibi_slopes=None):
     """Attention backward over a batch: returns float64 (dq, dk, dv) in the layouts of
     q, k, v.  dk/dv of a KV head sum the contributions of every query head that reads
     it.  ``heads`` restricts the work as in :func:`forward` (then dk/dv hold partial
@@ -251,7 +313,7 @@ def backward(do, q, k, v, scale=None, causal=False, cu_seqlens_q=None, cu_seqlen
         (q0, lq), (k0, lk) = seq_q[b], seq_k[b]
         g = kv_head_of(h, hq, hkv)
         results[bh] = head_backward(qf[q0:q0 + lq, h], kf[k0:k0 + lk, g], vf[k0:k0 + lk, g],
-                                    dof[q0:q0 + lq, h], scale, causal)
+                                    dof[q0:q0 + lq, h], scale, causal, window, _slope(alibi_slopes, b, h))
 
     _run(one, work, threads)
     # Accumulate in a fixed order so the result does not depend on thread timing.
@@ -265,6 +327,60 @@ def backward(do, q, k, v, scale=None, causal=False, cu_seqlens_q=None, cu_seqlen
     if varlen:
         return dq, dk, dv
     return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)
+
+
+def gather_kvcache(k_cache, v_cache, b: int, cache_seqlens=None, cache_batch_idx=None, block_table=None):
+    """The (len_k, Hkv, D) keys and values that sequence ``b`` reads from a KV cache
+    (``flash_attn_with_kvcache`` docstring, arguments ``cache_seqlens``,
+    ``cache_batch_idx`` and ``block_table``).
+
+    Without a block table the caches are (batch_cache, seqlen_cache, Hkv, D) and the
+    sequence reads rows ``0 .. len_k-1`` of entry ``cache_batch_idx[b]``.  With one they
+    are (num_blocks, page, Hkv, D) and key row ``j`` is row ``j % page`` of block
+    ``block_table[b, j // page]``.  ``len_k`` is ``cache_seqlens[b]`` (default: every row
+    the sequence can address)."""
+    if block_table is not None:
+        table = np.asarray(block_table, dtype=np.int64)
+        page = k_cache.shape[1]
+        cap = table.shape[1] * page
+    else:
+        cap = k_cache.shape[1]
+    len_k = cap if cache_seqlens is None else int(np.asarray(cache_seqlens)[b])
+    if not 0 <= len_k <= cap:
+        raise ValueError("cache_seqlens out of range")
+    j = np.arange(len_k)
+    if block_table is not None:
+        if cache_batch_idx is not None:
+            raise ValueError("cache_batch_idx and block_table are exclusive")
+        blk = table[b, j // page]
+        return k_cache[blk, j % page], v_cache[blk, j % page]
+    e = b if cache_batch_idx is None else int(np.asarray(cache_batch_idx)[b])
+    return k_cache[e, :len_k], v_cache[e, :len_k]
+
+
+def forward_kvcache(q, k_cache, v_cache, cache_seqlens=None, cache_batch_idx=None, block_table=None,
+                    scale=None, causal=False, window=(-1, -1), alibi_slopes=None, threads: int = 1):
+    """Attention of q (B, Sq, Hq, D) against a read-only KV cache (layouts as in
+    :func:`gather_kvcache`).  Returns float64 O (B, Sq, Hq, D) and LSE (B, Hq, Sq); the
+    mask and bias of sequence ``b`` use ``seqlen_k = cache_seqlens[b]``."""
+    q = np.asarray(q)
+    B, Sq, hq, D = q.shape
+    hkv = k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = np.zeros((B, Sq, hq, D))
+    lse = np.zeros((B, hq, Sq))
+    kv = [gather_kvcache(k_cache, v_cache, b, cache_seqlens, cache_batch_idx, block_table) for b in range(B)]
+
+    def one(bh):
+        b, h = bh
+        g = kv_head_of(h, hq, hkv)
+        kb, vb = kv[b]
+        o[b, :, h], lse[b, h] = head_forward(q[b, :, h], kb[:, g], vb[:, g], scale, causal, window,
+                                             _slope(alibi_slopes, b, h))
+
+    _run(one, [(b, h) for b in range(B) for h in range(hq)], threads)
+    return o, lse
 
 
 def _run(fn, work, threads):
