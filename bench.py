@@ -10,7 +10,8 @@ Prints ONE JSON line: throughput in algorithmic TFLOPS (forward 4*B*H*S*S*D/2 fo
 backward 2.5x that; masked work and recomputation are not counted), the roofline of the
 dominant kernel (the backward main loop) timed per launch with HIP events on the stream
 it runs on, the fp64 CPU oracle timed on a bounded sample of the same workload, and
-extra detail: the forward of the causal GQA workload B=2, Hq=32, Hkv=8, S=8192, D=128.
+extra detail: the forward of the causal GQA workload B=2, Hq=32, Hkv=8, S=8192, D=128, and
+the split-KV decode of 16 sequences against a 32k-position bf16 KV cache (GB/s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -188,6 +189,31 @@ def sweep(steps: int, warmup: int):
                 torch.cuda.empty_cache()
 
 
+def decode_detail(steps: int, warmup: int):
+    """Split-KV decode against a read-only KV cache (fa_fwd_kvcache, split kernel plus the
+    merge kernel): 16 sequences with one new query row each, GQA 32:8 heads of 128, bf16
+    cache of 32768 positions per sequence with lengths uniform in [1, 32768].  HBM-bound:
+    reported as algorithmic bytes (every cached key and value row up to the length, q,
+    out, LSE) per second of the whole call."""
+    import torch
+    from exact_tiled_attention_02_amd import fa, synth
+    w = synth.decode_workload()
+    d = {k: v.cuda() for k, v in synth.make_kvcache_inputs(w).items()}
+    B, Sq, Hq, D = d["q"].shape
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    ns = fa.kvcache_splits(d["q"], d["k_cache"])
+    ws = torch.empty(fa.fa_fwd_kvcache_workspace_bytes(B, Sq, Hq, D, ns), dtype=torch.uint8, device="cuda")
+    run = lambda: fa.fa_fwd_kvcache(d["q"], d["k_cache"], d["v_cache"], out, lse, cache_seqlens=d["cache_seqlens"],
+                                    causal=w.causal, scale=w.softmax_scale, workspace=ws)
+    for _ in range(warmup):
+        run()
+    t = time_launches(run, steps)
+    nbytes = synth.kvcache_bytes(w)
+    return w.name, {"us": t * 1e6, "gbs": nbytes / t / 1e9, "pct_hbm_peak": 100 * nbytes / t / 1e9 / PEAK_HBM_GBS,
+                    "bytes": nbytes, "cache_tokens": sum(w.cache_lengths()), "splits_max": ns}
+
+
 def cpu_baseline(target_s: float = 12.0):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload: whole
     (batch, head) slices of forward + backward, until about target_s seconds of work."""
@@ -225,6 +251,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-gqa", action="store_true", help="skip the S=8192 GQA forward detail")
     ap.add_argument("--gqa-backward", action="store_true", help="also time the backward at the S=8192 GQA shape")
+    ap.add_argument("--skip-decode", action="store_true", help="skip the KV-cache decode detail")
     ap.add_argument("--copy-calibration", action="store_true", help="only run a 512 MiB device copy (counter scale)")
     ap.add_argument("--sweep", action="store_true", help="only run the head-dim / seqlen sweep (one JSON line each)")
     args = ap.parse_args()
@@ -311,6 +338,12 @@ def main():
         del c3
         torch.cuda.empty_cache()
 
+    if not args.skip_decode:
+        name, dd = decode_detail(K, W)
+        detail[name] = dd
+        log(f"[bench] decode {dd['us']:.1f} us -> {dd['gbs']:.0f} GB/s ({dd['pct_hbm_peak']:.1f}% of HBM peak)")
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 CPU oracle on a bounded sample")
@@ -334,7 +367,7 @@ def main():
                    PEAK_TFLOPS},
         "roofline": {"bound": "mfma", "achieved": main_tflops, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": main_tflops / PEAK_TFLOPS, "traffic": measured_traffic(),
-                     "kernel": "bwd_main_kernel<D=128, bf16, causal, padded>"},
+                     "kernel": "bwd_main_k256_kernel<D=128, bf16, causal, padded, dQ atomics>"},
         "cpu_baseline": cpu,
         "detail": detail,
     }

@@ -2,6 +2,7 @@
 // Nothing here synchronises the host or allocates device memory.
 #include "fa.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -205,6 +206,153 @@ int fa_bwd_stage(int stage, const void* dout, const void* q, const void* k, cons
   }
   return bwd_impl(1 << (stage - 1), dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal,
                   cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+int decode_row_groups(int Sq, int Hq, int Hkv) { return (int)(((long long)Sq * (Hq / Hkv) + 31) / 32); }
+
+// Upper bound on the 32-key tiles one row group of a sequence can touch: the capacity, or
+// with a left window the window's span over the Sq queries (plus one tile on each side
+// for alignment).
+int decode_span_tiles(int cap, int Sq, int causal, int wl, int wr) {
+  const long long cap_tiles = (cap + 31) / 32;
+  if (wl < 0) return (int)cap_tiles;
+  const long long right = causal ? 0 : (wr >= 0 ? wr : (long long)cap);
+  const long long keys = (long long)Sq + wl + right;
+  return (int)std::min(cap_tiles, (keys + 31) / 32 + 1);
+}
+
+// Tiles per split for a given split count.
+int decode_chunk(int span_tiles, int splits) { return (span_tiles + splits - 1) / splits; }
+
+// Smallest split count for which no split of a paged cache touches more than 64 pages
+// (the kernel keeps a split's page list in one register per lane).
+int decode_min_splits(int span_tiles, int page) {
+  if (page <= 0) return 1;
+  for (int s = 1;; ++s) {
+    const long long chunk = decode_chunk(span_tiles, s);
+    if ((chunk * 32 + page - 1) / page + 1 <= 64) return s;
+  }
+}
+
+int decode_splits_heuristic(long long units, int span_tiles, int page) {
+  // About 4096 single-wavefront workgroups when every cache is full (five rounds of three
+  // per CU on 256 CUs; shorter caches leave some splits empty, and small equal chunks
+  // keep the rest balanced), at least 8 tiles (256 keys) per split, at most 1024 splits.
+  long long s = (4096 + units - 1) / units;
+  s = std::min<long long>(s, std::max(1, span_tiles / 8));
+  s = std::min<long long>(s, 1024);
+  s = std::max<long long>(s, decode_min_splits(span_tiles, page));
+  return (int)std::max<long long>(s, 1);
+}
+
+}  // namespace
+
+int fa_fwd_kvcache_num_splits(int B, int Sq, int Hq, int Hkv, int D, int seqlen_k, int page_block_size) {
+  if (B <= 0 || Sq <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || seqlen_k <= 0) return 1;
+  (void)D;
+  const long long units = (long long)B * Hkv * decode_row_groups(Sq, Hq, Hkv);
+  return decode_splits_heuristic(units, decode_span_tiles(seqlen_k, Sq, 0, -1, -1), page_block_size);
+}
+
+size_t fa_fwd_kvcache_workspace_bytes(int B, int Sq, int Hq, int D, int num_splits) {
+  if (B <= 0 || Sq <= 0 || Hq <= 0 || D <= 0 || num_splits <= 1) return 0;
+  const size_t rows = (size_t)num_splits * B * Sq * Hq;
+  return ((rows * D * sizeof(float) + 255) & ~(size_t)255) + ((rows * sizeof(float) + 255) & ~(size_t)255);
+}
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse, int B, int Sq,
+                   int Hq, int Hkv, int D, int cache_batch, int cache_seqlen, const int32_t* cache_seqlens,
+                   const int32_t* cache_batch_idx, const int32_t* block_table, int max_blocks_per_seq, float scale,
+                   int causal, int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride,
+                   int num_splits, int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  const bool paged = block_table != nullptr;
+  const long long cap_ll = paged ? (long long)max_blocks_per_seq * cache_seqlen : (long long)cache_seqlen;
+  int st = check_common(B, Sq, cap_ll > 0 && cap_ll < (1 << 30) ? (int)cap_ll : 1, Hq, Hkv, D, scale, nullptr,
+                        nullptr, dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k_cache, "k_cache")) || (st = check_ptr(v_cache, "v_cache")) ||
+      (st = check_ptr(out, "out")) || (st = check_ptr(lse, "lse")))
+    return st;
+  if (cache_batch <= 0 || cache_seqlen <= 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "cache dimensions must be positive (%d, %d)", cache_batch, cache_seqlen);
+  if (paged) {
+    if (cache_batch_idx != nullptr)
+      return fail(FA_ERR_INVALID_ARGUMENT, "cache_batch_idx cannot be combined with a block table");
+    if (max_blocks_per_seq <= 0)
+      return fail(FA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq must be positive (got %d)", max_blocks_per_seq);
+    if (cache_seqlen % 32 != 0)
+      return fail(FA_ERR_INVALID_ARGUMENT, "page_block_size must be a multiple of 32 (got %d)", cache_seqlen);
+    if (reinterpret_cast<uintptr_t>(block_table) & 3u)
+      return fail(FA_ERR_INVALID_ARGUMENT, "block_table must be 4-byte aligned");
+  }
+  if (cap_ll >= (1 << 30)) return fail(FA_ERR_INVALID_ARGUMENT, "KV cache longer than 2^30 keys per sequence");
+  if ((double)cache_batch * cache_seqlen * Hkv * D > 9.0e15)
+    return fail(FA_ERR_INVALID_ARGUMENT, "KV cache too large");
+  if ((cache_seqlens && (reinterpret_cast<uintptr_t>(cache_seqlens) & 3u)) ||
+      (cache_batch_idx && (reinterpret_cast<uintptr_t>(cache_batch_idx) & 3u)) ||
+      (alibi_slopes && (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "cache_seqlens, cache_batch_idx and alibi_slopes must be 4-byte aligned");
+  if (window_left < -1 || window_right < -1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "window sizes must be >= -1 (got %d, %d)", window_left, window_right);
+  if (alibi_slopes && alibi_batch_stride != 0 && alibi_batch_stride != Hq)
+    return fail(FA_ERR_INVALID_ARGUMENT, "alibi_batch_stride must be 0 or Hq (got %d)", alibi_batch_stride);
+  const int cap = (int)cap_ll;
+  const int page = paged ? cache_seqlen : 0;
+  if (num_splits < 0 || num_splits > 1024)
+    return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be in [0, 1024] (got %d)", num_splits);
+  const int span = decode_span_tiles(cap, Sq, causal, window_left, window_right);
+  // With a window the span (and so the heuristic count) can only shrink, so a workspace
+  // sized by fa_fwd_kvcache_num_splits is always large enough.
+  if (num_splits == 0)
+    num_splits = decode_splits_heuristic((long long)B * Hkv * decode_row_groups(Sq, Hq, Hkv), span, page);
+  if (paged && num_splits < decode_min_splits(span, page))
+    return fail(FA_ERR_INVALID_ARGUMENT, "a paged cache of %d keys in pages of %d needs num_splits >= %d", cap, page,
+                decode_min_splits(span, page));
+  const double items = (double)B * Hkv * num_splits * decode_row_groups(Sq, Hq, Hkv);
+  if (items > 2.0e9) return fail(FA_ERR_INVALID_ARGUMENT, "too many work items");
+  const size_t need = fa_fwd_kvcache_workspace_bytes(B, Sq, Hq, D, num_splits);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "%d splits need %zu bytes of workspace, 16-byte aligned (got %zu at %p)",
+                num_splits, need, workspace_bytes, workspace);
+  fa::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.lse = lse;
+  if (need > 0) {
+    const size_t rows = (size_t)num_splits * B * Sq * Hq;
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          ((rows * D * sizeof(float) + 255) & ~(size_t)255));
+  }
+  a.cache_seqlens = cache_seqlens;
+  a.cache_batch_idx = cache_batch_idx;
+  a.block_table = block_table;
+  a.alibi = alibi_slopes;
+  a.alibi_bstride = alibi_batch_stride;
+  a.B = B;
+  a.Sq = Sq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.cap = cap;
+  a.entry_stride = (long long)cache_seqlen * Hkv * D;
+  a.page = page;
+  a.max_blocks = paged ? max_blocks_per_seq : 0;
+  a.causal = causal ? 1 : 0;
+  a.window_left = window_left;
+  a.window_right = window_right;
+  a.bf16 = dtype == FA_DTYPE_BF16;
+  a.scale = scale;
+  a.scale_log2 = exp2_scale(scale);
+  a.splits = num_splits;
+  a.chunk_tiles = decode_chunk(span, num_splits);
+  a.row_groups = decode_row_groups(Sq, Hq, Hkv);
+  return hip_status(fa::launch_decode(a, stream), "fa_fwd_kvcache launch");
 }
 
 }  // extern "C"

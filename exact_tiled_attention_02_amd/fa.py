@@ -3,7 +3,8 @@ attention computation runs in the HIP kernels behind the C ABI of include/fa.h.
 PyTorch supplies device memory and the current stream.
 
 The low-level entry points keep the C names (``fa_fwd``, ``fa_bwd``,
-``fa_bwd_workspace_bytes``); ``forward``/``backward`` additionally allocate their outputs.
+``fa_bwd_workspace_bytes``, ``fa_fwd_kvcache`` ...); ``forward``/``backward``/
+``forward_kvcache`` additionally allocate their outputs.
 There is no fallback: if libfa.so is missing, every call raises.
 """
 
@@ -42,6 +43,13 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_deterministic.restype = i
         L.fa_bwd_stage.argtypes = [i] + L.fa_bwd.argtypes
         L.fa_bwd_stage.restype = i
+        L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, i, f, i, i, i, vp, i, i, i,
+                                     vp, sz, vp]
+        L.fa_fwd_kvcache.restype = i
+        L.fa_fwd_kvcache_num_splits.argtypes = [i, i, i, i, i, i, i]
+        L.fa_fwd_kvcache_num_splits.restype = i
+        L.fa_fwd_kvcache_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.fa_fwd_kvcache_workspace_bytes.restype = sz
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_last_error.argtypes = []
@@ -202,3 +210,105 @@ def backward(dout, q, k, v, out, lse, causal: bool = False, scale: float | None 
     run(dout, q, k, v, out, lse, dq, dk, dv, ws, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
         max_seqlen_k, stream)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------- KV-cache decode
+
+def _int32_vec(t, n, name):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_contiguous() or not t.is_cuda or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor of {n} entries")
+    return t
+
+
+def _kvcache_geometry(q, k_cache, block_table):
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q is (batch, seqlen_q, heads, headdim); the caches are 4-D")
+    B, Sq, Hq, D = q.shape
+    cache_batch, cache_seqlen, Hkv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[3] != D:
+        raise ValueError("q and the caches differ in head dimension")
+    max_blocks = 0
+    if block_table is not None:
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table is (batch, max_blocks_per_seq)")
+        if block_table.dtype != torch.int32 or not block_table.is_contiguous() or not block_table.is_cuda:
+            raise ValueError("block_table must be a contiguous int32 GPU tensor")
+        max_blocks = block_table.shape[1]
+    return B, Sq, Hq, Hkv, D, cache_batch, cache_seqlen, max_blocks
+
+
+def fa_fwd_kvcache_num_splits(B: int, Sq: int, Hq: int, Hkv: int, D: int, seqlen_k: int,
+                              page_block_size: int = 0) -> int:
+    return int(lib().fa_fwd_kvcache_num_splits(B, Sq, Hq, Hkv, D, seqlen_k, page_block_size))
+
+
+def fa_fwd_kvcache_workspace_bytes(B: int, Sq: int, Hq: int, D: int, num_splits: int) -> int:
+    return int(lib().fa_fwd_kvcache_workspace_bytes(B, Sq, Hq, D, num_splits))
+
+
+def kvcache_splits(q, k_cache, block_table=None, num_splits: int = 0) -> int:
+    """Split count fa_fwd_kvcache uses for these tensors (``num_splits`` 0 = heuristic)."""
+    B, Sq, Hq, Hkv, D, _, cache_seqlen, max_blocks = _kvcache_geometry(q, k_cache, block_table)
+    if num_splits:
+        return int(num_splits)
+    cap = max_blocks * cache_seqlen if block_table is not None else cache_seqlen
+    return fa_fwd_kvcache_num_splits(B, Sq, Hq, Hkv, D, cap, cache_seqlen if block_table is not None else 0)
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, out, lse, cache_seqlens=None, cache_batch_idx=None, block_table=None,
+                   causal: bool = False, scale: float | None = None, window_size=(-1, -1), alibi_slopes=None,
+                   num_splits: int = 0, workspace=None, stream=None) -> None:
+    """Enqueue attention of q (B, Sq, Hq, D) against a read-only KV cache; writes out and
+    lse (B, Hq, Sq).  Caches are (cache_batch, cache_seqlen, Hkv, D), or pages
+    (num_blocks, page_block_size, Hkv, D) addressed through ``block_table``
+    (B, max_blocks_per_seq).  ``cache_seqlens`` / ``cache_batch_idx``: int32 (B,) GPU
+    tensors or None.  ``alibi_slopes``: fp32 (Hq,) or (B, Hq).  With more than one split
+    ``workspace`` (uint8 GPU tensor) must hold fa_fwd_kvcache_workspace_bytes(...)."""
+    B, Sq, Hq, Hkv, D, cache_batch, cache_seqlen, max_blocks = _kvcache_geometry(q, k_cache, block_table)
+    dt = _dtype(q, k_cache, v_cache, out)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache differ in shape")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    _int32_vec(cache_seqlens, B, "cache_seqlens")
+    _int32_vec(cache_batch_idx, B, "cache_batch_idx")
+    stride = 0
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_contiguous() or not alibi_slopes.is_cuda:
+            raise ValueError("alibi_slopes must be a contiguous float32 GPU tensor")
+        if tuple(alibi_slopes.shape) == (Hq,):
+            stride = 0
+        elif tuple(alibi_slopes.shape) == (B, Hq):
+            stride = Hq
+        else:
+            raise ValueError("alibi_slopes is (nheads,) or (batch, nheads)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    wl, wr = (int(window_size[0]), int(window_size[1]))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None and not workspace.is_cuda:
+        raise ValueError("workspace must live in GPU memory")
+    check(lib().fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Sq, Hq, Hkv, D,
+                               cache_batch, cache_seqlen, _ptr(cache_seqlens), _ptr(cache_batch_idx),
+                               _ptr(block_table), max_blocks, float(scale), int(bool(causal)), wl, wr,
+                               _ptr(alibi_slopes), stride, int(num_splits), dt, _ptr(workspace), ws_bytes,
+                               _stream(stream)))
+
+
+def forward_kvcache(q, k_cache, v_cache, cache_seqlens=None, cache_batch_idx=None, block_table=None,
+                    causal: bool = False, scale: float | None = None, window_size=(-1, -1), alibi_slopes=None,
+                    num_splits: int = 0, stream=None):
+    """Allocate (out, lse) and the workspace and run :func:`fa_fwd_kvcache`.
+    ``cache_seqlens`` may also be a Python int (the same length for every sequence)."""
+    B, Sq, Hq, _, D, _, _, _ = _kvcache_geometry(q, k_cache, block_table)
+    if isinstance(cache_seqlens, int):
+        cache_seqlens = torch.full((B,), cache_seqlens, dtype=torch.int32, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    n = fa_fwd_kvcache_workspace_bytes(B, Sq, Hq, D, kvcache_splits(q, k_cache, block_table, num_splits))
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    fa_fwd_kvcache(q, k_cache, v_cache, out, lse, cache_seqlens, cache_batch_idx, block_table, causal, scale,
+                   window_size, alibi_slopes, num_splits, ws, stream)
+    return out, lse

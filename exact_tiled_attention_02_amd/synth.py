@@ -135,3 +135,102 @@ def flops(w: Workload) -> tuple[float, float]:
     if w.causal:
         f *= 0.5
     return f, 2.5 * f
+
+
+# ---------------------------------------------------------------------------- KV-cache decode
+
+@dataclass
+class KVCacheWorkload:
+    """Attention of ``seqlen_q`` new query rows per sequence against a read-only KV cache.
+
+    Contiguous cache (``page`` = 0): (cache_batch, capacity, Hkv, D).  Paged cache
+    (``page`` > 0): a pool of ``cache_batch`` blocks of ``page`` rows; each sequence
+    addresses ``capacity / page`` blocks through a block table.  ``lengths`` are the
+    per-sequence cache lengths (None: every sequence uses the whole capacity);
+    ``batch_idx`` maps sequence b to a cache entry.  ``alibi`` is None, "head" (one slope
+    per query head) or "batch_head"."""
+    name: str
+    batch: int
+    seqlen_q: int
+    heads_q: int
+    heads_kv: int
+    headdim: int
+    dtype: str
+    capacity: int
+    causal: bool = True
+    cache_batch: int | None = None
+    lengths: list | None = None
+    batch_idx: list | None = None
+    page: int = 0
+    window: tuple = (-1, -1)
+    alibi: str | None = None
+    seed: int = 0
+    scale: float | None = None
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.headdim)
+
+    @property
+    def max_blocks(self) -> int:
+        return self.capacity // self.page if self.page else 0
+
+    def cache_lengths(self) -> list:
+        return list(self.lengths) if self.lengths is not None else [self.capacity] * self.batch
+
+
+def make_kvcache_inputs(w: KVCacheWorkload) -> dict:
+    """Draw q (B, Sq, Hq, D) and the caches as 16-bit CPU tensors, plus the int32
+    ``cache_seqlens`` / ``cache_batch_idx`` / ``block_table`` and fp32 ``alibi_slopes``
+    that the workload asks for (absent keys mean "not given").
+
+    Draw order: q, k_cache, v_cache (standard normal, float32, one RNE cast), then the
+    block-table permutation of the pool, then the ALiBi slopes: the usual geometric
+    schedule 2^(-8 (h+1) / Hq) times a uniform factor in [0.5, 1.5)."""
+    if w.page and w.capacity % w.page:
+        raise ValueError("capacity must be a whole number of pages")
+    rng = np.random.default_rng(w.seed)
+    D = w.headdim
+    if w.page:
+        n_blocks = w.cache_batch if w.cache_batch is not None else w.batch * w.max_blocks + 3
+        cache_shape = (n_blocks, w.page, w.heads_kv, D)
+    else:
+        n_entries = w.cache_batch if w.cache_batch is not None else w.batch
+        cache_shape = (n_entries, w.capacity, w.heads_kv, D)
+    out = {}
+    out["q"] = _cast(rng.standard_normal((w.batch, w.seqlen_q, w.heads_q, D), dtype=np.float32), w.dtype)
+    out["k_cache"] = _cast(rng.standard_normal(cache_shape, dtype=np.float32), w.dtype)
+    out["v_cache"] = _cast(rng.standard_normal(cache_shape, dtype=np.float32), w.dtype)
+    if w.page:
+        if cache_shape[0] < w.batch * w.max_blocks:
+            raise ValueError("block pool smaller than the block tables")
+        perm = rng.permutation(cache_shape[0])[: w.batch * w.max_blocks]
+        out["block_table"] = torch.tensor(perm.reshape(w.batch, w.max_blocks), dtype=torch.int32)
+    if w.lengths is not None:
+        out["cache_seqlens"] = torch.tensor(w.lengths, dtype=torch.int32)
+    if w.batch_idx is not None:
+        out["cache_batch_idx"] = torch.tensor(w.batch_idx, dtype=torch.int32)
+    if w.alibi is not None:
+        base = 2.0 ** (-8.0 * (np.arange(w.heads_q) + 1) / w.heads_q)
+        shape = (w.heads_q,) if w.alibi == "head" else (w.batch, w.heads_q)
+        out["alibi_slopes"] = torch.tensor(base * rng.uniform(0.5, 1.5, shape), dtype=torch.float32)
+    return out
+
+
+def decode_workload() -> KVCacheWorkload:
+    """Serving-style decode step: 16 sequences, one new token each, GQA 32:8 query/KV
+    heads of 128, bf16 cache of 32768 positions per sequence, cache lengths drawn uniformly
+    from [1, 32768] (seed 16)."""
+    lens = varlen_lengths(16, 16, 1, 32768)
+    return KVCacheWorkload("decode_b16_hq32_hkv8_d128_bf16_cache32k", 16, 1, 32, 8, 128, "bf16", 32768, causal=True,
+                           lengths=lens, seed=16)
+
+
+def kvcache_bytes(w: KVCacheWorkload) -> float:
+    """Algorithmic HBM bytes of one decode call without a window: the first
+    ``cache_seqlens[b]`` key and value rows of every KV head once, q read once, out written
+    once (16-bit), the LSE written once (fp32)."""
+    e = 2
+    kv = sum(w.cache_lengths()) * w.heads_kv * w.headdim * e * 2
+    qo = 2 * w.batch * w.seqlen_q * w.heads_q * w.headdim * e
+    return float(kv + qo + w.batch * w.seqlen_q * w.heads_q * 4)

@@ -124,6 +124,66 @@ int fa_bwd_stage(int stage, const void* dout, const void* q, const void* k, cons
                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                  int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Attention of a few new query rows against a read-only KV cache (incremental decoding).
+ * Sources: the flash_attn_with_kvcache docstring in "How to use FlashAttention" (cache
+ * layouts, cache_seqlens, cache_batch_idx, block_table, causal and window alignment,
+ * ALiBi) and changelog entry 2.2 (split the cache over workgroups and merge the partial
+ * results in a separate kernel) of the FlashAttention README.  Appending new keys to the
+ * cache and rotary embeddings are not part of this call.
+ *
+ *   q, out          : [B, Sq, Hq, D] (dtype);   lse : [B, Hq, Sq] fp32 (natural log,
+ *                     +inf for a row that keeps no key)
+ *   contiguous cache (block_table == NULL):
+ *     k_cache, v_cache : [cache_batch, cache_seqlen, Hkv, D]; sequence b reads entry
+ *                     cache_batch_idx[b] (int32 device array of B entries; NULL: entry b)
+ *   paged cache (block_table != NULL):
+ *     k_cache, v_cache : [num_blocks = cache_batch, page_block_size = cache_seqlen, Hkv, D];
+ *     block_table : int32 device array [B, max_blocks_per_seq]; key j of sequence b is
+ *     row j % page_block_size of block block_table[b * max_blocks_per_seq + j / page_block_size].
+ *     page_block_size must be a multiple of 32.  cache_batch_idx must be NULL.
+ *   cache_seqlens  : int32 device array of B lengths, or NULL for "every addressable key"
+ *                    (cache_seqlen, or max_blocks_per_seq * page_block_size).  Lengths are
+ *                    clamped to [0, that capacity] on the device.
+ *   causal / window_left / window_right : bottom-right aligned with seqlen_k =
+ *                    cache_seqlens[b]: query i keeps key j iff
+ *                    i + Lk - Sq - window_left <= j <= i + Lk - Sq + window_right
+ *                    (-1 = unbounded side) and, if causal, j <= i + Lk - Sq.
+ *   alibi_slopes   : NULL, or fp32 device array; the slope of (b, h) is
+ *                    alibi_slopes[b * alibi_batch_stride + h] (stride 0: one slope per
+ *                    head; stride Hq: per sequence and head).  Adds
+ *                    -slope * |i + Lk - Sq - j| to the scaled score.
+ *   num_splits     : number of key ranges per (sequence, KV head); 0 picks a count
+ *                    from the same rule as fa_fwd_kvcache_num_splits(...) applied to the
+ *                    keys the window can reach, never more than that function returns
+ *                    (so a workspace sized with it suffices).  With more than one split the
+ *                    partial results go through `workspace`, which must hold
+ *                    fa_fwd_kvcache_workspace_bytes(B, Sq, Hq, D, splits) bytes (16-byte
+ *                    aligned; contents on entry do not matter); one split writes out and
+ *                    lse directly and needs no workspace.
+ * Device-side values (lengths, indices, block-table entries) are preconditions: indices
+ * must address existing cache entries and blocks.  Errors as for fa_fwd.
+ */
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                   int B, int Sq, int Hq, int Hkv, int D, int cache_batch, int cache_seqlen,
+                   const int32_t* cache_seqlens, const int32_t* cache_batch_idx,
+                   const int32_t* block_table, int max_blocks_per_seq,
+                   float scale, int causal, int window_left, int window_right,
+                   const float* alibi_slopes, int alibi_batch_stride,
+                   int num_splits, int dtype, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * Split count fa_fwd_kvcache uses for num_splits = 0: enough (sequence, KV head, split)
+ * work items to fill the GPU, at least 256 keys per split, and (paged caches) few enough
+ * pages per split.  seqlen_k is the cache capacity per sequence; page_block_size is 0 for
+ * a contiguous cache.  Returns 1 for invalid sizes.
+ */
+int fa_fwd_kvcache_num_splits(int B, int Sq, int Hq, int Hkv, int D, int seqlen_k, int page_block_size);
+
+/* Workspace bytes fa_fwd_kvcache needs for num_splits splits (0 when num_splits <= 1). */
+size_t fa_fwd_kvcache_workspace_bytes(int B, int Sq, int Hq, int D, int num_splits);
+
 /* Static description of a status code. */
 const char* fa_status_string(int status);
 

@@ -126,3 +126,69 @@ def test_bwd_stage_rejects_bad_stage(L, stage):
 def test_bwd_stage_validates_like_fa_bwd(L):
     args = [P] * 9 + [1, 128, 128, 6, 4, 128, 0.1, 1, None, None, 1, P, 1 << 40, None]
     assert L.fa_bwd_stage(2, *args) == 1
+
+
+# ---------------------------------------------------------------------------- KV-cache decode
+
+def _kvc(L, **over):
+    a = dict(q=P, k=P, v=P, out=P, lse=P, B=2, Sq=1, Hq=8, Hkv=2, D=128, cache_batch=2, cache_seqlen=4096,
+             seqlens=None, batch_idx=None, table=None, max_blocks=0, scale=0.1, causal=1, wl=-1, wr=-1,
+             alibi=None, alibi_stride=0, splits=1, dtype=1, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    return L.fa_fwd_kvcache(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Sq"], a["Hq"], a["Hkv"], a["D"],
+                            a["cache_batch"], a["cache_seqlen"], a["seqlens"], a["batch_idx"], a["table"],
+                            a["max_blocks"], a["scale"], a["causal"], a["wl"], a["wr"], a["alibi"],
+                            a["alibi_stride"], a["splits"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+KVC_INVALID = [
+    (dict(Hq=6, Hkv=4), 1),
+    (dict(D=80), 2),
+    (dict(dtype=3), 2),
+    (dict(B=0), 1),
+    (dict(Sq=0), 1),
+    (dict(cache_seqlen=0), 1),
+    (dict(cache_batch=0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(q=None), 1),
+    (dict(k=P + 8), 1),
+    (dict(lse=None), 1),
+    (dict(wl=-2), 1),
+    (dict(wr=-5), 1),
+    (dict(alibi=P, alibi_stride=3), 1),             # neither per-head nor per-(sequence, head)
+    (dict(alibi=P + 2), 1),                          # misaligned slopes
+    (dict(seqlens=P + 1), 1),
+    (dict(table=P, max_blocks=0), 1),                # paged without a block count
+    (dict(table=P, max_blocks=4, cache_seqlen=48), 1),  # page size not a multiple of 32
+    (dict(table=P, max_blocks=4, cache_seqlen=256, batch_idx=P), 1),  # batch index with pages
+    (dict(table=P, max_blocks=4096, cache_seqlen=256, splits=1), 1),  # too many pages per split
+    (dict(splits=-1), 1),
+    (dict(splits=4, ws=None), 3),                    # several splits need a workspace
+    (dict(splits=4, ws=P, ws_bytes=64), 3),
+    (dict(splits=4, ws=P + 8, ws_bytes=1 << 40), 3),
+]
+
+
+@pytest.mark.parametrize("over,status", KVC_INVALID, ids=lambda x: str(x))
+def test_kvcache_rejects(L, over, status):
+    assert _kvc(L, **over) == status
+    assert L.fa_last_error() != b""
+
+
+def test_kvcache_split_heuristic_and_workspace(L):
+    # few (sequence, KV head) units and a long cache: many splits, at least 256 keys each
+    assert L.fa_fwd_kvcache_num_splits(1, 1, 8, 1, 128, 1 << 17, 0) == 512
+    assert L.fa_fwd_kvcache_num_splits(1, 1, 8, 1, 128, 1 << 20, 0) == 1024
+    # enough units to fill the GPU by themselves: one split
+    assert L.fa_fwd_kvcache_num_splits(512, 1, 64, 8, 128, 8192, 0) == 1
+    assert L.fa_fwd_kvcache_num_splits(128, 1, 64, 8, 128, 8192, 0) == 4
+    # short cache: at least 256 keys per split
+    assert L.fa_fwd_kvcache_num_splits(1, 1, 8, 8, 128, 1024, 0) == 4
+    # paged: never more than 64 pages in a split
+    for cap, page in ((1 << 17, 256), (1 << 17, 32), (4096, 32)):
+        s = L.fa_fwd_kvcache_num_splits(64, 1, 8, 8, 128, cap, page)
+        tps = -(-(-(-cap // 32)) // s)
+        assert -(-tps * 32 // page) + 1 <= 64
+    assert L.fa_fwd_kvcache_workspace_bytes(2, 1, 8, 128, 1) == 0
+    n = L.fa_fwd_kvcache_workspace_bytes(2, 3, 8, 128, 5)
+    assert n >= 5 * 2 * 3 * 8 * (128 + 1) * 4 and n % 256 == 0
