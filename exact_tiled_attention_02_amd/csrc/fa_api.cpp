@@ -53,6 +53,25 @@ int check_common(int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, con
   return FA_OK;
 }
 
+// Window and ALiBi arguments shared by every entry point that takes them.
+int check_mask_args(int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride, int Hq) {
+  if (window_left < -1 || window_right < -1)
+    return fail(FA_ERR_INVALID_ARGUMENT, "window sizes must be >= -1 (got %d, %d)", window_left, window_right);
+  if (alibi_slopes && (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u))
+    return fail(FA_ERR_INVALID_ARGUMENT, "alibi_slopes must be 4-byte aligned");
+  if (alibi_slopes && alibi_batch_stride != 0 && alibi_batch_stride != Hq)
+    return fail(FA_ERR_INVALID_ARGUMENT, "alibi_batch_stride must be 0 or Hq (got %d)", alibi_batch_stride);
+  return FA_OK;
+}
+
+// A window side at least as long as the sequences can reach is no limit at all: query i
+// of a sequence with Lq <= Sq queries and Lk <= Sk keys keeps j >= i + Lk - Lq - left,
+// which holds for every j >= 0 once left >= Sk, and j <= i + Lk - Lq + right, which holds
+// for every j < Lk once right >= Sq.  Mapping those to -1 keeps the kernels' index
+// arithmetic far from overflow.
+int norm_left(int wl, int Sk) { return wl >= Sk ? -1 : wl; }
+int norm_right(int wr, int Sq) { return wr >= Sq ? -1 : wr; }
+
 int check_ptr(const void* p, const char* name) {
   if (p == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
   if (!aligned16(p)) return fail(FA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
@@ -93,12 +112,14 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk, int Hq, int Hkv,
-           int D, float scale, int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
-           hipStream_t stream) {
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk, int Hq,
+              int Hkv, int D, float scale, int causal, int window_left, int window_right, const float* alibi_slopes,
+              int alibi_batch_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+              hipStream_t stream) {
   g_last_error.clear();
   int st = check_common(B, Sq, Sk, Hq, Hkv, D, scale, cu_seqlens_q, cu_seqlens_k, dtype);
   if (st != FA_OK) return st;
+  if ((st = check_mask_args(window_left, window_right, alibi_slopes, alibi_batch_stride, Hq))) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(out, "out")) || (st = check_ptr(lse, "lse")))
     return st;
@@ -117,10 +138,21 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   a.Hkv = Hkv;
   a.D = D;
   a.causal = causal ? 1 : 0;
+  a.window_left = norm_left(window_left, Sk);
+  a.window_right = norm_right(window_right, Sq);
+  a.alibi = alibi_slopes;
+  a.alibi_bstride = alibi_batch_stride;
   a.bf16 = dtype == FA_DTYPE_BF16;
   a.scale = scale;
   a.scale_log2 = exp2_scale(scale);
   return hip_status(fa::launch_fwd(a, stream), "fa_fwd launch");
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk, int Hq, int Hkv,
+           int D, float scale, int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+           hipStream_t stream) {
+  return fa_fwd_ex(q, k, v, out, lse, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1, -1, nullptr, 0, cu_seqlens_q,
+                   cu_seqlens_k, dtype, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Sq, int Hq, int D) {
@@ -135,11 +167,13 @@ namespace {
 
 int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, const void* v, const void* out,
              const float* lse, void* dq, void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv, int D,
-             float scale, int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
+             float scale, int causal, int window_left, int window_right, const float* alibi_slopes,
+             int alibi_batch_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   int st = check_common(B, Sq, Sk, Hq, Hkv, D, scale, cu_seqlens_q, cu_seqlens_k, dtype);
   if (st != FA_OK) return st;
+  if ((st = check_mask_args(window_left, window_right, alibi_slopes, alibi_batch_stride, Hq))) return st;
   if ((st = check_ptr(dout, "dout")) || (st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) ||
       (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")) || (st = check_ptr(lse, "lse")) ||
       (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
@@ -171,6 +205,10 @@ int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, con
   a.Hkv = Hkv;
   a.D = D;
   a.causal = causal ? 1 : 0;
+  a.window_left = norm_left(window_left, Sk);
+  a.window_right = norm_right(window_right, Sq);
+  a.alibi = alibi_slopes;
+  a.alibi_bstride = alibi_batch_stride;
   a.bf16 = dtype == FA_DTYPE_BF16;
   a.scale = scale;
   a.scale_log2 = exp2_scale(scale);
@@ -184,16 +222,16 @@ int fa_bwd(const void* dout, const void* q, const void* k, const void* v, const 
            void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, int causal,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, void* workspace,
            size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(7, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, cu_seqlens_q,
-                  cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
+  return bwd_impl(7, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1, -1, nullptr, 0,
+                  cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_deterministic(const void* dout, const void* q, const void* k, const void* v, const void* out,
                          const float* lse, void* dq, void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv,
                          int D, float scale, int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                          int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(1 | 8, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, cu_seqlens_q,
-                  cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
+  return bwd_impl(1 | 8, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1, -1, nullptr,
+                  0, cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_stage(int stage, const void* dout, const void* q, const void* k, const void* v, const void* out,
@@ -204,8 +242,18 @@ int fa_bwd_stage(int stage, const void* dout, const void* q, const void* k, cons
     g_last_error.clear();
     return fail(FA_ERR_INVALID_ARGUMENT, "stage %d is not 1, 2 or 3", stage);
   }
-  return bwd_impl(1 << (stage - 1), dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal,
-                  cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
+  return bwd_impl(1 << (stage - 1), dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1,
+                  -1, nullptr, 0, cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_ex(const void* dout, const void* q, const void* k, const void* v, const void* out, const float* lse,
+              void* dq, void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, int causal,
+              int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride,
+              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, int deterministic,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(deterministic ? (1 | 8) : 7, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale,
+                  causal, window_left, window_right, alibi_slopes, alibi_batch_stride, cu_seqlens_q, cu_seqlens_k,
+                  dtype, workspace, workspace_bytes, stream);
 }
 
 namespace {
@@ -292,14 +340,12 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
   if ((double)cache_batch * cache_seqlen * Hkv * D > 9.0e15)
     return fail(FA_ERR_INVALID_ARGUMENT, "KV cache too large");
   if ((cache_seqlens && (reinterpret_cast<uintptr_t>(cache_seqlens) & 3u)) ||
-      (cache_batch_idx && (reinterpret_cast<uintptr_t>(cache_batch_idx) & 3u)) ||
-      (alibi_slopes && (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)))
-    return fail(FA_ERR_INVALID_ARGUMENT, "cache_seqlens, cache_batch_idx and alibi_slopes must be 4-byte aligned");
-  if (window_left < -1 || window_right < -1)
-    return fail(FA_ERR_INVALID_ARGUMENT, "window sizes must be >= -1 (got %d, %d)", window_left, window_right);
-  if (alibi_slopes && alibi_batch_stride != 0 && alibi_batch_stride != Hq)
-    return fail(FA_ERR_INVALID_ARGUMENT, "alibi_batch_stride must be 0 or Hq (got %d)", alibi_batch_stride);
+      (cache_batch_idx && (reinterpret_cast<uintptr_t>(cache_batch_idx) & 3u)))
+    return fail(FA_ERR_INVALID_ARGUMENT, "cache_seqlens and cache_batch_idx must be 4-byte aligned");
+  if ((st = check_mask_args(window_left, window_right, alibi_slopes, alibi_batch_stride, Hq))) return st;
   const int cap = (int)cap_ll;
+  window_left = norm_left(window_left, cap);
+  window_right = norm_right(window_right, Sq);
   const int page = paged ? cache_seqlen : 0;
   if (num_splits < 0 || num_splits > 1024)
     return fail(FA_ERR_INVALID_ARGUMENT, "num_splits must be in [0, 1024] (got %d)", num_splits);

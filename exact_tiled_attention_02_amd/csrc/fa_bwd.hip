@@ -23,6 +23,11 @@
 //      wavefronts), which its register footprint requires;
 //   3. finalize: fp32 accumulator -> dQ in the input dtype.
 // The softmax scale is folded into dS once, so neither dK nor dQ is rescaled later.
+// Sliding window and ALiBi (flash_attn_func docstring, window_size and alibi_slopes): the
+// kept keys of query i are [lo(i), hi(i)] as in the forward (KeyWindow); the main loops
+// visit only the query rows that keep a key of their block, and the ALiBi bias
+// -slope * |i + Lk - Lq - j| enters P through the exponent (it does not depend on q, k or
+// v, so the gradient formulas are unchanged).
 #include <type_traits>
 
 #include "fa_device.h"
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- 2a. main loop, D = 256
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN, bool DQ>
+template <int D, bool BF16, bool MASKED, bool VARLEN, bool DQ, bool ALIBI>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
@@ -131,13 +136,30 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     lse_row0 = (size_t)b * a.Hq * a.Sq;
   }
 
-  // Query rows that can see a key of this block: i >= k0 - diag.  The work is the flat
+  // Query rows that keep a key of this block, [i_begin, i_end).  The work is the flat
   // list of (query head of the group, 32-row query block) steps.
-  int qb_begin = 0;
-  if constexpr (CAUSAL) qb_begin = max(0, k0 - diag) / kBwdBQ;
-  const int qb_end = (Lq + kBwdBQ - 1) / kBwdBQ;
+  const int k_last = min(k0 + kBwdBN, Lk) - 1;
+  int i_begin = 0, i_end = Lq;
+  int rmin = -0x3fffffff, rmax = 0x3fffffff;  // rows that keep this lane's key
+  const int my_key = k0 + threadIdx.x / 64 * 32 + (threadIdx.x & 31);
+  if constexpr (MASKED) {
+    if (a.causal) {
+      i_begin = max(0, k0 - diag);
+      rmin = my_key - diag;
+    } else if (a.window_right >= 0) {
+      i_begin = max(0, k0 - diag - a.window_right);
+      rmin = my_key - diag - a.window_right;
+    }
+    if (a.window_left >= 0) {
+      i_end = min(Lq, k_last - diag + a.window_left + 1);
+      rmax = my_key - diag + a.window_left;
+    }
+  }
+  const int qb_begin = i_begin / kBwdBQ;
+  const int qb_end = i_end > i_begin ? (i_end + kBwdBQ - 1) / kBwdBQ : qb_begin;
   const int nqs = max(0, qb_end - qb_begin);
   const int nsteps = G * nqs;
+  float sl_next = 0.f;  // ALiBi slope (exp2 units) of the step fetched last
 
   // Direct global->LDS fetch of step it's Q, dO tiles and per-row LSE, Dsum.  Rows past
   // the end of the sequence re-read its last row (they are masked to P = 0).
@@ -160,6 +182,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     const int row = min(i0 + (lane & 31), Lq - 1);
     if (wave == 0) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, &lse_s[buf][0]);
     if (wave == 1) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, &dsum_s[buf][0]);
+    if constexpr (ALIBI) sl_next = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
   };
 
   if (nsteps > 0) fetch(0, 0);
@@ -174,7 +197,6 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   }
 
   // This wavefront's keys as B operands: lane holds K[key][16 s + 8 lh .. +7].
-  const int my_key = k0 + wave * 32 + li;
   const bool key_ok = my_key < Lk;
   Frag8 kf[NS], vf[NS];
 #pragma unroll
@@ -199,6 +221,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     const int buf = it & 1;
     const int h = hk * G + it / nqs;
     const int i0 = (qb_begin + it % nqs) * kBwdBQ;
+    const float sl = sl_next;
     if (it + 1 < nsteps) fetch(it + 1, buf ^ 1);
     const uint16_t* Q = Qs[buf];
     const uint16_t* dO = dOs[buf];
@@ -220,8 +243,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       const int rl = 8 * (r >> 2) + 4 * lh + (r & 3);
       const int row = i0 + rl;
       bool keep = key_ok && row < Lq;
-      if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
-      const float p = keep ? fast_exp2(fmaf(s[r], c, -lse_s[buf][rl] * kLog2e)) : 0.f;
+      if constexpr (MASKED) keep = keep && row >= rmin && row <= rmax;
+      float bias = -lse_s[buf][rl] * kLog2e;
+      if constexpr (ALIBI) bias = fmaf(-sl, fabsf((float)(row + diag - my_key)), bias);
+      const float p = keep ? fast_exp2(fmaf(s[r], c, bias)) : 0.f;
       s[r] = p;
       dp[r] = a.scale * p * (dp[r] - dsum_s[buf][rl]);
     }
@@ -330,7 +355,7 @@ constexpr int kK2Keys = 256;
 constexpr int kK2Waves = 8;
 constexpr int kK2BQ = 32;
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN, bool DQ>
+template <int D, bool BF16, bool MASKED, bool VARLEN, bool DQ, bool ALIBI>
 __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
@@ -392,11 +417,25 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
     lse_row0 = (size_t)b * a.Hq * a.Sq;
   }
 
-  int qb_begin = 0;
-  if constexpr (CAUSAL) qb_begin = max(0, k0 - diag) / kK2BQ;
-  const int qb_end = (Lq + kK2BQ - 1) / kK2BQ;
+  // Query rows that keep a key of this block, [i_begin, i_end), and the kept range of
+  // each row (KeyWindow; without a mask every row keeps [0, Lk - 1]).
+  KeyWindow kw{Lk, diag, 0, -1, -1};
+  if constexpr (MASKED) kw = KeyWindow{Lk, diag, a.causal, a.window_left, a.window_right};
+  const int k_last = min(k0 + kK2Keys, Lk) - 1;
+  int i_begin = 0, i_end = Lq;
+  if constexpr (MASKED) {
+    if (a.causal) {
+      i_begin = max(0, k0 - diag);
+    } else if (a.window_right >= 0) {
+      i_begin = max(0, k0 - diag - a.window_right);
+    }
+    if (a.window_left >= 0) i_end = min(Lq, k_last - diag + a.window_left + 1);
+  }
+  const int qb_begin = i_begin / kK2BQ;
+  const int qb_end = i_end > i_begin ? (i_end + kK2BQ - 1) / kK2BQ : qb_begin;
   const int nqs = max(0, qb_end - qb_begin);
   const int nsteps = G * nqs;
+  float sl_next = 0.f;  // ALiBi slope (exp2 units) of the step fetched last
 
   // Q / dO tile: QT/8 chunks, one direct load per lane for D = 128 (half the lanes
   // for D = 64).
@@ -422,6 +461,8 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
     const int row = min(i0 + (lane & 31), Lq - 1);
     if (wave == kK2Waves - 1) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, lsed);
     if (wave == kK2Waves - 2) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, dsumd);
+    // Issued before the step's dQ atomics, so the end-of-step vmcnt wait covers it too.
+    if constexpr (ALIBI) sl_next = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
   };
 
   if (nsteps > 0) fetch(0, Q0, dO0, lse0, dsum0);
@@ -437,6 +478,15 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   // This wavefront's keys; V as B operands of dP = dO V^T.
   const int my_key = k0 + wave * 32 + li;
   const bool key_ok = my_key < Lk;
+  int rmin = -0x3fffffff, rmax = 0x3fffffff;  // query rows that keep my_key
+  if constexpr (MASKED) {
+    if (a.causal) {
+      rmin = my_key - diag;
+    } else if (a.window_right >= 0) {
+      rmin = my_key - diag - a.window_right;
+    }
+    if (a.window_left >= 0) rmax = my_key - diag + a.window_left;
+  }
   Frag8 vf[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st)
@@ -473,10 +523,14 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
                   uint16_t* __restrict__ dOn, float* __restrict__ lse_n, float* __restrict__ dsum_n) {
     const int h = hk * G + it / nqs;
     const int i0 = (qb_begin + it % nqs) * kK2BQ;
+    const float sl = sl_next;
     if (it + 1 < nsteps) fetch(it + 1, Qn, dOn, lse_n, dsum_n);
 
-    bool live = true;
-    if constexpr (CAUSAL) live = !mask || wave * 32 + k0 <= i0 + kK2BQ - 1 + diag;  // some key visible
+    bool live = true;  // some key of this wavefront is kept by some row of the step
+    if constexpr (MASKED) {
+      const int kw0 = k0 + wave * 32;
+      live = !mask || (kw0 <= kw.hi(min(i0 + kK2BQ, Lq) - 1) && kw0 + 31 >= kw.lo(i0));
+    }
     f32x16 s = f32x16{}, dp = f32x16{};
     if (live) {
       const int ryo = opaque(ry);
@@ -496,10 +550,12 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int row = i0 + 8 * (r >> 2) + 4 * lh + (r & 3);
         bool keep = live && key_ok && row < Lq;
-        if constexpr (CAUSAL) keep = keep && (my_key <= row + diag);
+        if constexpr (MASKED) keep = keep && row >= rmin && row <= rmax;
         s[r] = keep ? s[r] : -INFINITY;  // exp2(-inf) = 0: c is strictly positive
       }
     }
+    // Register r holds query row i0 + 8 g4 + 4 lh + j (r = 4 g4 + j) of this lane's key.
+    const float abase = (float)(i0 + 4 * lh + diag - my_key);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x4 l4 = *(const f32x4*)(lse_c + 8 * g4 + 4 * lh);
@@ -507,7 +563,9 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g4 + j;
-        const float p = fast_exp2(fmaf(s[r], c, -l4[j] * kLog2e));
+        float bias = -l4[j] * kLog2e;
+        if constexpr (ALIBI) bias = fmaf(-sl, fabsf(abase + (float)(8 * g4 + j)), bias);
+        const float p = fast_exp2(fmaf(s[r], c, bias));
         s[r] = p;
         dp[r] = a.scale * p * (dp[r] - d4[j]);
       }
@@ -558,7 +616,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
     bool sixteen = false;  // exactly 16 atomics issued after the prefetch
     if (DQ && wave < ND) {
       bool any = true;
-      if (mask) any = i0 < Lq && !(CAUSAL && k0 > i0 + kK2BQ - 1 + diag);
+      if (mask) any = i0 < Lq && k0 <= kw.hi(min(i0 + kK2BQ, Lq) - 1) && k_last >= kw.lo(i0);
       if (any) {
         f32x16 dq = f32x16{};
 #pragma unroll
@@ -596,7 +654,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   auto needs_mask = [&](int it) {
     const int i0 = (qb_begin + it % nqs) * kK2BQ;
     bool full = i0 + kK2BQ <= Lq && k0 + kK2Keys <= Lk;
-    if constexpr (CAUSAL) full = full && (k0 + kK2Keys - 1 <= i0 + diag);
+    if constexpr (MASKED) full = full && kw.lo(i0 + kK2BQ - 1) <= k0 && kw.hi(i0) >= k0 + kK2Keys - 1;
     return !full;
   };
   for (int it = 0; it < nsteps; ++it) {
@@ -640,7 +698,7 @@ constexpr int kDqWaves = 4;
 constexpr int kDqBM = 32 * kDqWaves;
 constexpr int kDqBN = 64;
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
@@ -688,12 +746,18 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
   const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
 
   const int diag = Lk - Lq;
-  int kend = Lk;
-  if constexpr (CAUSAL) kend = min(Lk, q0 + kDqBM + diag);
-  const int nkb = kend > 0 ? (kend + kDqBN - 1) / kDqBN : 0;
+  KeyWindow kw{Lk, diag, 0, -1, -1};
+  if constexpr (MASKED) kw = KeyWindow{Lk, diag, a.causal, a.window_left, a.window_right};
+  const int last_row = min(q0 + kDqBM, Lq) - 1;
+  const int k_lo = kw.lo(q0), k_hi = kw.hi(last_row);
+  const int kb_begin = k_lo / kDqBN;
+  const int kb_end = k_hi >= k_lo ? k_hi / kDqBN + 1 : kb_begin;
+  const int all_lo = kw.lo(last_row), all_hi = kw.hi(q0);
   const int my_row = q0 + wave * 32 + li;
   const bool row_ok = my_row < Lq;
   const int wave_row0 = q0 + wave * 32;
+  const int wave_lo = kw.lo(wave_row0), wave_hi = kw.hi(min(wave_row0 + 31, Lq - 1));
+  const int my_lo = kw.lo(my_row), my_hi = kw.hi(my_row);
 
   constexpr int NI = TILE / 8 / 256;
   int foff[NI];
@@ -720,7 +784,7 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
       lds_direct_load16(vt + off, Vd + first * 8);
     }
   };
-  if (nkb > 0) fetch(0, K0, V0);
+  if (kb_begin < kb_end) fetch(kb_begin, K0, V0);
 
   Frag8 qf[NS], gf[NS];
 #pragma unroll
@@ -741,6 +805,9 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
     dsum = a.dsum[(size_t)(q_start + my_row) * a.Hq + h];
   }
   const float c = a.scale_log2;
+  float sl2 = 0.f;  // ALiBi slope in exp2 units
+  if constexpr (ALIBI) sl2 = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
+  const int row_diag = my_row + diag;
 
   f32x16 acc[ND];
 #pragma unroll
@@ -763,8 +830,8 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
   auto tile = [&](int kb, bool mask, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                   uint16_t* __restrict__ Kn, uint16_t* __restrict__ Vn) {
     const int k0 = kb * kDqBN;
-    if (kb + 1 < nkb) fetch(kb + 1, Kn, Vn);
-    if (!(CAUSAL && k0 > wave_row0 + 31 + diag)) {  // some key of the tile is visible
+    if (kb + 1 < kb_end) fetch(kb + 1, Kn, Vn);
+    if (!(mask && (k0 > wave_hi || k0 + kDqBN - 1 < wave_lo))) {  // some key of the tile is kept
       f32x16 s[2], dp[2];
       const int ryo = opaque(ry);
 #pragma unroll
@@ -787,17 +854,18 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            bool keep = key < Lk;
-            if constexpr (CAUSAL) keep = keep && (key <= my_row + diag);
-            s[sub][r] = keep ? s[sub][r] : -INFINITY;
+            s[sub][r] = (key >= my_lo && key <= my_hi) ? s[sub][r] : -INFINITY;
           }
       }
       Frag8 df[4];
+      const float abase = (float)(k0 + 4 * lh - row_diag);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[sub][r], c, -lse2));
+          float bias = -lse2;
+          if constexpr (ALIBI) bias = fmaf(-sl2, fabsf(abase + (float)(sub * 32 + 8 * (r >> 2) + (r & 3))), bias);
+          const float p = fast_exp2(fmaf(s[sub][r], c, bias));
           s[sub][r] = a.scale * p * (dp[sub][r] - dsum);
         }
 #pragma unroll
@@ -823,12 +891,11 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
     __syncthreads();
   };
 
-  int n_full = Lk / kDqBN;
-  if constexpr (CAUSAL) n_full = min(n_full, q0 + diag + 1 >= 0 ? (q0 + diag + 1) / kDqBN : 0);
-  n_full = min(n_full, nkb);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bool odd = kb & 1;
-    tile(kb, kb >= n_full, odd ? K1 : K0, odd ? V1 : V0, odd ? K0 : K1, odd ? V0 : V1);
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    const bool odd = (kb - kb_begin) & 1;
+    const int k0 = kb * kDqBN;
+    const bool full = k0 >= all_lo && k0 + kDqBN - 1 <= all_hi;
+    tile(kb, !full, odd ? K1 : K0, odd ? V1 : V0, odd ? K0 : K1, odd ? V0 : V1);
   }
 
   if (row_ok) {
@@ -871,7 +938,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- launch
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   const size_t rows = (size_t)a.B * a.Sq;  // bound on total_q in varlen mode
   if (stages & 1) {
@@ -888,17 +955,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
       const int nkb = (a.Sk + kK2Keys - 1) / kK2Keys;
       const dim3 grid((unsigned)nkb * a.B * a.Hkv);
       if (det) {
-        hipLaunchKernelGGL((bwd_main_k256_kernel<D, BF16, CAUSAL, VARLEN, false>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((bwd_main_k256_kernel<D, BF16, MASKED, VARLEN, false, ALIBI>), grid, dim3(512), 0, stream, a);
       } else {
-        hipLaunchKernelGGL((bwd_main_k256_kernel<D, BF16, CAUSAL, VARLEN, true>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((bwd_main_k256_kernel<D, BF16, MASKED, VARLEN, true, ALIBI>), grid, dim3(512), 0, stream, a);
       }
     } else {
       const int nkb = (a.Sk + kBwdBN - 1) / kBwdBN;
       const dim3 grid((unsigned)nkb * a.B * a.Hkv);
       if (det) {
-        hipLaunchKernelGGL((bwd_main_kernel<D, BF16, CAUSAL, VARLEN, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_main_kernel<D, BF16, MASKED, VARLEN, false, ALIBI>), grid, dim3(256), 0, stream, a);
       } else {
-        hipLaunchKernelGGL((bwd_main_kernel<D, BF16, CAUSAL, VARLEN, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_main_kernel<D, BF16, MASKED, VARLEN, true, ALIBI>), grid, dim3(256), 0, stream, a);
       }
     }
     hipError_t e = hipGetLastError();
@@ -906,7 +973,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     if (det) {
       const int nqb = (a.Sq + kDqBM - 1) / kDqBM;
       const dim3 grid((unsigned)nqb * a.B * a.Hq);
-      hipLaunchKernelGGL((bwd_dq_pass_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_pass_kernel<D, BF16, MASKED, VARLEN, ALIBI>), grid, dim3(256), 0, stream, a);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -922,14 +989,21 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   return hipSuccess;
 }
 
+template <int D, bool BF16, bool MASKED>
+hipError_t launch_bwd_m(const BwdArgs& a, int st, hipStream_t stream) {
+  const bool varlen = a.cu_q != nullptr;
+  if (a.alibi != nullptr) {
+    return varlen ? launch_bwd_t<D, BF16, MASKED, true, true>(a, st, stream)
+                  : launch_bwd_t<D, BF16, MASKED, false, true>(a, st, stream);
+  }
+  return varlen ? launch_bwd_t<D, BF16, MASKED, true, false>(a, st, stream)
+                : launch_bwd_t<D, BF16, MASKED, false, false>(a, st, stream);
+}
+
 template <int D, bool BF16>
 hipError_t launch_bwd_d(const BwdArgs& a, int st, hipStream_t stream) {
-  const bool varlen = a.cu_q != nullptr;
-  if (a.causal) {
-    return varlen ? launch_bwd_t<D, BF16, true, true>(a, st, stream) : launch_bwd_t<D, BF16, true, false>(a, st, stream);
-  }
-  return varlen ? launch_bwd_t<D, BF16, false, true>(a, st, stream)
-                : launch_bwd_t<D, BF16, false, false>(a, st, stream);
+  const bool masked = a.causal || a.window_left >= 0 || a.window_right >= 0;
+  return masked ? launch_bwd_m<D, BF16, true>(a, st, stream) : launch_bwd_m<D, BF16, false>(a, st, stream);
 }
 
 template <int D>

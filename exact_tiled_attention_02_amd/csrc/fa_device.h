@@ -142,6 +142,22 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// Kept keys of query row i of a sequence (bottom-right aligned, diag = Lk - Lq): the
+// causal limit, the sliding window and the end of the sequence, as a closed range.
+struct KeyWindow {
+  int Lk, diag, causal, wl, wr;
+  __device__ __forceinline__ int lo(int i) const { return wl >= 0 ? (i + diag - wl > 0 ? i + diag - wl : 0) : 0; }
+  __device__ __forceinline__ int hi(int i) const {
+    int h = Lk - 1;
+    if (causal) {
+      h = h < i + diag ? h : i + diag;
+    } else if (wr >= 0) {
+      h = h < i + diag + wr ? h : i + diag + wr;
+    }
+    return h;
+  }
+};
+
 __device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void store16(void* p, u32x4 x) { *(u32x4*)p = x; }
 

@@ -20,6 +20,12 @@
 //     appears;
 //   * epilogue: O = acc / l, LSE = m * scale + ln l; a row that kept no key writes O = 0
 //     and LSE = +inf.
+// Masks (flash_attn_func docstring: causal and window paragraphs, alibi_slopes): query i
+// keeps keys lo(i) <= j <= hi(i) with the causal limit and the sliding window aligned to
+// the bottom-right corner (KeyWindow).  A workgroup visits only the key tiles its rows can
+// see; tiles inside every row's range carry no masking code, the rest set masked scores
+// to -inf.  ALiBi adds -slope * |i + Lk - Lq - j| to the scaled score; that variant runs
+// the softmax on exp2-domain scores t = S * scale*log2(e) + bias*log2(e) directly.
 //
 // Orientation: computing S^T (keys x query rows) puts one query row in each lane (and
 // its twin lane l^32), so row reductions are in-lane plus one cross-half exchange
@@ -43,7 +49,7 @@ constexpr int kFwdWaves = 4;
 constexpr int kFwdBM = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBN = 64;              // keys per tile
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   constexpr int NS = D / 16;  // 16-wide slices of the head dimension (QK^T depth)
   constexpr int ND = D / 32;  // 32-wide blocks of the head dimension (output tiles)
@@ -95,15 +101,23 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
   const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
 
-  // Key j is kept for row i iff j <= i + diag (bottom-right alignment).
+  // Kept keys of row i: [kw.lo(i), kw.hi(i)], both non-decreasing in i.  Without a mask
+  // every row keeps [0, Lk - 1].
   const int diag = Lk - Lq;
-  int kend = Lk;
-  if constexpr (CAUSAL) kend = min(Lk, q0 + kFwdBM + diag);
-  const int nkb = kend > 0 ? (kend + kFwdBN - 1) / kFwdBN : 0;
+  KeyWindow kw{Lk, diag, 0, -1, -1};
+  if constexpr (MASKED) kw = KeyWindow{Lk, diag, a.causal, a.window_left, a.window_right};
+  const int last_row = min(q0 + kFwdBM, Lq) - 1;
+  // Tiles any row of the block can see, and the key range that every row keeps.
+  const int k_lo = kw.lo(q0), k_hi = kw.hi(last_row);
+  const int kb_begin = k_lo / kFwdBN;
+  const int kb_end = k_hi >= k_lo ? k_hi / kFwdBN + 1 : kb_begin;
+  const int all_lo = kw.lo(last_row), all_hi = kw.hi(q0);
 
   const int my_row = q0 + wave * 32 + li;
   const bool row_ok = my_row < Lq;
   const int wave_row0 = q0 + wave * 32;
+  const int wave_lo = kw.lo(wave_row0), wave_hi = kw.hi(min(wave_row0 + 31, Lq - 1));
+  const int my_lo = kw.lo(my_row), my_hi = kw.hi(my_row);
 
   // Direct global->LDS fetch of key/value tile kb into buffer buf.  The per-lane source
   // offsets do not depend on the tile; only a tile reaching past the end of the
@@ -143,7 +157,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
   };
 
-  if (nkb > 0) fetch(0, std::false_type{});
+  // Processing order: first the run of tiles inside the key range every row keeps (an
+  // even number of them, without masking code), then the remaining edge tiles -- those
+  // before the run (window) and after it (diagonal, tail) -- with masking.  The online
+  // softmax does not depend on the order.  Tiles alternate between the two buffers in
+  // processing order, so both loops advance in pairs and name the buffers statically.
+  const int u0 = min(max(kb_begin, (all_lo + kFwdBN - 1) / kFwdBN), kb_end);
+  int u1 = all_hi >= 0 ? min(kb_end, (all_hi + 1) / kFwdBN) : 0;
+  u1 = u1 > u0 ? u0 + ((u1 - u0) & ~1) : u0;
+  const int n_lead = u0 - kb_begin;
+  const int n_mask = n_lead + (kb_end - u1);
+  auto masked_kb = [&](int j) { return j < n_lead ? kb_begin + j : u1 + (j - n_lead); };
+  if (u1 > u0) {
+    fetch(u0, std::false_type{});
+  } else if (n_mask > 0) {
+    fetch(masked_kb(0), std::false_type{});
+  }
 
   // Q^T operand: lane holds Q[my_row][16 s + 8 lh .. +7] for every slice s.
   Frag8 qf[NS];
@@ -155,9 +184,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   f32x16 acc[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;  // running max: raw scores, or exp2-domain scores with ALiBi
   float l_run = 0.f;
   const float c = a.scale_log2;
+  constexpr float kLog2e = 1.4426950408889634f;
+  float sl2 = 0.f;  // ALiBi slope in exp2 units, and this row's diagonal key
+  if constexpr (ALIBI) sl2 = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
+  const int row_diag = my_row + diag;
 
   const int tr_row = 4 * lh + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -177,16 +210,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   wait_all_memory();
   __syncthreads();
 
-  // One key tile.  MASK selects the variant for tiles that touch the causal diagonal or
-  // the sequence tail; interior tiles carry no masking code at all.
-  auto tile = [&](int kb, auto mask_tag, auto buf_tag) {
+  // One key tile.  MASK selects the variant for tiles at the edges of the kept range
+  // (causal diagonal, window borders, sequence tail); interior tiles carry no masking
+  // code at all.
+  auto tile = [&](int kb, int next, auto mask_tag, auto buf_tag) {
     constexpr bool BUF = decltype(buf_tag)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = kb * kFwdBN;
-    if (kb + 1 < nkb) fetch(kb + 1, std::integral_constant<bool, !BUF>{});
+    if (next >= 0) fetch(next, std::integral_constant<bool, !BUF>{});
 
     // A wavefront whose rows keep no key of this tile has nothing to add.
-    if (!(MASK && CAUSAL && k0 > wave_row0 + 31 + diag)) {
+    if (!(MASK && (k0 > wave_hi || k0 + kFwdBN - 1 < wave_lo))) {
       const uint16_t* K = BUF ? K1 : K0;
       const uint16_t* V = BUF ? V1 : V0;
       // S^T (keys x rows): two 32-key blocks.
@@ -202,17 +236,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         }
       }
 
+      // ALiBi: scores move to the exp2 domain with the bias added,
+      // t = S c - slope log2(e) |key - (row + diag)|.
+      if constexpr (ALIBI) {
+        const float base = (float)(k0 + 4 * lh - row_diag);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float dist = base + (float)(sub * 32 + 8 * (r >> 2) + (r & 3));
+            s[sub][r] = fmaf(-sl2, fabsf(dist), s[sub][r] * c);
+          }
+      }
       // Masked scores become -inf, so their probabilities are exp2(-inf) = 0 (the factor c
-      // is strictly positive).  Only tiles touching the diagonal or the tail need it.
+      // is strictly positive).  Only tiles at the edges of the kept range need it.
       if constexpr (MASK) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            bool keep = key < Lk;
-            if constexpr (CAUSAL) keep = keep && (key <= my_row + diag);
-            s[sub][r] = keep ? s[sub][r] : -INFINITY;
+            s[sub][r] = (key >= my_lo && key <= my_hi) ? s[sub][r] : -INFINITY;
           }
         }
       }
@@ -224,19 +268,32 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
       mx = pair_max(mx);
       const float m_use = (mx == -INFINITY) ? 0.f : mx;
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
-      m_run = mx;
-      const float mc = m_use * c;
-
+      float alpha;
       float ls = 0.f;
+      if constexpr (ALIBI) {
+        alpha = fast_exp2(m_run - m_use);  // 0 while nothing was kept
+        m_run = mx;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(s[sub][r] - m_use);
+            s[sub][r] = p;
+            ls += p;
+          }
+      } else {
+        alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
+        m_run = mx;
+        const float mc = m_use * c;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
             const float p = fast_exp2(fmaf(s[sub][r], c, -mc));
-          s[sub][r] = p;
-          ls += p;
-        }
+            s[sub][r] = p;
+            ls += p;
+          }
+      }
       l_run = l_run * alpha + ls;
       // Rescale the accumulator; when no row of the wavefront changed its maximum every
       // factor is exactly 1.0f and the multiplication is skipped (bitwise identical).
@@ -270,26 +327,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     __syncthreads();    // ... and every wavefront is done with the current one
   };
 
-  // Leading tiles that no row of the workgroup masks, then the diagonal / tail tiles.
-  int n_full = Lk / kFwdBN;
-  if constexpr (CAUSAL) n_full = min(n_full, q0 + diag + 1 >= 0 ? (q0 + diag + 1) / kFwdBN : 0);
-  n_full = min(n_full, nkb);
-  // Tile kb lives in buffer kb % 2; both loops advance in pairs so that every buffer is
-  // named statically (an odd interior tile count leaves one interior tile to the masked
-  // variant, which is correct for any tile).
   using B0 = std::false_type;
   using B1 = std::true_type;
-  n_full &= ~1;
-  int kb = 0;
-  for (; kb < n_full; kb += 2) {
-    tile(kb, std::false_type{}, B0{});
-    tile(kb + 1, std::false_type{}, B1{});
+  for (int kb = u0; kb < u1; kb += 2) {
+    tile(kb, kb + 1, std::false_type{}, B0{});
+    tile(kb + 1, kb + 2 < u1 ? kb + 2 : (n_mask > 0 ? masked_kb(0) : -1), std::false_type{}, B1{});
   }
-  for (; kb + 2 <= nkb; kb += 2) {
-    tile(kb, std::true_type{}, B0{});
-    tile(kb + 1, std::true_type{}, B1{});
+  int j = 0;
+  for (; j + 2 <= n_mask; j += 2) {
+    tile(masked_kb(j), masked_kb(j + 1), std::true_type{}, B0{});
+    tile(masked_kb(j + 1), j + 2 < n_mask ? masked_kb(j + 2) : -1, std::true_type{}, B1{});
   }
-  if (kb < nkb) tile(kb, std::true_type{}, B0{});
+  if (j < n_mask) tile(masked_kb(j), -1, std::true_type{}, B0{});
 
   // Epilogue.
   const float l_tot = pair_sum(l_run);
@@ -308,7 +357,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       }
     }
     if (lh == 0) {
-      const float lse = l_tot > 0.f ? m_run * a.scale + __logf(l_tot) : INFINITY;
+      float lse = INFINITY;
+      if (l_tot > 0.f) lse = (ALIBI ? m_run * 0.69314718055994531f : m_run * a.scale) + __logf(l_tot);
       size_t idx;
       if constexpr (VARLEN) {
         idx = (size_t)h * a.cu_q[a.B] + q_start + my_row;
@@ -320,21 +370,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (a.Sq + kFwdBM - 1) / kFwdBM;
   const dim3 grid((unsigned)nqb * a.B * a.Hq);
-  hipLaunchKernelGGL((fwd_kernel<D, BF16, CAUSAL, VARLEN>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, BF16, MASKED, VARLEN, ALIBI>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, bool BF16, bool MASKED>
+hipError_t launch_fwd_m(const FwdArgs& a, hipStream_t stream) {
+  const bool varlen = a.cu_q != nullptr;
+  if (a.alibi != nullptr) {
+    return varlen ? launch_fwd_t<D, BF16, MASKED, true, true>(a, stream)
+                  : launch_fwd_t<D, BF16, MASKED, false, true>(a, stream);
+  }
+  return varlen ? launch_fwd_t<D, BF16, MASKED, true, false>(a, stream)
+                : launch_fwd_t<D, BF16, MASKED, false, false>(a, stream);
 }
 
 template <int D, bool BF16>
 hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
-  const bool varlen = a.cu_q != nullptr;
-  if (a.causal) {
-    return varlen ? launch_fwd_t<D, BF16, true, true>(a, stream) : launch_fwd_t<D, BF16, true, false>(a, stream);
-  }
-  return varlen ? launch_fwd_t<D, BF16, false, true>(a, stream) : launch_fwd_t<D, BF16, false, false>(a, stream);
+  const bool masked = a.causal || a.window_left >= 0 || a.window_right >= 0;
+  return masked ? launch_fwd_m<D, BF16, true>(a, stream) : launch_fwd_m<D, BF16, false>(a, stream);
 }
 
 template <int D>

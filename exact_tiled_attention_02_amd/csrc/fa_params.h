@@ -17,6 +17,10 @@ struct FwdArgs {
   const int32_t* cu_k;
   int B, Sq, Sk, Hq, Hkv, D;
   int causal;
+  int window_left;   // sliding window (-1: unbounded; normalised to < Sk, < Sq by the host)
+  int window_right;
+  const float* alibi;  // ALiBi slopes alibi[b * alibi_bstride + h], or null
+  int alibi_bstride;
   int bf16;
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
@@ -38,6 +42,10 @@ struct BwdArgs {
   const int32_t* cu_k;
   int B, Sq, Sk, Hq, Hkv, D;
   int causal;
+  int window_left;   // as in FwdArgs
+  int window_right;
+  const float* alibi;
+  int alibi_bstride;
   int bf16;
   float scale;
   float scale_log2;

@@ -43,6 +43,11 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_deterministic.restype = i
         L.fa_bwd_stage.argtypes = [i] + L.fa_bwd.argtypes
         L.fa_bwd_stage.restype = i
+        L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, i, vp, vp, i, vp]
+        L.fa_fwd_ex.restype = i
+        L.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, i, vp, vp, i, i,
+                                vp, sz, vp]
+        L.fa_bwd_ex.restype = i
         L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, i, f, i, i, i, vp, i, i, i,
                                      vp, sz, vp]
         L.fa_fwd_kvcache.restype = i
@@ -117,17 +122,43 @@ def _dtype(*ts):
     return _DTYPE_CODE[d]
 
 
+def _alibi_stride(alibi_slopes, B, Hq):
+    """Batch stride of an ALiBi slope tensor: (Hq,) -> 0, (B, Hq) -> Hq."""
+    if alibi_slopes is None:
+        return 0
+    if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_contiguous() or not alibi_slopes.is_cuda:
+        raise ValueError("alibi_slopes must be a contiguous float32 GPU tensor")
+    if tuple(alibi_slopes.shape) == (Hq,):
+        return 0
+    if tuple(alibi_slopes.shape) == (B, Hq):
+        return Hq
+    raise ValueError("alibi_slopes is (nheads,) or (batch, nheads)")
+
+
+def _plain(window_size, alibi_slopes) -> bool:
+    return alibi_slopes is None and tuple(window_size) == (-1, -1)
+
+
 def fa_fwd(q, k, v, out, lse, causal: bool = False, scale: float | None = None, cu_seqlens_q=None,
-           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None) -> None:
-    """Enqueue the forward on ``stream`` (default: torch's current stream); writes out, lse."""
+           cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None, window_size=(-1, -1),
+           alibi_slopes=None) -> None:
+    """Enqueue the forward on ``stream`` (default: torch's current stream); writes out, lse.
+    ``window_size`` = (left, right) sliding window (-1: unbounded); ``alibi_slopes`` fp32
+    (Hq,) or (B, Hq).  Without either this is the C ``fa_fwd``, else ``fa_fwd_ex``."""
     B, Sq, Sk, Hq, Hkv, D = _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     dt = _dtype(q, k, v, out)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 GPU tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, float(scale),
-                       int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), dt, _stream(stream)))
+    if _plain(window_size, alibi_slopes):
+        check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, float(scale),
+                           int(bool(causal)), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), dt, _stream(stream)))
+        return
+    stride = _alibi_stride(alibi_slopes, B, Hq)
+    check(lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Sk, Hq, Hkv, D, float(scale),
+                          int(bool(causal)), int(window_size[0]), int(window_size[1]), _ptr(alibi_slopes), stride,
+                          _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), dt, _stream(stream)))
 
 
 def fa_bwd_workspace_bytes(B: int, Sq: int, Hq: int, D: int) -> int:
@@ -135,11 +166,42 @@ def fa_bwd_workspace_bytes(B: int, Sq: int, Hq: int, D: int) -> int:
 
 
 def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: bool = False, scale: float | None = None,
-           cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None) -> None:
+           cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None,
+           window_size=(-1, -1), alibi_slopes=None) -> None:
     """Enqueue the backward; writes dq, dk, dv.  ``workspace``: a uint8 device tensor of
-    at least fa_bwd_workspace_bytes(B, Sq, Hq, D) bytes."""
-    fa_bwd_stage(0, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q, cu_seqlens_k,
-                 max_seqlen_q, max_seqlen_k, stream)
+    at least fa_bwd_workspace_bytes(B, Sq, Hq, D) bytes.  With a window or ALiBi this is
+    the C ``fa_bwd_ex``."""
+    if _plain(window_size, alibi_slopes):
+        fa_bwd_stage(0, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q, cu_seqlens_k,
+                     max_seqlen_q, max_seqlen_k, stream)
+    else:
+        _bwd_ex(False, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q, cu_seqlens_k,
+                max_seqlen_q, max_seqlen_k, stream, window_size, alibi_slopes)
+
+
+def _bwd_args(dout, q, k, v, out, lse, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+              max_seqlen_k):
+    B, Sq, Sk, Hq, Hkv, D = _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    dt = _dtype(q, k, v, out, dout, dq, dk, dv)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    if not workspace.is_cuda:
+        raise ValueError("workspace must live in GPU memory")
+    return B, Sq, Sk, Hq, Hkv, D, dt
+
+
+def _bwd_ex(deterministic, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q,
+            cu_seqlens_k, max_seqlen_q, max_seqlen_k, stream, window_size, alibi_slopes):
+    B, Sq, Sk, Hq, Hkv, D, dt = _bwd_args(dout, q, k, v, out, lse, dq, dk, dv, workspace, cu_seqlens_q,
+                                          cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    stride = _alibi_stride(alibi_slopes, B, Hq)
+    check(lib().fa_bwd_ex(_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                          B, Sq, Sk, Hq, Hkv, D, float(scale), int(bool(causal)), int(window_size[0]),
+                          int(window_size[1]), _ptr(alibi_slopes), stride, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                          dt, int(bool(deterministic)), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def fa_bwd_stage(stage, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: bool = False,
@@ -147,12 +209,8 @@ def fa_bwd_stage(stage, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: 
                  max_seqlen_k=None, stream=None) -> None:
     """Enqueue one backward stage (1 preprocess, 2 main loop, 3 finalize); stage 0 runs
     the whole backward (``fa_bwd``)."""
-    B, Sq, Sk, Hq, Hkv, D = _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
-    dt = _dtype(q, k, v, out, dout, dq, dk, dv)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous float32 GPU tensor")
-    if not workspace.is_cuda:
-        raise ValueError("workspace must live in GPU memory")
+    B, Sq, Sk, Hq, Hkv, D, dt = _bwd_args(dout, q, k, v, out, lse, dq, dk, dv, workspace, cu_seqlens_q,
+                                          cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     args = (_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, Sq, Sk,
@@ -168,10 +226,14 @@ def fa_bwd_stage(stage, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: 
 
 def fa_bwd_deterministic(dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: bool = False,
                          scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
-                         max_seqlen_k=None, stream=None) -> None:
+                         max_seqlen_k=None, stream=None, window_size=(-1, -1), alibi_slopes=None) -> None:
     """Enqueue the deterministic backward (dQ by a separate pass, no atomics)."""
-    fa_bwd_stage("deterministic", dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q,
-                 cu_seqlens_k, max_seqlen_q, max_seqlen_k, stream)
+    if _plain(window_size, alibi_slopes):
+        fa_bwd_stage("deterministic", dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q,
+                     cu_seqlens_k, max_seqlen_q, max_seqlen_k, stream)
+    else:
+        _bwd_ex(True, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q, cu_seqlens_k,
+                max_seqlen_q, max_seqlen_k, stream, window_size, alibi_slopes)
 
 
 def lse_shape(q, cu_seqlens_q=None):
@@ -182,11 +244,12 @@ def lse_shape(q, cu_seqlens_q=None):
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None,
-            max_seqlen_q=None, max_seqlen_k=None, stream=None):
+            max_seqlen_q=None, max_seqlen_k=None, stream=None, window_size=(-1, -1), alibi_slopes=None):
     """Allocate (out, lse) and run :func:`fa_fwd`."""
     out = torch.empty_like(q)
     lse = torch.empty(lse_shape(q, cu_seqlens_q), dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, out, lse, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, stream)
+    fa_fwd(q, k, v, out, lse, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, stream,
+           window_size, alibi_slopes)
     return out, lse
 
 
@@ -201,14 +264,15 @@ def workspace_for(q, cu_seqlens_q=None, max_seqlen_q=None):
 
 
 def backward(dout, q, k, v, out, lse, causal: bool = False, scale: float | None = None, cu_seqlens_q=None,
-             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None, deterministic: bool = False):
+             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None, deterministic: bool = False,
+             window_size=(-1, -1), alibi_slopes=None):
     """Allocate (dq, dk, dv) and the workspace, and run :func:`fa_bwd` (or
     :func:`fa_bwd_deterministic`)."""
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = workspace_for(q, cu_seqlens_q, max_seqlen_q)
     run = fa_bwd_deterministic if deterministic else fa_bwd
     run(dout, q, k, v, out, lse, dq, dk, dv, ws, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-        max_seqlen_k, stream)
+        max_seqlen_k, stream, window_size, alibi_slopes)
     return dq, dk, dv
 
 
@@ -274,16 +338,7 @@ def fa_fwd_kvcache(q, k_cache, v_cache, out, lse, cache_seqlens=None, cache_batc
         raise ValueError("lse must be a contiguous float32 GPU tensor")
     _int32_vec(cache_seqlens, B, "cache_seqlens")
     _int32_vec(cache_batch_idx, B, "cache_batch_idx")
-    stride = 0
-    if alibi_slopes is not None:
-        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_contiguous() or not alibi_slopes.is_cuda:
-            raise ValueError("alibi_slopes must be a contiguous float32 GPU tensor")
-        if tuple(alibi_slopes.shape) == (Hq,):
-            stride = 0
-        elif tuple(alibi_slopes.shape) == (B, Hq):
-            stride = Hq
-        else:
-            raise ValueError("alibi_slopes is (nheads,) or (batch, nheads)")
+    stride = _alibi_stride(alibi_slopes, B, Hq)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     wl, wr = (int(window_size[0]), int(window_size[1]))

@@ -41,6 +41,8 @@ class Workload:
     seed: int = 0
     scale: float | None = None
     extra: dict = field(default_factory=dict)
+    window: tuple = (-1, -1)
+    alibi: str | None = None  # None, "head" (Hq,) or "batch_head" (B, Hq) slopes
 
     @property
     def varlen(self) -> bool:
@@ -71,8 +73,17 @@ def varlen_lengths(seed: int, n: int, lo: int, hi: int) -> list:
     return [int(x) for x in rng.integers(lo, hi + 1, n)]
 
 
+def alibi_slopes(rng: np.random.Generator, heads_q: int, batch: int, kind: str) -> torch.Tensor:
+    """ALiBi slopes: the usual geometric schedule 2^(-8 (h+1) / Hq) times a uniform factor
+    in [0.5, 1.5), one per query head ("head") or per (sequence, head) ("batch_head")."""
+    base = 2.0 ** (-8.0 * (np.arange(heads_q) + 1) / heads_q)
+    shape = (heads_q,) if kind == "head" else (batch, heads_q)
+    return torch.tensor(base * rng.uniform(0.5, 1.5, shape), dtype=torch.float32)
+
+
 def make_inputs(w: Workload, rng: np.random.Generator | None = None) -> dict:
-    """Draw q, k, v (and dO when ``w.backward``) as 16-bit CPU tensors.
+    """Draw q, k, v (and dO when ``w.backward``, then ALiBi slopes when ``w.alibi``) as
+    CPU tensors (16-bit data, fp32 slopes).
 
     Padded: q/do (B, Sq, Hq, D), k/v (B, Sk, Hkv, D).  Varlen: q/do (total_q, Hq, D),
     k/v (total_k, Hkv, D) plus int32 ``cu_seqlens_q``/``cu_seqlens_k`` of length B+1."""
@@ -91,6 +102,8 @@ def make_inputs(w: Workload, rng: np.random.Generator | None = None) -> dict:
     out["v"] = _cast(rng.standard_normal(sk, dtype=np.float32), w.dtype)
     if w.backward:
         out["do"] = _cast(rng.standard_normal(sq, dtype=np.float32), w.dtype)
+    if w.alibi is not None:
+        out["alibi_slopes"] = alibi_slopes(rng, w.heads_q, w.batch, w.alibi)
     if w.varlen:
         out["cu_seqlens_q"] = torch.tensor(np.concatenate([[0], np.cumsum(w.lengths_q)]), dtype=torch.int32)
         out["cu_seqlens_k"] = torch.tensor(np.concatenate([[0], np.cumsum(w.lengths_k)]), dtype=torch.int32)
@@ -211,9 +224,7 @@ def make_kvcache_inputs(w: KVCacheWorkload) -> dict:
     if w.batch_idx is not None:
         out["cache_batch_idx"] = torch.tensor(w.batch_idx, dtype=torch.int32)
     if w.alibi is not None:
-        base = 2.0 ** (-8.0 * (np.arange(w.heads_q) + 1) / w.heads_q)
-        shape = (w.heads_q,) if w.alibi == "head" else (w.batch, w.heads_q)
-        out["alibi_slopes"] = torch.tensor(base * rng.uniform(0.5, 1.5, shape), dtype=torch.float32)
+        out["alibi_slopes"] = alibi_slopes(rng, w.heads_q, w.batch, w.alibi)
     return out
 
 

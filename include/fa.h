@@ -72,6 +72,24 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
            int dtype, hipStream_t stream);
 
 /*
+ * Forward with a sliding window and/or ALiBi (flash_attn_func docstring, "How to use
+ * FlashAttention": window_size and alibi_slopes arguments; changelog entries 2.3 and
+ * 2.4).  Query i keeps key j iff
+ *     i + Lk - Lq - window_left <= j <= i + Lk - Lq + window_right
+ * (-1 = that side unbounded) and, if causal, j <= i + Lk - Lq, per sequence.  With
+ * alibi_slopes (NULL: none; fp32 device array, slope of (b, h) at
+ * alibi_slopes[b * alibi_batch_stride + h], stride 0 or Hq) the bias
+ * -slope * |i + Lk - Lq - j| is added to the scaled score; the LSE is that of the biased
+ * scores.  fa_fwd(...) is fa_fwd_ex(..., -1, -1, NULL, 0, ...).  Other arguments, layouts
+ * and errors as for fa_fwd; window sizes below -1 or another stride are rejected.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+              int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, int causal,
+              int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride,
+              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+              int dtype, hipStream_t stream);
+
+/*
  * Bytes of device workspace fa_bwd needs: an fp32 dQ accumulator and an fp32 row
  * statistic (sum_d dO*O) for B*Sq rows of Hq heads (for varlen, B*Sq bounds total_q).
  * Returns 0 for invalid sizes.
@@ -107,6 +125,21 @@ int fa_bwd_deterministic(const void* dout, const void* q, const void* k, const v
                          int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, int causal,
                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                          int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward with a sliding window and/or ALiBi, the counterpart of fa_fwd_ex (same mask and
+ * bias arguments; out and lse must come from fa_fwd_ex with the same ones).  The bias does
+ * not depend on q, k or v, so the gradient formulas are unchanged; masked pairs get zero
+ * gradient.  deterministic != 0 selects the fa_bwd_deterministic scheme.  Workspace and
+ * errors as for fa_bwd.
+ */
+int fa_bwd_ex(const void* dout, const void* q, const void* k, const void* v,
+              const void* out, const float* lse, void* dq, void* dk, void* dv,
+              int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, int causal,
+              int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride,
+              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+              int dtype, int deterministic, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
 
 /*
  * One stage of fa_bwd, for callers that schedule or time the stages themselves.

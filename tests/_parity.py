@@ -44,7 +44,8 @@ def run_forward(w: synth.Workload, x: dict, poison: bool = True):
     if w.varlen:
         kw = dict(cu_seqlens_q=d["cu_seqlens_q"], cu_seqlens_k=d["cu_seqlens_k"], max_seqlen_q=w.seqlen_q,
                   max_seqlen_k=w.seqlen_k)
-    fa.fa_fwd(d["q"], d["k"], d["v"], out, lse, causal=w.causal, scale=w.softmax_scale, **kw)
+    fa.fa_fwd(d["q"], d["k"], d["v"], out, lse, causal=w.causal, scale=w.softmax_scale, window_size=w.window,
+              alibi_slopes=d.get("alibi_slopes"), **kw)
     torch.cuda.synchronize()
     return out, lse, d
 
@@ -53,8 +54,9 @@ def oracle_forward(w: synth.Workload, x: dict):
     kw = {}
     if w.varlen:
         kw = dict(cu_seqlens_q=x["cu_seqlens_q"].numpy(), cu_seqlens_k=x["cu_seqlens_k"].numpy())
+    slopes = x["alibi_slopes"].numpy() if "alibi_slopes" in x else None
     return orc.forward(f64(x["q"]), f64(x["k"]), f64(x["v"]), scale=w.softmax_scale, causal=w.causal,
-                       threads=THREADS, **kw)
+                       threads=THREADS, window=w.window, alibi_slopes=slopes, **kw)
 
 
 def compare_forward(w: synth.Workload, o_gpu, lse_gpu, o_ref, lse_ref, where: str = ""):
@@ -106,7 +108,12 @@ def check_forward_sampled(w: synth.Workload, x: dict, o_gpu, lse_gpu, heads, see
         if lq == 0:
             continue
         rows = sampled_rows(lq, rng)
-        o_ref, lse_ref = orc.rows_forward(f64(qs[rows]), rows, f64(ks), f64(vs), w.softmax_scale, w.causal, lq)
+        slope = None
+        if "alibi_slopes" in x:
+            a = x["alibi_slopes"].numpy()
+            slope = float(a[h] if a.ndim == 1 else a[b, h])
+        o_ref, lse_ref = orc.rows_forward(f64(qs[rows]), rows, f64(ks), f64(vs), w.softmax_scale, w.causal, lq,
+                                          window=w.window, alibi_slope=slope)
         e = compare_forward(w, og[rows], lg[rows], o_ref, lse_ref, where=f"{w.name} seq {b} head {h}")
         worst = (max(worst[0], e[0]), max(worst[1], e[1]))
     return worst

@@ -192,3 +192,44 @@ def test_kvcache_split_heuristic_and_workspace(L):
     assert L.fa_fwd_kvcache_workspace_bytes(2, 1, 8, 128, 1) == 0
     n = L.fa_fwd_kvcache_workspace_bytes(2, 3, 8, 128, 5)
     assert n >= 5 * 2 * 3 * 8 * (128 + 1) * 4 and n % 256 == 0
+
+
+# ---------------------------------------------------------------------------- window / ALiBi entry points
+
+def _fwd_ex(L, **over):
+    a = dict(q=P, k=P, v=P, out=P, lse=P, B=1, Sq=128, Sk=128, Hq=4, Hkv=2, D=128, scale=0.1, causal=1, wl=-1,
+             wr=-1, alibi=None, stride=0, cu_q=None, cu_k=None, dtype=1, stream=None)
+    a.update(over)
+    return L.fa_fwd_ex(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hkv"],
+                       a["D"], a["scale"], a["causal"], a["wl"], a["wr"], a["alibi"], a["stride"], a["cu_q"],
+                       a["cu_k"], a["dtype"], a["stream"])
+
+
+def _bwd_ex(L, **over):
+    a = dict(do=P, q=P, k=P, v=P, out=P, lse=P, dq=P, dk=P, dv=P, B=1, Sq=128, Sk=128, Hq=4, Hkv=2, D=128,
+             scale=0.1, causal=1, wl=-1, wr=-1, alibi=None, stride=0, cu_q=None, cu_k=None, dtype=1, det=0, ws=P,
+             ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    return L.fa_bwd_ex(a["do"], a["q"], a["k"], a["v"], a["out"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                       a["Sq"], a["Sk"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["wl"], a["wr"],
+                       a["alibi"], a["stride"], a["cu_q"], a["cu_k"], a["dtype"], a["det"], a["ws"], a["ws_bytes"],
+                       a["stream"])
+
+
+EX_INVALID = INVALID + [
+    (dict(wl=-2), 1),
+    (dict(wr=-7), 1),
+    (dict(alibi=P, stride=3), 1),   # stride must be 0 or Hq
+    (dict(alibi=P + 2), 1),         # misaligned slopes
+]
+
+
+@pytest.mark.parametrize("over,status", EX_INVALID, ids=lambda x: str(x))
+def test_fwd_ex_rejects(L, over, status):
+    assert _fwd_ex(L, **over) == status
+
+
+@pytest.mark.parametrize("over,status", EX_INVALID + [(dict(ws=None), 3), (dict(ws_bytes=16), 3)],
+                         ids=lambda x: str(x))
+def test_bwd_ex_rejects(L, over, status):
+    assert _bwd_ex(L, **over) == status

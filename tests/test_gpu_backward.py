@@ -22,7 +22,8 @@ def run_fwd_bwd(w, x, poison=True, deterministic=False):
     if w.varlen:
         kw = dict(cu_seqlens_q=d["cu_seqlens_q"], cu_seqlens_k=d["cu_seqlens_k"], max_seqlen_q=w.seqlen_q,
                   max_seqlen_k=w.seqlen_k)
-    out, lse = fa.forward(d["q"], d["k"], d["v"], causal=w.causal, scale=w.softmax_scale, **kw)
+    mk = dict(window_size=w.window, alibi_slopes=d.get("alibi_slopes"))
+    out, lse = fa.forward(d["q"], d["k"], d["v"], causal=w.causal, scale=w.softmax_scale, **mk, **kw)
     if poison:
         dq = torch.full_like(d["q"], float("nan"))
         dk = torch.full_like(d["k"], float("nan"))
@@ -32,7 +33,8 @@ def run_fwd_bwd(w, x, poison=True, deterministic=False):
     ws = fa.workspace_for(d["q"], d.get("cu_seqlens_q"), w.seqlen_q if w.varlen else None)
     ws.fill_(0xFF)  # the workspace's contents on entry must not matter
     run = fa.fa_bwd_deterministic if deterministic else fa.fa_bwd
-    run(d["do"], d["q"], d["k"], d["v"], out, lse, dq, dk, dv, ws, causal=w.causal, scale=w.softmax_scale, **kw)
+    run(d["do"], d["q"], d["k"], d["v"], out, lse, dq, dk, dv, ws, causal=w.causal, scale=w.softmax_scale, **mk,
+        **kw)
     torch.cuda.synchronize()
     return out, lse, dq, dk, dv
 
@@ -41,8 +43,9 @@ def check_grads(w, x, dq, dk, dv, heads=None):
     kw = {}
     if w.varlen:
         kw = dict(cu_seqlens_q=x["cu_seqlens_q"].numpy(), cu_seqlens_k=x["cu_seqlens_k"].numpy())
+    slopes = x["alibi_slopes"].numpy() if "alibi_slopes" in x else None
     ref = orc.backward(f64(x["do"]), f64(x["q"]), f64(x["k"]), f64(x["v"]), scale=w.softmax_scale, causal=w.causal,
-                       threads=THREADS, heads=heads, **kw)
+                       threads=THREADS, heads=heads, window=w.window, alibi_slopes=slopes, **kw)
     got = [f64(t) for t in (dq, dk, dv)]
     for g, name in zip(got, ("dq", "dk", "dv")):
         assert np.isfinite(g).all(), f"{w.name}: non-finite {name} (unwritten or NaN)"
@@ -61,12 +64,14 @@ def check_grads(w, x, dq, dk, dv, heads=None):
     return errs
 
 
-def W(name, B, Hq, Hkv, Sq, Sk, D, dtype, causal, seed=0, lengths=None, scale=None):
+def W(name, B, Hq, Hkv, Sq, Sk, D, dtype, causal, seed=0, lengths=None, scale=None, window=(-1, -1), alibi=None):
     if lengths is not None:
         lq, lk = lengths
         return synth.Workload(name, len(lq), Hq, Hkv, max(max(lq), 1), max(max(lk), 1), D, dtype, causal,
-                              backward=True, lengths_q=list(lq), lengths_k=list(lk), seed=seed, scale=scale)
-    return synth.Workload(name, B, Hq, Hkv, Sq, Sk, D, dtype, causal, backward=True, seed=seed, scale=scale)
+                              backward=True, lengths_q=list(lq), lengths_k=list(lk), seed=seed, scale=scale,
+                              window=window, alibi=alibi)
+    return synth.Workload(name, B, Hq, Hkv, Sq, Sk, D, dtype, causal, backward=True, seed=seed, scale=scale,
+                          window=window, alibi=alibi)
 
 
 def _full(w, deterministic=False):
