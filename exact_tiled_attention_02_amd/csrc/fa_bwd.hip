@@ -367,7 +367,8 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Q1[QT];
   __shared__ __attribute__((aligned(16))) uint16_t dO0[QT];
   __shared__ __attribute__((aligned(16))) uint16_t dO1[QT];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[kK2BQ * SSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t dS0[kK2BQ * SSTR];  // dS, double-buffered by step
+  __shared__ __attribute__((aligned(16))) uint16_t dS1[kK2BQ * SSTR];
   __shared__ __attribute__((aligned(16))) float lse0[64];
   __shared__ __attribute__((aligned(16))) float lse1[64];
   __shared__ __attribute__((aligned(16))) float dsum0[64];
@@ -513,14 +514,15 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   }
   int ktr[2];
 #pragma unroll
-  for (int hi = 0; hi < 2; ++hi) ktr[hi] = Swz::elem(8 * lh + ((lane & 15) >> 2) + 4 * hi, wave * 32 + tr_col);
+  for (int hi = 0; hi < 2; ++hi) ktr[hi] = Swz::elem(8 * lh + ((lane & 15) >> 2) + 4 * hi, (wave % ND) * 32 + tr_col);
 
   wait_all_memory();
   __syncthreads();
 
   auto step = [&](int it, bool mask, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
                   const float* __restrict__ lse_c, const float* __restrict__ dsum_c, uint16_t* __restrict__ Qn,
-                  uint16_t* __restrict__ dOn, float* __restrict__ lse_n, float* __restrict__ dsum_n) {
+                  uint16_t* __restrict__ dOn, float* __restrict__ lse_n, float* __restrict__ dsum_n,
+                  uint16_t* __restrict__ dSc) {
     const int h = hk * G + it / nqs;
     const int i0 = (qb_begin + it % nqs) * kK2BQ;
     const float sl = sl_next;
@@ -586,8 +588,8 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
         const uint32_t two = dsf[t].v[w];
         const int r = 8 * t + 2 * w;
         const int rl0 = 8 * (r >> 2) + 4 * lh + (r & 3);
-        dSs[rl0 * SSTR + wave * 32 + li] = (uint16_t)(two & 0xffff);
-        dSs[(rl0 + 1) * SSTR + wave * 32 + li] = (uint16_t)(two >> 16);
+        dSc[rl0 * SSTR + wave * 32 + li] = (uint16_t)(two & 0xffff);
+        dSc[(rl0 + 1) * SSTR + wave * 32 + li] = (uint16_t)(two >> 16);
       }
     }
     if (live) {
@@ -610,45 +612,50 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
         }
       }
     }
-    if constexpr (DQ) lds_barrier();  // dS of all eight wavefronts is in LDS (atomics stay in flight)
-
-    // dQ[32 rows][d-block wave] = dS[32 rows][256 keys] K[256 keys][d-block].
-    bool sixteen = false;  // exactly 16 atomics issued after the prefetch
-    if (DQ && wave < ND) {
-      bool any = true;
-      if (mask) any = i0 < Lq && k0 <= kw.hi(min(i0 + kK2BQ, Lq) - 1) && k_last >= kw.lo(i0);
-      if (any) {
-        f32x16 dq = f32x16{};
+    if constexpr (DQ) {
+      // This wavefront's prefetch of the next step has landed (and the dQ atomics it issued
+      // before that prefetch have completed).  After the barrier every wavefront's dS is in
+      // dSc, nobody reads this step's Q / dO / LSE / Dsum tiles any more, and the next
+      // step's tiles are in LDS everywhere -- so no second barrier closes the step: the
+      // wavefronts that compute this step's dQ overlap with the others starting the next
+      // step, which writes its dS into the other buffer.
+      wait_vmcnt<0>();
+      lds_barrier();
+      // dQ[32 rows][d-block] = dS[32 rows][256 keys] K[256 keys][d-block]: groups of ND
+      // wavefronts take turns by step, one d-block per wavefront.
+      if (wave / ND == it % (kK2Waves / ND)) {
+        const int dblk = wave % ND;
+        bool any = true;
+        if (mask) any = i0 < Lq && k0 <= kw.hi(min(i0 + kK2BQ, Lq) - 1) && k_last >= kw.lo(i0);
+        if (any) {
+          f32x16 dq = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < kK2Keys / 16; ++ks) {
-          Frag8 sa, kb2;
-          sa.v = load16(&dSs[li * SSTR + ks * 16 + lh * 8]);
-          const u32x2 lo = lds_read_tr16(Ks + ks * 16 * D + ktr[0]);
-          const u32x2 hi = lds_read_tr16(Ks + ks * 16 * D + ktr[1]);
-          kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
-          dq = mfma32x32x16<BF16>(sa, kb2, dq);
-        }
-        float* dst = a.dq_acc + ((size_t)(q_start + i0 + 4 * lh) * a.Hq + h) * D + wave * 32 + li;
-        const size_t rstride = (size_t)a.Hq * D;
-        if (__builtin_expect(i0 + kK2BQ <= Lq, 1)) {
+          for (int ks = 0; ks < kK2Keys / 16; ++ks) {
+            Frag8 sa, kb2;
+            sa.v = load16(&dSc[li * SSTR + ks * 16 + lh * 8]);
+            const u32x2 lo = lds_read_tr16(Ks + ks * 16 * D + ktr[0]);
+            const u32x2 hi = lds_read_tr16(Ks + ks * 16 * D + ktr[1]);
+            kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+            dq = mfma32x32x16<BF16>(sa, kb2, dq);
+          }
+          float* dst = a.dq_acc + ((size_t)(q_start + i0 + 4 * lh) * a.Hq + h) * D + dblk * 32 + li;
+          const size_t rstride = (size_t)a.Hq * D;
+          if (__builtin_expect(i0 + kK2BQ <= Lq, 1)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * rstride, dq[r]);
-          sixteen = true;
-        } else {
+            for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * rstride, dq[r]);
+          } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = 8 * (r >> 2) + (r & 3);
-            if (i0 + 4 * lh + rr < Lq) unsafeAtomicAdd(dst + rr * rstride, dq[r]);
+            for (int r = 0; r < 16; ++r) {
+              const int rr = 8 * (r >> 2) + (r & 3);
+              if (i0 + 4 * lh + rr < Lq) unsafeAtomicAdd(dst + rr * rstride, dq[r]);
+            }
           }
         }
       }
-    }
-    if (sixteen) {
-      wait_vmcnt<16>();
     } else {
-      wait_vmcnt<0>();
+      wait_vmcnt<0>();  // the prefetched step has landed
+      lds_barrier();    // everywhere, and every wavefront is done with this step's tiles
     }
-    lds_barrier();
   };
 
   auto needs_mask = [&](int it) {
@@ -660,7 +667,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   for (int it = 0; it < nsteps; ++it) {
     const bool odd = it & 1;
     step(it, needs_mask(it), odd ? Q1 : Q0, odd ? dO1 : dO0, odd ? lse1 : lse0, odd ? dsum1 : dsum0,
-         odd ? Q0 : Q1, odd ? dO0 : dO1, odd ? lse0 : lse1, odd ? dsum0 : dsum1);
+         odd ? Q0 : Q1, odd ? dO0 : dO1, odd ? lse0 : lse1, odd ? dsum0 : dsum1, odd ? dS1 : dS0);
   }
 
   if (key_ok) {
