@@ -175,9 +175,9 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       const int chunk = first + lane;
       const int r = chunk / Swz::CH;
       const int p = chunk % Swz::CH;
-      const size_t src = (size_t)min(i0 + r, Lq - 1) * q_rs + Swz::chunk(r, p) * 8;
-      lds_direct_load16(qp + src, &Qs[buf][first * 8]);
-      lds_direct_load16(dop + src, &dOs[buf][first * 8]);
+      const uint32_t src = (uint32_t)(min(r, Lq - 1 - i0) * (int)q_rs + Swz::chunk(r, p) * 8) * 2u;
+      lds_direct_load16(qp + (size_t)i0 * q_rs, src, &Qs[buf][first * 8]);
+      lds_direct_load16(dop + (size_t)i0 * q_rs, src, &dOs[buf][first * 8]);
     }
     const int row = min(i0 + (lane & 31), Lq - 1);
     if (wave == 0) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, &lse_s[buf][0]);
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   const int qchunk = wave * 64 + lane;
   const bool qloader = wave * 64 < QCH;  // uniform per wavefront
   const int qr = qchunk / Swz::CH;
-  const int qoff = qr * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8;
+  const uint32_t qoff = (uint32_t)(qr * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8) * 2u;  // bytes
   auto fetch = [&](int it, uint16_t* __restrict__ Qd, uint16_t* __restrict__ dOd, float* __restrict__ lsed,
                    float* __restrict__ dsumd) {
     const int h = hk * G + it / nqs;
@@ -454,10 +454,11 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
     const uint16_t* qt = (const uint16_t*)a.q + base;
     const uint16_t* dot = (const uint16_t*)a.dout + base;
     if (qloader) {
-      int off = qoff;
-      if (i0 + kK2BQ > Lq) off = min(qr, Lq - 1 - i0) * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8;
-      lds_direct_load16(qt + off, Qd + wave * 64 * 8);
-      lds_direct_load16(dot + off, dOd + wave * 64 * 8);
+      uint32_t off = qoff;
+      if (i0 + kK2BQ > Lq)
+        off = (uint32_t)(min(qr, Lq - 1 - i0) * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8) * 2u;
+      lds_direct_load16(qt, off, Qd + wave * 64 * 8);
+      lds_direct_load16(dot, off, dOd + wave * 64 * 8);
     }
     const int row = min(i0 + (lane & 31), Lq - 1);
     if (wave == kK2Waves - 1) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, lsed);
@@ -767,12 +768,12 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
   const int my_lo = kw.lo(my_row), my_hi = kw.hi(my_row);
 
   constexpr int NI = TILE / 8 / 256;
-  int foff[NI];
+  uint32_t foff[NI];  // bytes
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int chunk = (i * kDqWaves + wave) * 64 + lane;
     const int r = chunk / Swz::CH;
-    foff[i] = r * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
+    foff[i] = (uint32_t)(r * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
   }
   auto fetch = [&](int kb, uint16_t* __restrict__ Kd, uint16_t* __restrict__ Vd) {
     const int k0 = kb * kDqBN;
@@ -781,14 +782,14 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int first = (i * kDqWaves + wave) * 64;
-      int off = foff[i];
+      uint32_t off = foff[i];
       if (k0 + kDqBN > Lk) {
         const int chunk = first + lane;
         const int r = chunk / Swz::CH;
-        off = min(r, Lk - 1 - k0) * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
+        off = (uint32_t)(min(r, Lk - 1 - k0) * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
       }
-      lds_direct_load16(kt + off, Kd + first * 8);
-      lds_direct_load16(vt + off, Vd + first * 8);
+      lds_direct_load16(kt, off, Kd + first * 8);
+      lds_direct_load16(vt, off, Vd + first * 8);
     }
   };
   if (kb_begin < kb_end) fetch(kb_begin, K0, V0);

@@ -168,12 +168,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 
   // Per-lane source offsets of the direct loads within a tile (LDS chunk c of row rr
   // receives the global chunk c ^ f(rr)).
-  int foff[NI];
+  uint32_t foff[NI];  // bytes
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int chunk = i * 64 + lane;
     const int rr = chunk / CH;
-    foff[i] = rr * (int)rs + Swz::chunk(rr, chunk % CH) * 8;
+    foff[i] = (uint32_t)(rr * (int)rs + Swz::chunk(rr, chunk % CH) * 8) * 2u;
   }
 
   // Issue the loads of tile t into ring slot k.  Tiles are issued in increasing order,
@@ -200,8 +200,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     if (k0 + kDecKeys <= Lk) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        lds_direct_load16(kt + foff[i], dst + i * 512);
-        lds_direct_load16(vt + foff[i], dst + TILE + i * 512);
+        lds_direct_load16(kt, foff[i], dst + i * 512);
+        lds_direct_load16(vt, foff[i], dst + TILE + i * 512);
       }
     } else {
       // Rows past the last key re-read the last key (finite data, masked to P = 0); they
@@ -210,9 +210,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       for (int i = 0; i < NI; ++i) {
         const int chunk = i * 64 + lane;
         const int rr = chunk / CH;
-        const int off = min(rr, Lk - 1 - k0) * (int)rs + Swz::chunk(rr, chunk % CH) * 8;
-        lds_direct_load16(kt + off, dst + i * 512);
-        lds_direct_load16(vt + off, dst + TILE + i * 512);
+        const uint32_t off = (uint32_t)(min(rr, Lk - 1 - k0) * (int)rs + Swz::chunk(rr, chunk % CH) * 8) * 2u;
+        lds_direct_load16(kt, off, dst + i * 512);
+        lds_direct_load16(vt, off, dst + TILE + i * 512);
       }
     }
   };

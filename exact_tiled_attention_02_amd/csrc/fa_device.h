@@ -78,6 +78,13 @@ __device__ __forceinline__ void lds_direct_load16(const void* gptr, void* lds_ba
   __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_base, 16, 0, 0);
 }
 
+// The same load from a wavefront-uniform base plus an unsigned 32-bit per-lane byte
+// offset: this is the instruction's scalar-base form, so no per-lane 64-bit address has to
+// be formed.
+__device__ __forceinline__ void lds_direct_load16(const void* base, uint32_t byte_off, void* lds_base) {
+  lds_direct_load16((const char*)base + byte_off, lds_base);
+}
+
 // 4 bytes per lane straight into LDS (global_load_lds_dword): lane l writes lds_base + 4*l.
 __device__ __forceinline__ void lds_direct_load4(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_base, 4, 0, 0);

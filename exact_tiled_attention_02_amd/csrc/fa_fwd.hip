@@ -124,12 +124,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   // sequence needs its rows clamped (they re-read the last row: finite data, masked to
   // P = 0).
   constexpr int NI = TILE / 8 / 256;  // direct loads per wavefront per tensor
-  int foff[NI];
+  uint32_t foff[NI];  // bytes
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int chunk = (i * kFwdWaves + wave) * 64 + lane;
     const int r = chunk / Swz::CH;
-    foff[i] = r * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
+    foff[i] = (uint32_t)(r * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
   }
   auto fetch = [&](int kb, auto buf_tag) {
     uint16_t* Kd = decltype(buf_tag)::value ? K1 : K0;
@@ -141,8 +141,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int first = (i * kFwdWaves + wave) * 64;
-        lds_direct_load16(kt + foff[i], Kd + first * 8);
-        lds_direct_load16(vt + foff[i], Vd + first * 8);
+        lds_direct_load16(kt, foff[i], Kd + first * 8);
+        lds_direct_load16(vt, foff[i], Vd + first * 8);
       }
     } else {
 #pragma unroll
@@ -150,9 +150,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const int first = (i * kFwdWaves + wave) * 64;
         const int chunk = first + lane;
         const int r = chunk / Swz::CH;
-        const int off = min(r, Lk - 1 - k0) * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8;
-        lds_direct_load16(kt + off, Kd + first * 8);
-        lds_direct_load16(vt + off, Vd + first * 8);
+        const uint32_t off = (uint32_t)(min(r, Lk - 1 - k0) * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
+        lds_direct_load16(kt, off, Kd + first * 8);
+        lds_direct_load16(vt, off, Vd + first * 8);
       }
     }
   };
