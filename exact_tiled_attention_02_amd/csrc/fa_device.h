@@ -85,6 +85,22 @@ __device__ __forceinline__ void lds_direct_load16(const void* base, uint32_t byt
   lds_direct_load16((const char*)base + byte_off, lds_base);
 }
 
+// Buffer resource for raw (unstructured) buffer loads over [base, base + bytes): offsets
+// at or past `bytes` read as zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset byte_off + uniform_off straight into LDS
+// (buffer_load_dwordx4 with the lds bit; uniform_off goes in the scalar offset and is
+// not range-checked): lane l writes lds_base + 16*l.  Unlike the flat-encoded global form, this
+// load does not count against the LDS wait counter, so later LDS reads can still be
+// waited for one by one.
+__device__ __forceinline__ void lds_buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, void* lds_base,
+                                                  uint32_t uniform_off = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds_base, 16, byte_off, (int)uniform_off, 0, 0);
+}
+
 // 4 bytes per lane straight into LDS (global_load_lds_dword): lane l writes lds_base + 4*l.
 __device__ __forceinline__ void lds_direct_load4(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_base, 4, 0, 0);

@@ -370,8 +370,493 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Ping-pong forward kernel (D <= 128).
+//
+// Same arithmetic as fwd_kernel, scheduled so that the matrix pipe stays busy.  On a CDNA4
+// SIMD one wavefront issues a VALU instruction only every ~6 cycles while a 32x32x16 MFMA
+// holds the matrix pipe for 32 cycles; two wavefronts that run their softmax at the same
+// time (and then their products at the same time) leave the pipe idle for about half of
+// the loop.  Here a workgroup of 8 wavefronts (256 query rows, 32 per wavefront) splits
+// into two groups with one wavefront of each on every SIMD, and workgroup barriers cut the
+// loop into phases:
+//   M phase of tile j: S^T(j) = K(j) Q^T and O^T += V(j-1)^T P^T(j-1)   (MFMA and LDS reads)
+//   X phase of tile j: masking, running max and sum, P(j) = exp2(...), rescale of O
+// Group 1 runs one phase behind group 0, so on every SIMD one wavefront multiplies while
+// the other runs its softmax.  Both groups execute the same instruction stream (group 1
+// only starts one barrier later), which keeps the register allocation that of one path.
+//
+// Tiles move through LDS in stages: stage s holds K of tile s and V of tile s-1 in
+// processing order, in buffer s % 3.  Every wavefront issues its share of stage j+2 among
+// the VALU work of X(j) and waits for it at the end of M(j+1), just before the barrier
+// after which stage j+2 may be read.  The query rows live in LDS too (each wavefront its
+// own 32 rows, read with the same offsets as a K tile), which leaves the registers to the
+// accumulators and to operand reads issued a few products ahead.
+constexpr int kPPWaves = 8;
+constexpr int kPPBM = 32 * kPPWaves;  // query rows per workgroup
+constexpr int kPPBN = 64;             // keys per tile
+
+// Register values that must be complete where the call stands: an empty asm statement
+// that reads and rewrites them, so that the compiler cannot sink their computation past a
+// phase barrier.
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(u32x4& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+// Workgroup barrier that also fences the instruction scheduler, so that no product or
+// softmax instruction migrates into the neighbouring phase.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int I>
+using Idx = std::integral_constant<int, I>;
+
+template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(FwdArgs a) {
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int TILE = kPPBN * D;
+  using Swz = DualSwizzle<D>;
+  // Stage buffers as distinct LDS objects, always addressed statically, so that the
+  // compiler can tell operand reads from the direct loads in flight into other buffers.
+  __shared__ __attribute__((aligned(16))) uint16_t K0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t K2[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V2[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kPPWaves * 32 * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // waves w and w + 4 share a SIMD
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+
+  const int nqb = (a.Sq + kPPBM - 1) / kPPBM;
+  const int nbh = a.B * a.Hq;
+  const int lin = blockIdx.x;
+  const int qb = nqb - 1 - lin / nbh;
+  const int bh = lin % nbh;
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+
+  int q_start, k_start, Lq, Lk;
+  if constexpr (VARLEN) {
+    q_start = a.cu_q[b];
+    Lq = a.cu_q[b + 1] - q_start;
+    k_start = a.cu_k[b];
+    Lk = a.cu_k[b + 1] - k_start;
+  } else {
+    q_start = b * a.Sq;
+    Lq = a.Sq;
+    k_start = b * a.Sk;
+    Lk = a.Sk;
+  }
+  const int q0 = qb * kPPBM;
+  if (q0 >= Lq) return;  // uniform over the workgroup
+
+  const int hk = h / (a.Hq / a.Hkv);
+  const size_t q_rs = (size_t)a.Hq * D;
+  const size_t k_rs = (size_t)a.Hkv * D;
+  const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+
+  const int diag = Lk - Lq;
+  KeyWindow kw{Lk, diag, 0, -1, -1};
+  if constexpr (MASKED) kw = KeyWindow{Lk, diag, a.causal, a.window_left, a.window_right};
+  const int last_row = min(q0 + kPPBM, Lq) - 1;
+  const int k_lo = kw.lo(q0), k_hi = kw.hi(last_row);
+  const int kb_begin = k_lo / kPPBN;
+  const int kb_end = k_hi >= k_lo ? k_hi / kPPBN + 1 : kb_begin;
+  const int all_lo = kw.lo(last_row), all_hi = kw.hi(q0);
+
+  const int my_row = q0 + wave * 32 + li;
+  const bool row_ok = my_row < Lq;
+  const int wave_row0 = q0 + wave * 32;
+  const int wave_lo = kw.lo(wave_row0), wave_hi = kw.hi(min(wave_row0 + 31, Lq - 1));
+  const int my_lo = kw.lo(my_row), my_hi = kw.hi(my_row);
+
+  // Processing order: the run of tiles every row keeps in full (a multiple of three
+  // long, so that the three stage buffers repeat with the loop), then the edge tiles
+  // (before the run: window; after it: diagonal, tail).
+  const int u0 = min(max(kb_begin, (all_lo + kPPBN - 1) / kPPBN), kb_end);
+  int u1 = all_hi >= 0 ? min(kb_end, (all_hi + 1) / kPPBN) : 0;
+  u1 = u1 > u0 ? u0 + (u1 - u0) / 3 * 3 : u0;
+  const int n_un = u1 - u0;
+  const int n_lead = u0 - kb_begin;
+  const int n = n_un + n_lead + (kb_end - u1);
+  auto kbj = [&](int j) __attribute__((always_inline)) {
+    const int i = j - n_un;
+    const int edge = i < n_lead ? kb_begin + i : u1 + (i - n_lead);
+    return j < n_un ? u0 + j : edge;
+  };
+
+  // This wavefront's share of stage st (NI 16-byte chunks per lane of each tile).
+  // Indexes past either end repeat a valid tile (the buffer it lands in is free and is
+  // not read), so the loads carry no branch and can be scheduled among other work; rows
+  // past the end of the sequence re-read the last row (finite data, masked to P = 0).
+  constexpr int NI = TILE / 8 / (64 * kPPWaves);
+  static_assert(NI >= 1 && (TILE / 8) % (64 * kPPWaves) == 0, "whole chunks per lane");
+  // One buffer resource per tensor over this sequence and head (K/V rows of a sequence
+  // span less than 4 GiB, which the host checks); a tile's first row goes in the scalar
+  // offset, the row and column within the tile in the lane offset.
+  const uint32_t krs2 = (uint32_t)k_rs * 2u;
+  const size_t kv_first = (size_t)k_start * k_rs + (size_t)hk * D;
+  const size_t kv_rest = ((size_t)(VARLEN ? a.cu_k[a.B] : a.B * a.Sk) * k_rs - kv_first) * 2u;
+  const uint32_t kv_bytes = (uint32_t)(kv_rest < 0xffffffffu ? kv_rest : 0xffffffffu);
+  const auto kr = make_rsrc(kp, kv_bytes);
+  const auto vr = make_rsrc(vp, kv_bytes);
+  // Row and swizzled column (bytes) of this lane's chunks within a tile.
+  int lrow[NI];
+  uint32_t lcol[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int chunk = (i * kPPWaves + wave) * 64 + lane;
+    lrow[i] = chunk / Swz::CH;
+    lcol[i] = (uint32_t)(Swz::chunk(lrow[i], chunk % Swz::CH) * 16);
+  }
+  // First keys of the K and V tiles of stage st (wavefront-uniform), computed before the
+  // M phase that precedes the X phase issuing the loads.
+  struct StageSrc {
+    int kk0, vk0;
+  };
+  auto stage_src = [&](int st) __attribute__((always_inline)) {
+    // readfirstlane: keep them in scalar registers (the scalar offset of a buffer load).
+    return StageSrc{__builtin_amdgcn_readfirstlane(kbj(min(st, n - 1)) * kPPBN),
+                    __builtin_amdgcn_readfirstlane(kbj(max(min(st - 1, n - 1), 0)) * kPPBN)};
+  };
+  auto load_stage = [&](StageSrc src, uint16_t* Kd, uint16_t* Vd) __attribute__((always_inline)) {
+    const int klim = Lk - 1 - src.kk0, vlim = Lk - 1 - src.vk0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      // row * row_bytes + column in one 24-bit multiply-add (rows < 64; the host keeps
+      // row_bytes below 2^24).
+      lds_buffer_load16(kr, __umul24((uint32_t)min(lrow[i], klim), krs2) + lcol[i],
+                        Kd + (i * kPPWaves + wave) * 64 * 8, (uint32_t)src.kk0 * krs2);
+      lds_buffer_load16(vr, __umul24((uint32_t)min(lrow[i], vlim), krs2) + lcol[i],
+                        Vd + (i * kPPWaves + wave) * 64 * 8, (uint32_t)src.vk0 * krs2);
+    }
+  };
+  auto kbuf = [&](auto bi) __attribute__((always_inline)) {
+    constexpr int I = decltype(bi)::value % 3;
+    return I == 0 ? K0 : (I == 1 ? K1 : K2);
+  };
+  auto vbuf = [&](auto bi) __attribute__((always_inline)) {
+    constexpr int I = decltype(bi)::value % 3;
+    return I == 0 ? V0 : (I == 1 ? V1 : V2);
+  };
+
+  // Q rows of this wavefront into its LDS region (rows past the end of the sequence
+  // re-read the last row; their results are not stored), then stages 0 and 1.
+  // A wavefront can lie wholly past the end (q0 < Lq <= wave_row0): rows are clamped as
+  // absolute indexes and addressed from a clamped base row, so every offset is >= 0.
+  uint16_t* Qw = Qs + wave * 32 * D;
+  {
+    const int base_row = min(wave_row0, Lq - 1);
+    const size_t qfirst = (size_t)(q_start + base_row) * q_rs + (size_t)h * D;
+    const size_t qrest = ((size_t)(VARLEN ? a.cu_q[a.B] : a.B * a.Sq) * q_rs - qfirst) * 2u;
+    const auto qr = make_rsrc((const uint16_t*)a.q + qfirst, (uint32_t)(qrest < 0xffffffffu ? qrest : 0xffffffffu));
+#pragma unroll
+    for (int i = 0; i < 32 * D / 8 / 64; ++i) {
+      const int chunk = i * 64 + lane;
+      const int r = chunk / Swz::CH;
+      const int row = min(wave_row0 + r, Lq - 1) - base_row;
+      const uint32_t off = (uint32_t)(row * (int)q_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
+      lds_buffer_load16(qr, off, Qw + i * 64 * 8);
+    }
+  }
+  if (n > 0) {
+    load_stage(stage_src(0), K0, V0);
+    load_stage(stage_src(1), K1, V1);
+  }
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float c = a.scale_log2;
+  constexpr float kLog2e = 1.4426950408889634f;
+  float sl2 = 0.f;
+  if constexpr (ALIBI) sl2 = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
+  const int row_diag = my_row + diag;
+
+  const int tr_row = 4 * lh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int koff[NS], voff[2][ND];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) koff[st] = Swz::row_elem(li, st * 2 + lh);
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int d = 0; d < ND; ++d) voff[hi][d] = Swz::elem(tr_row + 8 * hi, d * 32 + tr_col);
+
+  f32x16 s[2];           // S^T of the current tile: M phase -> X phase
+  Frag8 pf[4];           // P^T of the previous tile: X phase -> next M phase
+  bool pv_live = false;  // pf holds probabilities to add
+
+  // M phase on stage buffer BI: S^T(j) (when the tile is live for this wavefront) and the
+  // P V product of the previous tile.  Alone on the matrix pipe, the wavefront has to hide
+  // its own LDS latency: the scheduling groups issue the operand reads a few products
+  // ahead.
+  auto s_part = [&](const uint16_t* K) __attribute__((always_inline)) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      Frag8 qf;
+      qf.v = load16(Qw + koff[st]);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        Frag8 kf;
+        kf.v = load16(K + sub * 32 * D + koff[st]);
+        s[sub] = mfma32x32x16<BF16>(kf, qf, s[sub]);
+      }
+    }
+  };
+  auto pv_part = [&](const uint16_t* V) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        const u32x2 lo = lds_read_tr16(V + t * 16 * D + voff[0][d]);
+        const u32x2 hi = lds_read_tr16(V + t * 16 * D + voff[1][d]);
+        Frag8 vf;
+        vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+        acc[d] = mfma32x32x16<BF16>(vf, pf[t], acc[d]);
+      }
+    }
+  };
+  // Operand reads spread over NM products: R0 issued ahead, the rest evenly over all
+  // but the last two products.
+  auto read_schedule = [&](auto nm_tag, auto nr_tag, auto id_tag) __attribute__((always_inline)) {
+    constexpr int NM = decltype(nm_tag)::value, NR = decltype(nr_tag)::value, ID = decltype(id_tag)::value;
+    constexpr int R0 = NR < 8 ? NR : 8, RR = NR - R0, SL = NM - 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, R0, ID);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);
+      const int cnt = i < SL ? (i + 1) * RR / SL - i * RR / SL : 0;
+#pragma unroll
+      for (int k = 0; k < cnt; ++k) __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);
+    }
+  };
+
+  // M phase on stage buffer BI: S^T(j) (when the tile is live for this wavefront) and the
+  // P V product of the previous tile.  Alone on the matrix pipe, the wavefront has to hide
+  // its own LDS latency, so the operand reads are issued several products ahead; when
+  // both products are certain (FUSED: interior tiles after the first) they form one block
+  // and share one read schedule.
+  auto mphase = [&](bool s_live, auto bi, auto fused_tag) __attribute__((always_inline)) {
+    constexpr bool FUSED = decltype(fused_tag)::value;
+    const uint16_t* K = kbuf(bi);
+    const uint16_t* V = vbuf(bi);
+    if constexpr (FUSED) {
+      s_part(K);
+      pv_part(V);
+      read_schedule(Idx<2 * NS + 4 * ND>{}, Idx<3 * NS + 8 * ND>{}, Idx<0>{});
+    } else {
+      if (s_live) {
+        s_part(K);
+        read_schedule(Idx<2 * NS>{}, Idx<3 * NS>{}, Idx<0>{});
+      }
+      if (pv_live) {
+        pv_part(V);
+        read_schedule(Idx<4 * ND>{}, Idx<8 * ND>{}, Idx<1>{});
+      }
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) pin(s[sub]);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) pin(acc[d]);
+  };
+
+  // X phase of the tile at key k0; first issues this wavefront's share of stage st_next
+  // into buffer BI, spread among the softmax arithmetic.
+  auto xphase = [&](int k0, bool live, auto mask_tag, StageSrc next, auto bi) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    load_stage(next, kbuf(bi), vbuf(bi));
+    pv_live = live;
+    if (!live) return;
+    if constexpr (ALIBI) {
+      const float base = (float)(k0 + 4 * lh - row_diag);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float dist = base + (float)(sub * 32 + 8 * (r >> 2) + (r & 3));
+          s[sub][r] = fmaf(-sl2, fabsf(dist), s[sub][r] * c);
+        }
+    }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + sub * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+          s[sub][r] = (key >= my_lo && key <= my_hi) ? s[sub][r] : -INFINITY;
+        }
+    }
+    float mx = m_run;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+    mx = pair_max(mx);
+    const float m_use = (mx == -INFINITY) ? 0.f : mx;
+    float alpha;
+    float ls = 0.f;
+    if constexpr (ALIBI) {
+      alpha = fast_exp2(m_run - m_use);
+      m_run = mx;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(s[sub][r] - m_use);
+          s[sub][r] = p;
+          ls += p;
+        }
+    } else {
+      alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
+      m_run = mx;
+      const float mc = m_use * c;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[sub][r], c, -mc));
+          s[sub][r] = p;
+          ls += p;
+        }
+    }
+    if constexpr (!MASK) {
+      // Spread the direct loads over the softmax arithmetic.
+#pragma unroll
+      for (int i = 0; i < 2 * NI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x002, 20, 2);
+      }
+    }
+    l_run = l_run * alpha + ls;
+    if (__builtin_expect(__any(alpha != 1.f), 0)) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int sub = t >> 1, r0 = (t & 1) * 8;
+      pf[t].v = u32x4{pack2<BF16>(s[sub][r0 + 0], s[sub][r0 + 1]), pack2<BF16>(s[sub][r0 + 2], s[sub][r0 + 3]),
+                      pack2<BF16>(s[sub][r0 + 4], s[sub][r0 + 5]), pack2<BF16>(s[sub][r0 + 6], s[sub][r0 + 7])};
+      pin(pf[t].v);
+    }
+#pragma unroll
+    for (int d = 0; d < ND; ++d) pin(acc[d]);
+    pin(m_run);
+    pin(l_run);
+  };
+
+  // Tile j of the processing order, stage buffer BI = j % 3.  The wait at the end of the
+  // M phase covers the stage this wavefront issued in the previous X phase.
+  auto step = [&](int j, auto mask_tag, auto bi, auto fused_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int BI = decltype(bi)::value;
+    const int k0 = kbj(j) * kPPBN;
+    const bool live = !MASK || !(k0 > wave_hi || k0 + kPPBN - 1 < wave_lo);
+    const StageSrc next = stage_src(j + 2);
+    mphase(live, bi, fused_tag);
+    wait_vmcnt<0>();
+    phase_barrier();
+    xphase(k0, live, mask_tag, next, Idx<BI + 2>{});
+    phase_barrier();
+  };
+
+  wait_all_memory();
+  __syncthreads();
+  if (grp == 1) phase_barrier();
+  using F = std::false_type;
+  using T = std::true_type;
+  // Interior tiles; the first one has no previous tile to add.
+  if (n_un > 0) {
+    step(0, F{}, Idx<0>{}, F{});
+    step(1, F{}, Idx<1>{}, T{});
+    step(2, F{}, Idx<2>{}, T{});
+  }
+  for (int j = 3; j < n_un; j += 3) {
+    step(j, F{}, Idx<0>{}, T{});
+    step(j + 1, F{}, Idx<1>{}, T{});
+    step(j + 2, F{}, Idx<2>{}, T{});
+  }
+  // Edge tiles.
+  int j = n_un;
+  for (; j + 3 <= n; j += 3) {
+    step(j, T{}, Idx<0>{}, F{});
+    step(j + 1, T{}, Idx<1>{}, F{});
+    step(j + 2, T{}, Idx<2>{}, F{});
+  }
+  if (j < n) step(j, T{}, Idx<0>{}, F{});
+  if (j + 1 < n) step(j + 1, T{}, Idx<1>{}, F{});
+  // Last M phase: the P V product of the last tile (stage n, buffer n % 3).
+  const int nb = n % 3;
+  if (nb == 0) {
+    mphase(false, Idx<0>{}, F{});
+  } else if (nb == 1) {
+    mphase(false, Idx<1>{}, F{});
+  } else {
+    mphase(false, Idx<2>{}, F{});
+  }
+  wait_vmcnt<0>();  // the last X phase's loads (repeats of valid tiles) have landed
+  if (grp == 0) phase_barrier();
+
+  const float l_tot = pair_sum(l_run);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = d * 32 + 8 * g + 4 * lh;
+        u32x2 w;
+        w.x = pack2<BF16>(acc[d][4 * g + 0] * inv, acc[d][4 * g + 1] * inv);
+        w.y = pack2<BF16>(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv);
+        *(u32x2*)(op + col) = w;
+      }
+    }
+    if (lh == 0) {
+      float lse = INFINITY;
+      if (l_tot > 0.f) lse = (ALIBI ? m_run * 0.69314718055994531f : m_run * a.scale) + __logf(l_tot);
+      size_t idx;
+      if constexpr (VARLEN) {
+        idx = (size_t)h * a.cu_q[a.B] + q_start + my_row;
+      } else {
+        idx = ((size_t)b * a.Hq + h) * a.Sq + my_row;
+      }
+      a.lse[idx] = lse;
+    }
+  }
+}
+
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  if constexpr (D <= 128) {
+    // The ping-pong kernel addresses a sequence's K/V rows with 32-bit byte offsets and a
+    // K/V row stride below 2^24 bytes.
+    const bool offsets_fit =
+        (uint64_t)a.Sk * a.Hkv * D * 2u < (1ull << 32) - (1ull << 20) && (uint64_t)a.Hkv * D * 2u < (1ull << 24);
+    if (a.Sq > kFwdBM && offsets_fit) {
+      const int nqb = (a.Sq + kPPBM - 1) / kPPBM;
+      const dim3 grid((unsigned)nqb * a.B * a.Hq);
+      hipLaunchKernelGGL((fwd_pp_kernel<D, BF16, MASKED, VARLEN, ALIBI>), grid, dim3(512), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   const int nqb = (a.Sq + kFwdBM - 1) / kFwdBM;
   const dim3 grid((unsigned)nqb * a.B * a.Hq);
   hipLaunchKernelGGL((fwd_kernel<D, BF16, MASKED, VARLEN, ALIBI>), grid, dim3(256), 0, stream, a);
