@@ -446,10 +446,10 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   const bool qloader = wave * 64 < QCH;  // uniform per wavefront
   const int qr = qchunk / Swz::CH;
   const uint32_t qoff = (uint32_t)(qr * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8) * 2u;  // bytes
-  auto fetch = [&](int it, uint16_t* __restrict__ Qd, uint16_t* __restrict__ dOd, float* __restrict__ lsed,
+  // Steps walk (query head of the group, query block) with the block fastest; the
+  // position is carried as counters (no division by the runtime block count).
+  auto fetch = [&](int h, int i0, uint16_t* __restrict__ Qd, uint16_t* __restrict__ dOd, float* __restrict__ lsed,
                    float* __restrict__ dsumd) {
-    const int h = hk * G + it / nqs;
-    const int i0 = (qb_begin + it % nqs) * kK2BQ;
     const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * D;
     const uint16_t* qt = (const uint16_t*)a.q + base;
     const uint16_t* dot = (const uint16_t*)a.dout + base;
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
     if constexpr (ALIBI) sl_next = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
   };
 
-  if (nsteps > 0) fetch(0, Q0, dO0, lse0, dsum0);
+  if (nsteps > 0) fetch(hk * G, qb_begin * kK2BQ, Q0, dO0, lse0, dsum0);
 #pragma unroll
   for (int i = 0; i < kK2Keys * D / 8 / 512; ++i) {
     const int first = (i * kK2Waves + wave) * 64;
@@ -520,14 +520,12 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   wait_all_memory();
   __syncthreads();
 
-  auto step = [&](int it, bool mask, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
-                  const float* __restrict__ lse_c, const float* __restrict__ dsum_c, uint16_t* __restrict__ Qn,
-                  uint16_t* __restrict__ dOn, float* __restrict__ lse_n, float* __restrict__ dsum_n,
-                  uint16_t* __restrict__ dSc) {
-    const int h = hk * G + it / nqs;
-    const int i0 = (qb_begin + it % nqs) * kK2BQ;
+  auto step = [&](int it, int h, int i0, int h_next, int i0_next, bool mask, const uint16_t* __restrict__ Q,
+                  const uint16_t* __restrict__ dO, const float* __restrict__ lse_c, const float* __restrict__ dsum_c,
+                  uint16_t* __restrict__ Qn, uint16_t* __restrict__ dOn, float* __restrict__ lse_n,
+                  float* __restrict__ dsum_n, uint16_t* __restrict__ dSc) {
     const float sl = sl_next;
-    if (it + 1 < nsteps) fetch(it + 1, Qn, dOn, lse_n, dsum_n);
+    if (it + 1 < nsteps) fetch(h_next, i0_next, Qn, dOn, lse_n, dsum_n);
 
     bool live = true;  // some key of this wavefront is kept by some row of the step
     if constexpr (MASKED) {
@@ -659,16 +657,28 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
     }
   };
 
-  auto needs_mask = [&](int it) {
-    const int i0 = (qb_begin + it % nqs) * kK2BQ;
+  auto needs_mask = [&](int i0) {
     bool full = i0 + kK2BQ <= Lq && k0 + kK2Keys <= Lk;
     if constexpr (MASKED) full = full && kw.lo(i0 + kK2BQ - 1) <= k0 && kw.hi(i0) >= k0 + kK2Keys - 1;
     return !full;
   };
+  int h_c = hk * G, q_c = qb_begin;  // this step's query head and block
+  int h_n = h_c, q_n = q_c + 1;      // the next step's
+  if (q_n == qb_end) {
+    q_n = qb_begin;
+    ++h_n;
+  }
   for (int it = 0; it < nsteps; ++it) {
     const bool odd = it & 1;
-    step(it, needs_mask(it), odd ? Q1 : Q0, odd ? dO1 : dO0, odd ? lse1 : lse0, odd ? dsum1 : dsum0,
-         odd ? Q0 : Q1, odd ? dO0 : dO1, odd ? lse0 : lse1, odd ? dsum0 : dsum1, odd ? dS1 : dS0);
+    step(it, h_c, q_c * kK2BQ, h_n, q_n * kK2BQ, needs_mask(q_c * kK2BQ), odd ? Q1 : Q0, odd ? dO1 : dO0,
+         odd ? lse1 : lse0, odd ? dsum1 : dsum0, odd ? Q0 : Q1, odd ? dO0 : dO1, odd ? lse0 : lse1,
+         odd ? dsum0 : dsum1, odd ? dS1 : dS0);
+    h_c = h_n;
+    q_c = q_n;
+    if (++q_n == qb_end) {
+      q_n = qb_begin;
+      ++h_n;
+    }
   }
 
   if (key_ok) {
