@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -127,6 +129,24 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4));  // lgkmcnt(0)
   asm volatile("s_barrier" ::: "memory");
 }
+
+// Register values that must be complete where the call stands: an empty asm statement
+// that reads and rewrites them, so that the compiler cannot sink their computation past a
+// phase barrier.
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(u32x4& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+// Workgroup barrier that also fences the instruction scheduler, so that no product or
+// softmax instruction migrates into the neighbouring phase of a ping-pong schedule.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int I>
+using Idx = std::integral_constant<int, I>;
 
 // Combine a value with the one held by lane l^32 (the other half of the wavefront).
 __device__ __forceinline__ float pair_max(float x) {

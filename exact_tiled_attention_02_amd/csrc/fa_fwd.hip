@@ -396,24 +396,6 @@ constexpr int kPPWaves = 8;
 constexpr int kPPBM = 32 * kPPWaves;  // query rows per workgroup
 constexpr int kPPBN = 64;             // keys per tile
 
-// Register values that must be complete where the call stands: an empty asm statement
-// that reads and rewrites them, so that the compiler cannot sink their computation past a
-// phase barrier.
-__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(u32x4& x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
-
-// Workgroup barrier that also fences the instruction scheduler, so that no product or
-// softmax instruction migrates into the neighbouring phase.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int I>
-using Idx = std::integral_constant<int, I>;
-
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(FwdArgs a) {
   constexpr int NS = D / 16;
