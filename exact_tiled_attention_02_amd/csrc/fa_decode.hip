@@ -40,13 +40,6 @@ constexpr int kDecKeys = 32;  // keys per tile
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
 
 // Keys [lo, hi] kept for query s of a sequence with Lk keys and Sq queries.
 struct KeyRange {

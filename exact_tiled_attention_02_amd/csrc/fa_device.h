@@ -148,6 +148,15 @@ __device__ __forceinline__ void phase_barrier() {
 template <int I>
 using Idx = std::integral_constant<int, I>;
 
+// f(Idx<I>), f(Idx<I+1>), ..., f(Idx<N-1>), unrolled at compile time.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // Combine a value with the one held by lane l^32 (the other half of the wavefront).
 __device__ __forceinline__ float pair_max(float x) {
   const uint32_t b = __builtin_bit_cast(uint32_t, x);

@@ -825,13 +825,514 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Key-split ping-pong forward kernel (D = 256).
+//
+// The ping-pong schedule of fwd_pp_kernel needs two wavefronts per SIMD; at D = 256 the
+// output accumulator alone takes 128 registers per lane, and 256 query rows of Q (128 KiB)
+// do not fit in LDS beside the tile stages.  Here the two wavefronts of a SIMD work on the
+// SAME 32 query rows and split the keys instead: group 0 takes the even tiles of the
+// processing order, group 1 the odd ones, each with its own running max, sum and
+// accumulator.  A workgroup is 128 query rows (four SIMD pairs) and its Q takes 64 KiB of
+// LDS.  Tiles are 32 keys, so the X phase handles half as many scores per wavefront as
+// at D = 128 while the M phase has the same 32 products: the matrix pipe, not the softmax,
+// sets the period.  At the end the two partial softmax states of each row are merged
+// (the rule of the online softmax: rescale both to the larger max and add), through LDS.
+//
+// Items (one K tile and one V tile each) are consumed in interval order: item k is read by
+// the M phase of group k % 2 at interval k and holds K of tile k and V of tile k - 2 (the
+// P V product of that group's previous tile).  Item k lives in buffer k % 3: the X phase
+// right after a group read item k loads item k + 3 into the same buffer, and the group
+// waits for it at the end of its next M phase, before the barrier after which item k + 3
+// is read.
+constexpr int kKPWaves = 8;
+constexpr int kKPBM = 32 * (kKPWaves / 2);  // query rows per workgroup
+constexpr int kKPBN = 32;                   // keys per tile
+
+template <bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kp_kernel(FwdArgs a) {
+  constexpr int D = 256;
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int TILE = kKPBN * D;
+  using Swz = DualSwizzle<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t K2[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t V2[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[(kKPWaves / 2) * 32 * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // waves w and w + 4 share a SIMD and their query rows
+  const int pr = wave & 3;    // the pair: rows 32 pr .. 32 pr + 31 of the block
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+
+  const int nqb = (a.Sq + kKPBM - 1) / kKPBM;
+  const int nbh = a.B * a.Hq;
+  const int lin = blockIdx.x;
+  const int qb = nqb - 1 - lin / nbh;
+  const int bh = lin % nbh;
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+
+  int q_start, k_start, Lq, Lk;
+  if constexpr (VARLEN) {
+    q_start = a.cu_q[b];
+    Lq = a.cu_q[b + 1] - q_start;
+    k_start = a.cu_k[b];
+    Lk = a.cu_k[b + 1] - k_start;
+  } else {
+    q_start = b * a.Sq;
+    Lq = a.Sq;
+    k_start = b * a.Sk;
+    Lk = a.Sk;
+  }
+  const int q0 = qb * kKPBM;
+  if (q0 >= Lq) return;  // uniform over the workgroup
+
+  const int hk = h / (a.Hq / a.Hkv);
+  const size_t q_rs = (size_t)a.Hq * D;
+  const size_t k_rs = (size_t)a.Hkv * D;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+
+  const int diag = Lk - Lq;
+  KeyWindow kw{Lk, diag, 0, -1, -1};
+  if constexpr (MASKED) kw = KeyWindow{Lk, diag, a.causal, a.window_left, a.window_right};
+  const int last_row = min(q0 + kKPBM, Lq) - 1;
+  const int k_lo = kw.lo(q0), k_hi = kw.hi(last_row);
+  const int kb_begin = k_lo / kKPBN;
+  const int kb_end = k_hi >= k_lo ? k_hi / kKPBN + 1 : kb_begin;
+  const int all_lo = kw.lo(last_row), all_hi = kw.hi(q0);
+
+  const int wave_row0 = q0 + pr * 32;
+  const int my_row = wave_row0 + li;
+  const bool row_ok = my_row < Lq;
+  const int wave_lo = kw.lo(wave_row0), wave_hi = kw.hi(min(wave_row0 + 31, Lq - 1));
+  const int my_lo = kw.lo(my_row), my_hi = kw.hi(my_row);
+
+  // Processing order: the run of tiles every row keeps in full (a multiple of six long,
+  // so that each group's steps repeat the three buffers with the loop), then the edge
+  // tiles (before the run: window; after it: diagonal, tail).
+  const int u0 = min(max(kb_begin, (all_lo + kKPBN - 1) / kKPBN), kb_end);
+  int u1 = all_hi >= 0 ? min(kb_end, (all_hi + 1) / kKPBN) : 0;
+  u1 = u1 > u0 ? u0 + (u1 - u0) / 6 * 6 : u0;
+  const int n_un = u1 - u0;
+  const int n_lead = u0 - kb_begin;
+  const int n = n_un + n_lead + (kb_end - u1);
+  auto kbj = [&](int j) __attribute__((always_inline)) {
+    const int i = j - n_un;
+    const int edge = i < n_lead ? kb_begin + i : u1 + (i - n_lead);
+    return j < n_un ? u0 + j : edge;
+  };
+  const int n_s = (n + 1) / 2;  // steps per group; group 1's last one is empty when n is odd
+  const int s_un = n_un / 2;    // interior steps per group, a multiple of three
+
+  // An item is loaded by the four wavefronts of one group: NI 16-byte chunks per lane of
+  // each tile.  Indexes past either end repeat a valid tile (its buffer is free and is not
+  // read); rows past the end of the sequence re-read the last row (finite, masked to 0).
+  constexpr int NI = TILE / 8 / (64 * 4);
+  static_assert(NI >= 1 && (TILE / 8) % (64 * 4) == 0, "whole chunks per lane");
+  const uint32_t krs2 = (uint32_t)k_rs * 2u;
+  const size_t kv_first = (size_t)k_start * k_rs + (size_t)hk * D;
+  const size_t kv_rest = ((size_t)(VARLEN ? a.cu_k[a.B] : a.B * a.Sk) * k_rs - kv_first) * 2u;
+  const uint32_t kv_bytes = (uint32_t)(kv_rest < 0xffffffffu ? kv_rest : 0xffffffffu);
+  const auto kr = make_rsrc(kp, kv_bytes);
+  const auto vr = make_rsrc(vp, kv_bytes);
+  // Row and swizzled column (bytes) of this lane's chunk i of a tile.
+  auto lrow = [&](int i) __attribute__((always_inline)) { return ((i * 4 + pr) * 64 + lane) / Swz::CH; };
+  auto lcol = [&](int i) __attribute__((always_inline)) {
+    return (uint32_t)(Swz::chunk(lrow(i), lane % Swz::CH) * 16);
+  };
+  uint32_t loff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) loff[i] = __umul24((uint32_t)lrow(i), krs2) + lcol(i);
+  struct ItemSrc {
+    int kk0, vk0;
+  };
+  auto item_src = [&](int k) __attribute__((always_inline)) {
+    return ItemSrc{__builtin_amdgcn_readfirstlane(kbj(min(k, n - 1)) * kKPBN),
+                   __builtin_amdgcn_readfirstlane(kbj(max(min(k - 2, n - 1), 0)) * kKPBN)};
+  };
+  auto load_item = [&](ItemSrc src, uint16_t* Kd, uint16_t* Vd) __attribute__((always_inline)) {
+    if (max(src.kk0, src.vk0) + kKPBN <= Lk) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        lds_buffer_load16(kr, loff[i], Kd + (i * 4 + pr) * 64 * 8, (uint32_t)src.kk0 * krs2);
+        lds_buffer_load16(vr, loff[i], Vd + (i * 4 + pr) * 64 * 8, (uint32_t)src.vk0 * krs2);
+      }
+    } else {
+      // A tile that runs past the last key: clamp its rows (rows < 32; the host keeps
+      // row_bytes below 2^24 for the 24-bit multiply).
+      const int klim = Lk - 1 - src.kk0, vlim = Lk - 1 - src.vk0;
+      const int ln = opaque(lane);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = ((i * 4 + pr) * 64 + ln) / Swz::CH;
+        const uint32_t col = (uint32_t)(Swz::chunk(row, ln % Swz::CH) * 16);
+        lds_buffer_load16(kr, __umul24((uint32_t)min(row, klim), krs2) + col, Kd + (i * 4 + pr) * 64 * 8,
+                          (uint32_t)src.kk0 * krs2);
+        lds_buffer_load16(vr, __umul24((uint32_t)min(row, vlim), krs2) + col, Vd + (i * 4 + pr) * 64 * 8,
+                          (uint32_t)src.vk0 * krs2);
+      }
+    }
+  };
+  auto kbuf = [&](auto bi) __attribute__((always_inline)) {
+    constexpr int I = decltype(bi)::value % 3;
+    return I == 0 ? K0 : (I == 1 ? K1 : K2);
+  };
+  auto vbuf = [&](auto bi) __attribute__((always_inline)) {
+    constexpr int I = decltype(bi)::value % 3;
+    return I == 0 ? V0 : (I == 1 ? V1 : V2);
+  };
+
+  // Q rows of the pair into its LDS region, split between its two wavefronts (rows past
+  // the end re-read the last row, clamped as absolute indexes from a clamped base row),
+  // then items 0 and 2 by group 0, item 1 by group 1.
+  uint16_t* Qw = Qs + pr * 32 * D;
+  {
+    const int base_row = min(wave_row0, Lq - 1);
+    const size_t qfirst = (size_t)(q_start + base_row) * q_rs + (size_t)h * D;
+    const size_t qrest = ((size_t)(VARLEN ? a.cu_q[a.B] : a.B * a.Sq) * q_rs - qfirst) * 2u;
+    const auto qr = make_rsrc((const uint16_t*)a.q + qfirst, (uint32_t)(qrest < 0xffffffffu ? qrest : 0xffffffffu));
+#pragma unroll
+    for (int i = 0; i < 32 * D / 8 / 128; ++i) {
+      const int chunk = (i * 2 + grp) * 64 + lane;
+      const int r = chunk / Swz::CH;
+      const int row = min(wave_row0 + r, Lq - 1) - base_row;
+      const uint32_t off = (uint32_t)(row * (int)q_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
+      lds_buffer_load16(qr, off, Qw + (i * 2 + grp) * 64 * 8);
+    }
+  }
+  if (n > 0) {
+    if (grp == 0) {
+      load_item(item_src(0), K0, V0);
+      load_item(item_src(2), K2, V2);
+    } else {
+      load_item(item_src(1), K1, V1);
+    }
+  }
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float c = a.scale_log2;
+  constexpr float kLog2e = 1.4426950408889634f;
+  float sl2 = 0.f;
+  if constexpr (ALIBI) sl2 = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
+  const int row_diag = my_row + diag;
+
+  // Row reads (row li, chunk 2 st + lh) and transposed reads (rows tr_row + 8 hi, column
+  // 32 d + tr_col) of a tile, formed from one base each: with f = f(row) < 16 the swizzled
+  // chunk (2 st + lh) ^ f is 2 (st ^ (f >> 1)) + (lh ^ (f & 1)), so the element offset is
+  // kbase ^ 16 st; likewise (4 d + c) ^ f = 4 (d ^ (f >> 2)) + (c ^ (f & 3)) for c < 4
+  // gives vbase ^ 32 d.  The XOR touches only bits below 256 = D, where the bases hold
+  // the row's swizzle; the second half of either range is the first plus 128 (bit 7 of
+  // the base is clear), which the reads take as an immediate offset.
+  const int tr_row = 4 * lh + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int kbase = Swz::row_elem(li, lh);
+  int vbase[2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) vbase[hi] = Swz::elem(tr_row + 8 * hi, tr_col);
+
+  f32x16 s;              // S^T of the current tile: M phase -> X phase
+  Frag8 pf[2];           // P^T of the previous tile: X phase -> next M phase
+  bool pv_live = false;  // pf holds probabilities to add
+
+  // The read offsets are re-formed in every M phase from opaque copies of the bases
+  // (taken before the phase's reads, so that they do not split its schedule) rather than
+  // hoisted into registers that would stay live across the loop.
+  // M phase: S^T of this step's tile (when live for this wavefront) and the P V product
+  // of the group's previous tile, both from the item this step reads, as one sequence of
+  // products: ops 0..NS-1 form S^T (K and Q row reads), ops NS..NS+2ND-1 the P V product
+  // (16-key chunk t, d-block d; two transposed V reads).  The operand reads run PD ops
+  // ahead, written out in that order and fenced for the machine scheduler, which would
+  // otherwise sink each read down to its product.
+  constexpr int NOPS = NS + 2 * ND;
+  constexpr int PD = 4;
+  auto mphase = [&](bool s_live, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, auto fused_tag)
+                    __attribute__((always_inline)) {
+    constexpr bool FUSED = decltype(fused_tag)::value;
+    const int kb = opaque(kbase), vb0 = opaque(vbase[0]), vb1 = opaque(vbase[1]);
+    Frag8 opa[PD], opb[PD];
+    auto issue = [&](auto op_tag) __attribute__((always_inline)) {
+      constexpr int OP = decltype(op_tag)::value, SL = OP % PD;
+      if constexpr (OP < NS) {
+        const int o = (kb ^ (16 * (OP % (NS / 2)))) + 128 * (OP / (NS / 2));
+        opb[SL].v = load16(Qw + o);
+        opa[SL].v = load16(K + o);
+      } else {
+        constexpr int t = (OP - NS) / ND, d = (OP - NS) % ND;
+        const int o0 = (vb0 ^ (32 * (d % (ND / 2)))) + 128 * (d / (ND / 2));
+        const int o1 = (vb1 ^ (32 * (d % (ND / 2)))) + 128 * (d / (ND / 2));
+        const u32x2 lo = lds_read_tr16(V + t * 16 * D + o0);
+        const u32x2 hi = lds_read_tr16(V + t * 16 * D + o1);
+        opa[SL].v = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    };
+    auto run = [&](auto op_tag) __attribute__((always_inline)) {
+      constexpr int OP = decltype(op_tag)::value, SL = OP % PD;
+      if constexpr (OP < NS) {
+        s = mfma32x32x16<BF16>(opa[SL], opb[SL], s);
+      } else {
+        constexpr int t = (OP - NS) / ND, d = (OP - NS) % ND;
+        acc[d] = mfma32x32x16<BF16>(opa[SL], pf[t], acc[d]);
+      }
+    };
+    // Ops [B, E) as one pipeline.
+    auto pipeline = [&](auto b_tag, auto e_tag) __attribute__((always_inline)) {
+      constexpr int B = decltype(b_tag)::value, E = decltype(e_tag)::value;
+      static_for<B, (B + PD < E ? B + PD : E)>([&](auto op) { issue(op); });
+      static_for<B, E>([&](auto op) {
+        __builtin_amdgcn_sched_barrier(0);  // keep the written order
+        run(op);
+        constexpr int NX = decltype(op)::value + PD;
+        if constexpr (NX < E) issue(Idx<NX>{});
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (FUSED) {
+      s = f32x16{};
+      pipeline(Idx<0>{}, Idx<NOPS>{});
+    } else {
+      if (s_live) {
+        s = f32x16{};
+        pipeline(Idx<0>{}, Idx<NS>{});
+      }
+      if (pv_live) pipeline(Idx<NS>{}, Idx<NOPS>{});
+    }
+    pin(s);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) pin(acc[d]);
+  };
+
+  // X phase of the tile at key k0; first issues the next item into the buffer the M phase
+  // just read.
+  auto xphase = [&](int k0, bool live, auto mask_tag, ItemSrc next, uint16_t* __restrict__ Kd,
+                    uint16_t* __restrict__ Vd) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    load_item(next, Kd, Vd);
+    pv_live = live;
+    if (!live) return;
+    if constexpr (ALIBI) {
+      const float base = (float)(k0 + 4 * lh - row_diag);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float dist = base + (float)(8 * (r >> 2) + (r & 3));
+        s[r] = fmaf(-sl2, fabsf(dist), s[r] * c);
+      }
+    }
+    if constexpr (MASK) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        s[r] = (key >= my_lo && key <= my_hi) ? s[r] : -INFINITY;
+      }
+    }
+    float mx = m_run;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = pair_max(mx);
+    const float m_use = (mx == -INFINITY) ? 0.f : mx;
+    float alpha;
+    float ls = 0.f;
+    if constexpr (ALIBI) {
+      alpha = fast_exp2(m_run - m_use);
+      m_run = mx;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[r] - m_use);
+        s[r] = p;
+        ls += p;
+      }
+    } else {
+      alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
+      m_run = mx;
+      const float mc = m_use * c;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[r], c, -mc));
+        s[r] = p;
+        ls += p;
+      }
+    }
+    l_run = l_run * alpha + ls;
+    if (__builtin_expect(__any(alpha != 1.f), 0)) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) acc[d] *= alpha;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = t * 8;
+      pf[t].v = u32x4{pack2<BF16>(s[r0 + 0], s[r0 + 1]), pack2<BF16>(s[r0 + 2], s[r0 + 3]),
+                      pack2<BF16>(s[r0 + 4], s[r0 + 5]), pack2<BF16>(s[r0 + 6], s[r0 + 7])};
+      pin(pf[t].v);
+    }
+#pragma unroll
+    for (int d = 0; d < ND; ++d) pin(acc[d]);
+    pin(m_run);
+    pin(l_run);
+  };
+
+  // Step i of this group: tile j = 2 i + grp of the processing order, item j, buffer
+  // j % 3 = (2 U + grp) % 3 with U = i % 3 (group 0 walks buffers 0, 2, 1, group 1 walks
+  // 1, 0, 2).  Both buffer choices are selects on the same condition, so the compiler can
+  // still tell the loads in flight from the reads of the next step.
+  auto step = [&](int i, auto mask_tag, auto u, auto fused_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int U = decltype(u)::value;
+    const int j = 2 * i + grp;
+    const int k0 = kbj(min(j, n - 1)) * kKPBN;
+    bool live = true;
+    if constexpr (MASK) live = j < n && !(k0 > wave_hi || k0 + kKPBN - 1 < wave_lo);
+    const ItemSrc next = item_src(j + 3);
+    uint16_t* Kc = grp ? kbuf(Idx<2 * U + 1>{}) : kbuf(Idx<2 * U>{});
+    uint16_t* Vc = grp ? vbuf(Idx<2 * U + 1>{}) : vbuf(Idx<2 * U>{});
+    mphase(live, Kc, Vc, fused_tag);
+    wait_vmcnt<0>();
+    phase_barrier();
+    xphase(k0, live, mask_tag, next, Kc, Vc);
+    phase_barrier();
+  };
+
+  wait_all_memory();
+  __syncthreads();
+  if (grp == 1) phase_barrier();
+  using F = std::false_type;
+  using T = std::true_type;
+  // Interior steps; the first one has no previous tile to add.
+  if (s_un > 0) {
+    step(0, F{}, Idx<0>{}, F{});
+    step(1, F{}, Idx<1>{}, T{});
+    step(2, F{}, Idx<2>{}, T{});
+  }
+  for (int i = 3; i < s_un; i += 3) {
+    step(i, F{}, Idx<0>{}, T{});
+    step(i + 1, F{}, Idx<1>{}, T{});
+    step(i + 2, F{}, Idx<2>{}, T{});
+  }
+  // Edge steps.
+  int i = s_un;
+  for (; i + 3 <= n_s; i += 3) {
+    step(i, T{}, Idx<0>{}, F{});
+    step(i + 1, T{}, Idx<1>{}, F{});
+    step(i + 2, T{}, Idx<2>{}, F{});
+  }
+  if (i < n_s) step(i, T{}, Idx<0>{}, F{});
+  if (i + 1 < n_s) step(i + 1, T{}, Idx<1>{}, F{});
+  // Last M phase: the P V product of the group's last tile (item 2 n_s + grp).
+  const int nb = n_s % 3;
+  if (nb == 0) {
+    mphase(false, grp ? K1 : K0, grp ? V1 : V0, F{});
+  } else if (nb == 1) {
+    mphase(false, grp ? K0 : K2, grp ? V0 : V2, F{});
+  } else {
+    mphase(false, grp ? K2 : K1, grp ? V2 : V1, F{});
+  }
+  wait_vmcnt<0>();  // the last X phase's loads (repeats of valid tiles) have landed
+  if (grp == 0) phase_barrier();
+
+  // Merge the two groups' partial states of each row through LDS (every buffer is free
+  // once all wavefronts are past the barrier): group 1 writes its accumulator, max and
+  // sum; group 0 rescales both to the larger max, adds, and stores.
+  const float l_tot = pair_sum(l_run);
+  __syncthreads();
+  float* xa;
+  float* xb;
+  if (pr == 0) {
+    xa = (float*)K0;
+    xb = (float*)K1;
+  } else if (pr == 1) {
+    xa = (float*)K2;
+    xb = (float*)V0;
+  } else if (pr == 2) {
+    xa = (float*)V1;
+    xb = (float*)V2;
+  } else {
+    xa = (float*)Qs;
+    xb = (float*)Qs + TILE / 2;
+  }
+  float* xs = (float*)Qs + TILE + pr * 128;  // max, sum of the pair's group-1 wavefront
+  if (grp == 1) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float* dst = (d < ND / 2 ? xa : xb) + (((d % (ND / 2)) * 4 + g) * 64 + lane) * 4;
+        *(f32x4*)dst = f32x4{acc[d][4 * g + 0], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]};
+      }
+    xs[lane] = m_run;
+    xs[64 + lane] = l_tot;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float m1 = xs[lane], l1 = xs[64 + lane];
+  const float m = fmaxf(m_run, m1);
+  float a0 = 0.f, a1 = 0.f;
+  if (m != -INFINITY) {
+    if constexpr (ALIBI) {
+      a0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m);
+      a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - m);
+    } else {
+      a0 = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m) * c);
+      a1 = m1 == -INFINITY ? 0.f : fast_exp2((m1 - m) * c);
+    }
+  }
+  const float l_all = l_tot * a0 + l1 * a1;
+  if (row_ok) {
+    const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
+    const float w0 = a0 * inv, w1 = a1 * inv;
+    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * D;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      __builtin_amdgcn_sched_barrier(0);  // one d-block at a time: no hoisted reads
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 o1 = *(const f32x4*)((d < ND / 2 ? xa : xb) + (((d % (ND / 2)) * 4 + g) * 64 + lane) * 4);
+        const int col = d * 32 + 8 * g + 4 * lh;
+        u32x2 w;
+        w.x = pack2<BF16>(acc[d][4 * g + 0] * w0 + o1[0] * w1, acc[d][4 * g + 1] * w0 + o1[1] * w1);
+        w.y = pack2<BF16>(acc[d][4 * g + 2] * w0 + o1[2] * w1, acc[d][4 * g + 3] * w0 + o1[3] * w1);
+        *(u32x2*)(op + col) = w;
+      }
+    }
+    if (lh == 0) {
+      float lse = INFINITY;
+      if (l_all > 0.f) lse = (ALIBI ? m * 0.69314718055994531f : m * a.scale) + __logf(l_all);
+      size_t idx;
+      if constexpr (VARLEN) {
+        idx = (size_t)h * a.cu_q[a.B] + q_start + my_row;
+      } else {
+        idx = ((size_t)b * a.Hq + h) * a.Sq + my_row;
+      }
+      a.lse[idx] = lse;
+    }
+  }
+}
+
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  // The ping-pong kernels address a sequence's K/V rows with 32-bit byte offsets and a
+  // K/V row stride below 2^24 bytes.
+  const bool offsets_fit =
+      (uint64_t)a.Sk * a.Hkv * D * 2u < (1ull << 32) - (1ull << 20) && (uint64_t)a.Hkv * D * 2u < (1ull << 24);
+  if constexpr (D == 256) {
+    if (offsets_fit) {
+      const int nqb = (a.Sq + kKPBM - 1) / kKPBM;
+      const dim3 grid((unsigned)nqb * a.B * a.Hq);
+      hipLaunchKernelGGL((fwd_kp_kernel<BF16, MASKED, VARLEN, ALIBI>), grid, dim3(512), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (D <= 128) {
-    // The ping-pong kernel addresses a sequence's K/V rows with 32-bit byte offsets and a
-    // K/V row stride below 2^24 bytes.
-    const bool offsets_fit =
-        (uint64_t)a.Sk * a.Hkv * D * 2u < (1ull << 32) - (1ull << 20) && (uint64_t)a.Hkv * D * 2u < (1ull << 24);
     if (a.Sq > kFwdBM && offsets_fit) {
       const int nqb = (a.Sq + kPPBM - 1) / kPPBM;
       const dim3 grid((unsigned)nqb * a.B * a.Hq);
