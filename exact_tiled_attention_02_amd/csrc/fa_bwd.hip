@@ -450,19 +450,23 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   // position is carried as counters (no division by the runtime block count).
   auto fetch = [&](int h, int i0, uint16_t* __restrict__ Qd, uint16_t* __restrict__ dOd, float* __restrict__ lsed,
                    float* __restrict__ dsumd) {
+    // Buffer-form direct loads from the step's first row (the flat form would make the
+    // compiler wait for every LDS read with lgkmcnt(0)).  The lane offsets address clamped
+    // rows only, so the resources need no range.
     const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * D;
-    const uint16_t* qt = (const uint16_t*)a.q + base;
-    const uint16_t* dot = (const uint16_t*)a.dout + base;
     if (qloader) {
       uint32_t off = qoff;
       if (i0 + kK2BQ > Lq)
         off = (uint32_t)(min(qr, Lq - 1 - i0) * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8) * 2u;
-      lds_direct_load16(qt, off, Qd + wave * 64 * 8);
-      lds_direct_load16(dot, off, dOd + wave * 64 * 8);
+      lds_buffer_load16(make_rsrc((const uint16_t*)a.q + base, 0xffffffffu), off, Qd + wave * 64 * 8);
+      lds_buffer_load16(make_rsrc((const uint16_t*)a.dout + base, 0xffffffffu), off, dOd + wave * 64 * 8);
     }
-    const int row = min(i0 + (lane & 31), Lq - 1);
-    if (wave == kK2Waves - 1) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, lsed);
-    if (wave == kK2Waves - 2) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, dsumd);
+    const uint32_t rr = (uint32_t)min(lane & 31, Lq - 1 - i0);
+    if (wave == kK2Waves - 1)
+      lds_buffer_load4(make_rsrc(a.lse + lse_row0 + (size_t)h * lse_hs + i0, 0xffffffffu), rr * 4u, lsed);
+    if (wave == kK2Waves - 2)
+      lds_buffer_load4(make_rsrc(a.dsum + (size_t)(q_start + i0) * a.Hq + h, 0xffffffffu), rr * (uint32_t)a.Hq * 4u,
+                       dsumd);
     // Issued before the step's dQ atomics, so the end-of-step vmcnt wait covers it too.
     if constexpr (ALIBI) sl_next = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
   };
@@ -534,17 +538,28 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
     }
     f32x16 s = f32x16{}, dp = f32x16{};
     if (live) {
+      // The row reads run SPD k-steps ahead of their products, written out in that order
+      // and fenced for the machine scheduler (which would sink each read down to its
+      // product and leave every product waiting for LDS).
+      constexpr int SPD = 2;
       const int ryo = opaque(ry);
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        Frag8 qa, ga, kf;
+      Frag8 qa[SPD], ga[SPD], kf[SPD];
+      auto issue = [&](auto st_tag) __attribute__((always_inline)) {
+        constexpr int st = decltype(st_tag)::value, sl = st % SPD;
         const int ro = li * D + ((st * 2) ^ ryo) * 8;
-        qa.v = load16(Q + ro);
-        ga.v = load16(dO + ro);
-        kf.v = load16(Ks + wave * 32 * D + ro);
-        s = mfma32x32x16<BF16>(qa, kf, s);
-        dp = mfma32x32x16<BF16>(ga, vf[st], dp);
-      }
+        qa[sl].v = load16(Q + ro);
+        ga[sl].v = load16(dO + ro);
+        kf[sl].v = load16(Ks + wave * 32 * D + ro);
+      };
+      static_for<0, SPD>([&](auto st) __attribute__((always_inline)) { issue(st); });
+      static_for<0, NS>([&](auto st_tag) __attribute__((always_inline)) {
+        constexpr int st = decltype(st_tag)::value, sl = st % SPD;
+        __builtin_amdgcn_sched_barrier(0);
+        s = mfma32x32x16<BF16>(qa[sl], kf[sl], s);
+        dp = mfma32x32x16<BF16>(ga[sl], vf[st], dp);
+        if constexpr (st + SPD < NS) issue(Idx<st + SPD>{});
+      });
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (__builtin_expect(mask, 0)) {
 #pragma unroll

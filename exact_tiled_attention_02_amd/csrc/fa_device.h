@@ -103,6 +103,12 @@ __device__ __forceinline__ void lds_buffer_load16(__amdgpu_buffer_rsrc_t r, uint
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds_base, 16, byte_off, (int)uniform_off, 0, 0);
 }
 
+// The same with 4 bytes per lane (buffer_load_dword with the lds bit): lane l writes
+// lds_base + 4*l.
+__device__ __forceinline__ void lds_buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds_base, 4, byte_off, 0, 0, 0);
+}
+
 // 4 bytes per lane straight into LDS (global_load_lds_dword): lane l writes lds_base + 4*l.
 __device__ __forceinline__ void lds_direct_load4(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_base, 4, 0, 0);
