@@ -607,24 +607,31 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
       }
     }
     if (live) {
+      // dV^T += dO^T P^T and dK^T += Q^T dS^T over ops (t, d), transposed reads KPD ops
+      // ahead in fenced order.
+      constexpr int KPD = 2, NKO = 2 * ND;
       const int b0 = opaque(trb[0]), b1 = opaque(trb[1]);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const int o_lo = b0 + 32 * (d ^ trx[0]) + t * 16 * D;
-          const int o_hi = b1 + 32 * (d ^ trx[1]) + t * 16 * D;
-          const u32x2 g_lo = lds_read_tr16(dO + o_lo);
-          const u32x2 g_hi = lds_read_tr16(dO + o_hi);
-          const u32x2 q_lo = lds_read_tr16(Q + o_lo);
-          const u32x2 q_hi = lds_read_tr16(Q + o_hi);
-          Frag8 ga, qa;
-          ga.v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
-          qa.v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
-          dvt[d] = mfma32x32x16<BF16>(ga, pf[t], dvt[d]);
-          dkt[d] = mfma32x32x16<BF16>(qa, dsf[t], dkt[d]);
-        }
-      }
+      Frag8 ga[KPD], qa[KPD];
+      auto issue = [&](auto op_tag) __attribute__((always_inline)) {
+        constexpr int op = decltype(op_tag)::value, sl = op % KPD, t = op / ND, d = op % ND;
+        const int o_lo = b0 + 32 * (d ^ trx[0]) + t * 16 * D;
+        const int o_hi = b1 + 32 * (d ^ trx[1]) + t * 16 * D;
+        const u32x2 g_lo = lds_read_tr16(dO + o_lo);
+        const u32x2 g_hi = lds_read_tr16(dO + o_hi);
+        const u32x2 q_lo = lds_read_tr16(Q + o_lo);
+        const u32x2 q_hi = lds_read_tr16(Q + o_hi);
+        ga[sl].v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
+        qa[sl].v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
+      };
+      static_for<0, KPD>([&](auto op) __attribute__((always_inline)) { issue(op); });
+      static_for<0, NKO>([&](auto op_tag) __attribute__((always_inline)) {
+        constexpr int op = decltype(op_tag)::value, sl = op % KPD, t = op / ND, d = op % ND;
+        __builtin_amdgcn_sched_barrier(0);
+        dvt[d] = mfma32x32x16<BF16>(ga[sl], pf[t], dvt[d]);
+        dkt[d] = mfma32x32x16<BF16>(qa[sl], dsf[t], dkt[d]);
+        if constexpr (op + KPD < NKO) issue(Idx<op + KPD>{});
+      });
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (DQ) {
       // This wavefront's prefetch of the next step has landed (and the dQ atomics it issued
@@ -643,25 +650,40 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
         if (mask) any = i0 < Lq && k0 <= kw.hi(min(i0 + kK2BQ, Lq) - 1) && k_last >= kw.lo(i0);
         if (any) {
           f32x16 dq = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < kK2Keys / 16; ++ks) {
-            Frag8 sa, kb2;
-            sa.v = load16(&dSc[li * SSTR + ks * 16 + lh * 8]);
+          // Operand reads QPD key steps ahead, in fenced order (as for S and dP above).
+          constexpr int QPD = 3, NKS = kK2Keys / 16;
+          Frag8 sa[QPD], kb2[QPD];
+          auto issue = [&](auto ks_tag) __attribute__((always_inline)) {
+            constexpr int ks = decltype(ks_tag)::value, sl = ks % QPD;
+            sa[sl].v = load16(&dSc[li * SSTR + ks * 16 + lh * 8]);
             const u32x2 lo = lds_read_tr16(Ks + ks * 16 * D + ktr[0]);
             const u32x2 hi = lds_read_tr16(Ks + ks * 16 * D + ktr[1]);
-            kb2.v = u32x4{lo.x, lo.y, hi.x, hi.y};
-            dq = mfma32x32x16<BF16>(sa, kb2, dq);
-          }
-          float* dst = a.dq_acc + ((size_t)(q_start + i0 + 4 * lh) * a.Hq + h) * D + dblk * 32 + li;
-          const size_t rstride = (size_t)a.Hq * D;
+            kb2[sl].v = u32x4{lo.x, lo.y, hi.x, hi.y};
+          };
+          static_for<0, QPD>([&](auto ks) __attribute__((always_inline)) { issue(ks); });
+          static_for<0, NKS>([&](auto ks_tag) __attribute__((always_inline)) {
+            constexpr int ks = decltype(ks_tag)::value, sl = ks % QPD;
+            __builtin_amdgcn_sched_barrier(0);
+            dq = mfma32x32x16<BF16>(sa[sl], kb2[sl], dq);
+            if constexpr (ks + QPD < NKS) issue(Idx<ks + QPD>{});
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          // Buffer atomics from the step's first row: the row offset of register r is
+          // uniform (scalar offset), the lane's row half and column form the lane offset.
+          const auto dqr = make_rsrc(a.dq_acc + ((size_t)(q_start + i0) * a.Hq + h) * D, 0xffffffffu);
+          const uint32_t rs4 = (uint32_t)a.Hq * D * 4u;  // bytes per row
+          const uint32_t voff = 4u * lh * rs4 + (uint32_t)(dblk * 32 + li) * 4u;
           if (__builtin_expect(i0 + kK2BQ <= Lq, 1)) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * rstride, dq[r]);
+            for (int r = 0; r < 16; ++r)
+              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[r], dqr, (int)voff, (int)((8 * (r >> 2) + (r & 3)) * rs4),
+                                                            0);
           } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int rr = 8 * (r >> 2) + (r & 3);
-              if (i0 + 4 * lh + rr < Lq) unsafeAtomicAdd(dst + rr * rstride, dq[r]);
+              if (i0 + 4 * lh + rr < Lq)
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[r], dqr, (int)voff, (int)(rr * rs4), 0);
             }
           }
         }
