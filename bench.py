@@ -51,7 +51,7 @@ class Case:
             d["do"] = synth._cast(rng.standard_normal(tuple(d["q"].shape), dtype=np.float32), self.w.dtype).cuda()
         self.d = d
         self.out = torch.empty_like(d["q"])
-        self.lse = torch.empty(fa.lse_shape(d["q"]), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty(fa.lse_shape(d["q"], d.get("cu_seqlens_q")), dtype=torch.float32, device="cuda")
         if with_bwd:
             self.dq, self.dk, self.dv = (torch.empty_like(d[k]) for k in ("q", "k", "v"))
             self.ws = fa.workspace_for(d["q"])
@@ -59,6 +59,11 @@ class Case:
 
     def fwd(self):
         from exact_tiled_attention_02_amd import fa
+        if "cu_seqlens_q" in self.d:  # packed variable-length batch
+            fa.fa_fwd(self.d["q"], self.d["k"], self.d["v"], self.out, self.lse, causal=self.w.causal,
+                      scale=self.w.softmax_scale, cu_seqlens_q=self.d["cu_seqlens_q"],
+                      cu_seqlens_k=self.d["cu_seqlens_k"], max_seqlen_q=self.w.seqlen_q, max_seqlen_k=self.w.seqlen_k)
+            return
         fa.fa_fwd(self.d["q"], self.d["k"], self.d["v"], self.out, self.lse, causal=self.w.causal,
                   scale=self.w.softmax_scale)
 
@@ -249,7 +254,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--skip-gqa", action="store_true", help="skip the S=8192 GQA forward detail")
+    ap.add_argument("--skip-gqa", action="store_true",
+                    help="skip the forward details of the other workloads (GQA S=8192, MHA S=2048, varlen D=256)")
     ap.add_argument("--gqa-backward", action="store_true", help="also time the backward at the S=8192 GQA shape")
     ap.add_argument("--skip-decode", action="store_true", help="skip the KV-cache decode detail")
     ap.add_argument("--copy-calibration", action="store_true", help="only run a 512 MiB device copy (counter scale)")
@@ -336,6 +342,20 @@ def main():
             })
         log(f"[bench] GQA S=8192 forward {t3 * 1e6:.1f} us -> {detail[c3.w.name]['fwd_tflops']:.1f} TFLOPS")
         del c3
+        torch.cuda.empty_cache()
+
+    if not args.skip_gqa:
+        # forwards of the causal MHA (B=4, H=16, S=2048, D=128, bf16) and the packed
+        # variable-length (16 sequences, H=8, D=256, fp16) workloads
+        for n in (2, 4):
+            cn = Case(n, with_bwd=False)
+            for _ in range(W):
+                cn.fwd()
+            tn = time_launches(cn.fwd, K)
+            detail[cn.w.name] = {"fwd_tflops": cn.fwd_flops / tn / 1e12,
+                                 "fwd_pct_peak": 100 * cn.fwd_flops / tn / 1e12 / PEAK_TFLOPS, "fwd_us": tn * 1e6}
+            log(f"[bench] {cn.w.name} forward {tn * 1e6:.1f} us -> {detail[cn.w.name]['fwd_tflops']:.1f} TFLOPS")
+            del cn
         torch.cuda.empty_cache()
 
     if not args.skip_decode:
