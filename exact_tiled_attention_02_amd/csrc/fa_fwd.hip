@@ -1283,16 +1283,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   if (i < n_s) step(i, T{}, Idx<0>{}, F{});
   if (i + 1 < n_s) step(i + 1, T{}, Idx<1>{}, F{});
-  // Last M phase: the P V product of the group's last tile (item 2 n_s + grp).
-  const int nb = n_s % 3;
-  if (nb == 0) {
-    mphase(false, grp ? K1 : K0, grp ? V1 : V0, F{});
-  } else if (nb == 1) {
-    mphase(false, grp ? K0 : K2, grp ? V0 : V2, F{});
-  } else {
-    mphase(false, grp ? K2 : K1, grp ? V2 : V1, F{});
-  }
-  wait_vmcnt<0>();  // the last X phase's loads (repeats of valid tiles) have landed
+  // Last M phase: the P V product of the group's last tile (item 2 n_s + grp, buffer
+  // (2 n_s + grp) % 3).  One copy of the product block with the buffer picked at run time
+  // (three static copies made the register allocator spill the accumulators around
+  // their join); the last X phase's loads (repeats of valid tiles) are waited for first,
+  // as the compiler cannot tell the picked buffer from theirs.
+  wait_vmcnt<0>();
+  const int vi = (2 * n_s + grp) % 3;
+  mphase(false, K0, vi == 0 ? V0 : (vi == 1 ? V1 : V2), F{});
   if (grp == 0) phase_barrier();
 
   // Merge the two groups' partial states of each row through LDS (every buffer is free
