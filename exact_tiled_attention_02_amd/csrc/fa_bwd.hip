@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   const int ch = tid % CH;
   const size_t pair = (size_t)blockIdx.x * PAIRS + pair_local;
   size_t rows = (size_t)a.B * a.Sq;
-  if constexpr (VARLEN) rows = (size_t)a.cu_q[a.B];
+  if constexpr (VARLEN) rows = (size_t)load_uniform(a.cu_q + a.B);
   const bool live = pair < rows * a.Hq;
   float s = 0.f;
   if (live) {
@@ -105,10 +105,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
 
   int q_start, k_start, Lq, Lk;
   if constexpr (VARLEN) {
-    q_start = a.cu_q[b];
-    Lq = a.cu_q[b + 1] - q_start;
-    k_start = a.cu_k[b];
-    Lk = a.cu_k[b + 1] - k_start;
+    q_start = load_uniform(a.cu_q + b);
+    Lq = load_uniform(a.cu_q + b + 1) - q_start;
+    k_start = load_uniform(a.cu_k + b);
+    Lk = load_uniform(a.cu_k + b + 1) - k_start;
   } else {
     q_start = b * a.Sq;
     Lq = a.Sq;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   size_t lse_row0;  // index of row 0 of this sequence in the LSE of head 0
   size_t lse_hs;    // LSE stride between heads
   if constexpr (VARLEN) {
-    lse_hs = (size_t)a.cu_q[a.B];
+    lse_hs = (size_t)load_uniform(a.cu_q + a.B);
     lse_row0 = (size_t)q_start;
   } else {
     lse_hs = (size_t)a.Sq;
@@ -388,10 +388,10 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
 
   int q_start, k_start, Lq, Lk;
   if constexpr (VARLEN) {
-    q_start = a.cu_q[b];
-    Lq = a.cu_q[b + 1] - q_start;
-    k_start = a.cu_k[b];
-    Lk = a.cu_k[b + 1] - k_start;
+    q_start = load_uniform(a.cu_q + b);
+    Lq = load_uniform(a.cu_q + b + 1) - q_start;
+    k_start = load_uniform(a.cu_k + b);
+    Lk = load_uniform(a.cu_k + b + 1) - k_start;
   } else {
     q_start = b * a.Sq;
     Lq = a.Sq;
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   constexpr float kLog2e = 1.4426950408889634f;
   size_t lse_row0, lse_hs;
   if constexpr (VARLEN) {
-    lse_hs = (size_t)a.cu_q[a.B];
+    lse_hs = (size_t)load_uniform(a.cu_q + a.B);
     lse_row0 = (size_t)q_start;
   } else {
     lse_hs = (size_t)a.Sq;
@@ -779,10 +779,10 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
 
   int q_start, k_start, Lq, Lk;
   if constexpr (VARLEN) {
-    q_start = a.cu_q[b];
-    Lq = a.cu_q[b + 1] - q_start;
-    k_start = a.cu_k[b];
-    Lk = a.cu_k[b + 1] - k_start;
+    q_start = load_uniform(a.cu_q + b);
+    Lq = load_uniform(a.cu_q + b + 1) - q_start;
+    k_start = load_uniform(a.cu_k + b);
+    Lk = load_uniform(a.cu_k + b + 1) - k_start;
   } else {
     q_start = b * a.Sq;
     Lq = a.Sq;
@@ -852,7 +852,7 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
   if (row_ok) {
     size_t li_idx;
     if constexpr (VARLEN) {
-      li_idx = (size_t)h * a.cu_q[a.B] + q_start + my_row;
+      li_idx = (size_t)h * load_uniform(a.cu_q + a.B) + q_start + my_row;
     } else {
       li_idx = ((size_t)b * a.Hq + h) * a.Sq + my_row;
     }
@@ -975,7 +975,7 @@ template <bool BF16, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   // 8 elements per thread
   size_t rows = (size_t)a.B * a.Sq;
-  if constexpr (VARLEN) rows = (size_t)a.cu_q[a.B];
+  if constexpr (VARLEN) rows = (size_t)load_uniform(a.cu_q + a.B);
   const size_t n8 = rows * a.Hq * a.D / 8;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
     const u32x4 x0 = load16(a.dq_acc + i * 8);

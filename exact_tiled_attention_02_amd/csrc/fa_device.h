@@ -74,6 +74,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_ptr) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// An int loaded from a wavefront-uniform address, kept in a scalar register.  The compiler
+// cannot prove such a load uniform; without this, buffer resources and offsets built from
+// the value sit in vector registers and every buffer access becomes a loop over lanes.
+__device__ __forceinline__ int load_uniform(const int32_t* p) { return __builtin_amdgcn_readfirstlane(*p); }
+
 // 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): lane l of the
 // wavefront writes lds_base + 16*l.  lds_base must be the same in every lane.
 __device__ __forceinline__ void lds_direct_load16(const void* gptr, void* lds_base) {

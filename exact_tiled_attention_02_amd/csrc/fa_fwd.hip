@@ -80,6 +80,7 @@ __device__ __forceinline__ bool fwd_block(const FwdArgs& a, int& b, int& h, int&
       cnt = (len + BM - 1) / BM * hx;
       total = cnt;
       for (int o = 32; o >= 1; o >>= 1) total += __shfl_xor(total, o);
+      total = __builtin_amdgcn_readfirstlane(total);  // equal in every lane
     }
     if (total < kSeqMajorMinBlocks) {
       const int per = a.B * hx;
@@ -110,6 +111,7 @@ __device__ __forceinline__ bool fwd_block(const FwdArgs& a, int& b, int& h, int&
     const int u = t - pre_b;
     qb = cnt_b / hx - 1 - u / hx;
     h = x * hx + u % hx;
+    b = __builtin_amdgcn_readfirstlane(b);  // uniform: keeps what is built from it scalar
     return true;
   }
   const int nbh = a.B * a.Hq;
@@ -146,10 +148,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   int q_start, k_start, Lq, Lk;
   if constexpr (VARLEN) {
-    q_start = a.cu_q[b];
-    Lq = a.cu_q[b + 1] - q_start;
-    k_start = a.cu_k[b];
-    Lk = a.cu_k[b + 1] - k_start;
+    q_start = load_uniform(a.cu_q + b);
+    Lq = load_uniform(a.cu_q + b + 1) - q_start;
+    k_start = load_uniform(a.cu_k + b);
+    Lk = load_uniform(a.cu_k + b + 1) - k_start;
   } else {
     q_start = b * a.Sq;
     Lq = a.Sq;
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       if (l_tot > 0.f) lse = (ALIBI ? m_run * 0.69314718055994531f : m_run * a.scale) + __logf(l_tot);
       size_t idx;
       if constexpr (VARLEN) {
-        idx = (size_t)h * a.cu_q[a.B] + q_start + my_row;
+        idx = (size_t)h * load_uniform(a.cu_q + a.B) + q_start + my_row;
       } else {
         idx = ((size_t)b * a.Hq + h) * a.Sq + my_row;
       }
@@ -489,10 +491,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int q_start, k_start, Lq, Lk;
   if constexpr (VARLEN) {
-    q_start = a.cu_q[b];
-    Lq = a.cu_q[b + 1] - q_start;
-    k_start = a.cu_k[b];
-    Lk = a.cu_k[b + 1] - k_start;
+    q_start = load_uniform(a.cu_q + b);
+    Lq = load_uniform(a.cu_q + b + 1) - q_start;
+    k_start = load_uniform(a.cu_k + b);
+    Lk = load_uniform(a.cu_k + b + 1) - k_start;
   } else {
     q_start = b * a.Sq;
     Lq = a.Sq;
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // offset, the row and column within the tile in the lane offset.
   const uint32_t krs2 = (uint32_t)k_rs * 2u;
   const size_t kv_first = (size_t)k_start * k_rs + (size_t)hk * D;
-  const size_t kv_rest = ((size_t)(VARLEN ? a.cu_k[a.B] : a.B * a.Sk) * k_rs - kv_first) * 2u;
+  const size_t kv_rest = ((size_t)(VARLEN ? load_uniform(a.cu_k + a.B) : a.B * a.Sk) * k_rs - kv_first) * 2u;
   const uint32_t kv_bytes = (uint32_t)(kv_rest < 0xffffffffu ? kv_rest : 0xffffffffu);
   const auto kr = make_rsrc(kp, kv_bytes);
   const auto vr = make_rsrc(vp, kv_bytes);
@@ -602,7 +604,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   {
     const int base_row = min(wave_row0, Lq - 1);
     const size_t qfirst = (size_t)(q_start + base_row) * q_rs + (size_t)h * D;
-    const size_t qrest = ((size_t)(VARLEN ? a.cu_q[a.B] : a.B * a.Sq) * q_rs - qfirst) * 2u;
+    const size_t qrest = ((size_t)(VARLEN ? load_uniform(a.cu_q + a.B) : a.B * a.Sq) * q_rs - qfirst) * 2u;
     const auto qr = make_rsrc((const uint16_t*)a.q + qfirst, (uint32_t)(qrest < 0xffffffffu ? qrest : 0xffffffffu));
 #pragma unroll
     for (int i = 0; i < 32 * D / 8 / 64; ++i) {
@@ -876,7 +878,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (l_tot > 0.f) lse = (ALIBI ? m_run * 0.69314718055994531f : m_run * a.scale) + __logf(l_tot);
       size_t idx;
       if constexpr (VARLEN) {
-        idx = (size_t)h * a.cu_q[a.B] + q_start + my_row;
+        idx = (size_t)h * load_uniform(a.cu_q + a.B) + q_start + my_row;
       } else {
         idx = ((size_t)b * a.Hq + h) * a.Sq + my_row;
       }
@@ -937,10 +939,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int q_start, k_start, Lq, Lk;
   if constexpr (VARLEN) {
-    q_start = a.cu_q[b];
-    Lq = a.cu_q[b + 1] - q_start;
-    k_start = a.cu_k[b];
-    Lk = a.cu_k[b + 1] - k_start;
+    q_start = load_uniform(a.cu_q + b);
+    Lq = load_uniform(a.cu_q + b + 1) - q_start;
+    k_start = load_uniform(a.cu_k + b);
+    Lk = load_uniform(a.cu_k + b + 1) - k_start;
   } else {
     q_start = b * a.Sq;
     Lq = a.Sq;
@@ -995,7 +997,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(NI >= 1 && (TILE / 8) % (64 * 4) == 0, "whole chunks per lane");
   const uint32_t krs2 = (uint32_t)k_rs * 2u;
   const size_t kv_first = (size_t)k_start * k_rs + (size_t)hk * D;
-  const size_t kv_rest = ((size_t)(VARLEN ? a.cu_k[a.B] : a.B * a.Sk) * k_rs - kv_first) * 2u;
+  const size_t kv_rest = ((size_t)(VARLEN ? load_uniform(a.cu_k + a.B) : a.B * a.Sk) * k_rs - kv_first) * 2u;
   const uint32_t kv_bytes = (uint32_t)(kv_rest < 0xffffffffu ? kv_rest : 0xffffffffu);
   const auto kr = make_rsrc(kp, kv_bytes);
   const auto vr = make_rsrc(vp, kv_bytes);
@@ -1053,7 +1055,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   {
     const int base_row = min(wave_row0, Lq - 1);
     const size_t qfirst = (size_t)(q_start + base_row) * q_rs + (size_t)h * D;
-    const size_t qrest = ((size_t)(VARLEN ? a.cu_q[a.B] : a.B * a.Sq) * q_rs - qfirst) * 2u;
+    const size_t qrest = ((size_t)(VARLEN ? load_uniform(a.cu_q + a.B) : a.B * a.Sq) * q_rs - qfirst) * 2u;
     const auto qr = make_rsrc((const uint16_t*)a.q + qfirst, (uint32_t)(qrest < 0xffffffffu ? qrest : 0xffffffffu));
 #pragma unroll
     for (int i = 0; i < 32 * D / 8 / 128; ++i) {
@@ -1362,7 +1364,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (l_all > 0.f) lse = (ALIBI ? m * 0.69314718055994531f : m * a.scale) + __logf(l_all);
       size_t idx;
       if constexpr (VARLEN) {
-        idx = (size_t)h * a.cu_q[a.B] + q_start + my_row;
+        idx = (size_t)h * load_uniform(a.cu_q + a.B) + q_start + my_row;
       } else {
         idx = ((size_t)b * a.Hq + h) * a.Sq + my_row;
       }
