@@ -30,6 +30,8 @@
 // v, so the gradient formulas are unchanged).
 #include <type_traits>
 
+#include <algorithm>
+
 #include "fa_device.h"
 #include "fa_params.h"
 
@@ -73,6 +75,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
   for (int m = CH / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
   if (live && ch == 0) a.dsum[pair] = s;
+  if (blockIdx.x == 0 && tid == 0) {  // the main loop's key-block queue starts empty
+    a.work[0] = 0;
+    a.work[1] = 0;
+  }
 }
 
 // ---------------------------------------------------------------- 2a. main loop, D = 256
@@ -356,7 +362,7 @@ constexpr int kK2Waves = 8;
 constexpr int kK2BQ = 32;
 
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool DQ, bool ALIBI>
-__global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) {
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
   constexpr int SSTR = kK2Keys + 8;  // dS tile [query row][key], padded
@@ -381,8 +387,8 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   const int lh = lane >> 5;
 
   const int nbh = a.B * a.Hkv;
-  const int kb = blockIdx.x / nbh;
-  const int bh = blockIdx.x % nbh;
+  const int kb = lin / nbh;
+  const int bh = lin % nbh;
   const int hk = bh % a.Hkv;
   const int b = bh / a.Hkv;
 
@@ -738,6 +744,34 @@ __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   }
 }
 
+// The key blocks of one launch, longest query range first (causal: ascending key block),
+// are handed out from a queue in the workspace: a fixed grid of at most one workgroup per
+// CU takes the next block whenever it finishes one.  Every CU stays busy until the queue
+// runs dry, whatever the XCD and shader-engine placement of the workgroups and however the
+// XCDs' speeds differ (the hardware dispatcher places workgroups in order, shader engine by
+// shader engine, so a launch with one workgroup per block left CUs idle for tens of
+// microseconds).  The preprocess empties the queue; the last workgroup to finish empties it
+// again, so a main loop launched on its own (after a complete one) finds it empty too.
+template <int D, bool BF16, bool MASKED, bool VARLEN, bool DQ, bool ALIBI>
+__global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
+  __shared__ int next;
+  const int nblocks = (a.Sk + kK2Keys - 1) / kK2Keys * a.B * a.Hkv;
+  for (;;) {
+    wait_all_memory();  // the previous block's loads into LDS and its atomics are done
+    if (threadIdx.x == 0) next = (int)atomicAdd(a.work, 1u);
+    __syncthreads();
+    const int lin = next;
+    __syncthreads();  // every wavefront has read it before it is overwritten
+    if (lin >= nblocks) break;
+    bwd_k256_block<D, BF16, MASKED, VARLEN, DQ, ALIBI>(a, lin);
+  }
+  if (threadIdx.x == 0 && atomicAdd(a.work + 1, 1u) == gridDim.x - 1) {
+    // Every workgroup is past its last take from the queue.
+    a.work[0] = 0;
+    a.work[1] = 0;
+  }
+}
+
 // ---------------------------------------------------------------- 2c. deterministic dQ pass
 
 // dQ without atomics (the deterministic backward): one workgroup per (128-row query
@@ -993,6 +1027,15 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- launch
 
+// Compute units of the current device (the backward main loop runs one workgroup per CU).
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  return n;
+}
+
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   const size_t rows = (size_t)a.B * a.Sq;  // bound on total_q in varlen mode
@@ -1008,7 +1051,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     const bool det = (stages & 8) != 0;
     if constexpr (D <= 128) {
       const int nkb = (a.Sk + kK2Keys - 1) / kK2Keys;
-      const dim3 grid((unsigned)nkb * a.B * a.Hkv);
+      const dim3 grid((unsigned)std::min(nkb * a.B * a.Hkv, cu_count()));
       if (det) {
         hipLaunchKernelGGL((bwd_main_k256_kernel<D, BF16, MASKED, VARLEN, false, ALIBI>), grid, dim3(512), 0, stream, a);
       } else {

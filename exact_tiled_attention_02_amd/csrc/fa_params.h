@@ -50,6 +50,7 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int zero_acc;  // preprocess also zeroes dq_acc (the atomic path needs it)
+  unsigned int* work;  // [2]: key blocks handed out, workgroups finished (zero between launches)
 };
 
 // Decode against a read-only KV cache (few query rows, long cache), split over the keys.
