@@ -156,3 +156,73 @@ def test_sweep_point_d64_s2048_sampled_heads():
     say(f"bwd {w.name}")
     _, _, dq, dk, dv = run_fwd_bwd(w, x)
     print(check_grads(w, x, dq, dk, dv, heads=[(0, 0), (7, 31)]))
+
+
+# ---------------------------------------------------------------- the main loop's key-block queue
+
+def _setup(w):
+    x = synth.make_inputs(w)
+    d = dev(x)
+    out, lse = fa.forward(d["q"], d["k"], d["v"], causal=w.causal, scale=w.softmax_scale)
+    grads = [torch.full_like(d[k], float("nan")) for k in ("q", "k", "v")]
+    ws = fa.workspace_for(d["q"])
+    ws.fill_(0xFF)
+    args = (d["do"], d["q"], d["k"], d["v"], out, lse, *grads, ws)
+    return x, d, grads, args
+
+
+@pytest.mark.parametrize("shape", [(3, 8, 4, 2100, 128), (4, 16, 16, 4200, 64)], ids=["108blocks", "1088blocks"])
+def test_main_loop_repeated_alone(shape):
+    """Stage 2 launched again on its own finds its key-block queue empty (the last
+    workgroup empties it): dK/dV come out bitwise the same, dQ accumulates twice."""
+    B, Hq, Hkv, S, D = shape
+    w = W("queue_repeat", B, Hq, Hkv, S, S, D, "bf16", True, seed=31)
+    say(f"bwd queue repeat B={B} Hq={Hq} Hkv={Hkv} S={S} D={D}")
+    x, d, (dq, dk, dv), args = _setup(w)
+    fa.fa_bwd(*args, causal=True)
+    torch.cuda.synchronize()
+    dq1, dk1, dv1 = dq.clone(), dk.clone(), dv.clone()
+    assert torch.isfinite(dk1).all() and torch.isfinite(dv1).all() and torch.isfinite(dq1).all()
+    dk.fill_(float("nan"))
+    dv.fill_(float("nan"))
+    for stage in (1, 2, 2, 3):
+        fa.fa_bwd_stage(stage, *args, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk1) and torch.equal(dv, dv1)
+    err = rel_fro(f64(dq), 2.0 * f64(dq1))
+    assert err <= 1e-2, f"dq after two main loops vs 2 x dq: rel Frobenius {err}"
+    if B * Hq * S <= 3 * 8 * 2100:
+        check_grads(w, x, dq1, dk1, dv1)
+
+
+def test_backward_graph_replays():
+    """The whole backward captured in a HIP graph (no memset nodes; the queue counters are
+    reset by the kernels themselves) and replayed several times, with eager work between
+    the replays: every replay matches the eager result."""
+    w = W("graph_bwd", 2, 8, 2, 1500, 1500, 128, "bf16", True, seed=32)
+    say("bwd graph capture and replays")
+    x, d, (dq, dk, dv), args = _setup(w)
+    fa.fa_bwd(*args, causal=True)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (dq, dk, dv)]
+    check_grads(w, x, *ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fa.fa_bwd(*args, causal=True)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.fa_bwd(*args, causal=True)
+    for rep in range(3):
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dk, ref[1]) and torch.equal(dv, ref[2]), f"replay {rep}: dk/dv differ"
+        err = rel_fro(f64(dq), f64(ref[0]))
+        assert err <= 1e-3, f"replay {rep}: dq rel Frobenius {err}"
+        fa.fa_bwd(*args, causal=True)  # eager work between replays
+        torch.cuda.synchronize()
