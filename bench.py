@@ -255,7 +255,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-gqa", action="store_true",
-                    help="skip the forward details of the other workloads (GQA S=8192, MHA S=2048, varlen D=256)")
+                    help="skip the forward details of the other workloads (GQA S=8192, small S=128, MHA S=2048, varlen D=256)")
     ap.add_argument("--gqa-backward", action="store_true", help="also time the backward at the S=8192 GQA shape")
     ap.add_argument("--skip-decode", action="store_true", help="skip the KV-cache decode detail")
     ap.add_argument("--copy-calibration", action="store_true", help="only run a 512 MiB device copy (counter scale)")
@@ -345,15 +345,34 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.skip_gqa:
-        # forwards of the causal MHA (B=4, H=16, S=2048, D=128, bf16) and the packed
-        # variable-length (16 sequences, H=8, D=256, fp16) workloads
-        for n in (2, 4):
+        # forwards of the small non-causal (B=1, H=2, S=128, D=64, fp16: launch/latency
+        # bound, so also in GB/s of Q, K, V, O and LSE), the causal MHA (B=4, H=16, S=2048,
+        # D=128, bf16) and the packed variable-length (16 sequences, H=8, D=256, fp16) workloads
+        for n in (1, 2, 4):
             cn = Case(n, with_bwd=False)
             for _ in range(W):
                 cn.fwd()
             tn = time_launches(cn.fwd, K)
             detail[cn.w.name] = {"fwd_tflops": cn.fwd_flops / tn / 1e12,
                                  "fwd_pct_peak": 100 * cn.fwd_flops / tn / 1e12 / PEAK_TFLOPS, "fwd_us": tn * 1e6}
+            if n == 1:
+                # A call this small is bound by the host (argument checks, ctypes): time K
+                # launches captured in one HIP graph as well, which leaves the device time.
+                g = torch.cuda.CUDAGraph()
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    cn.fwd()
+                torch.cuda.current_stream().wait_stream(s)
+                with torch.cuda.graph(g):
+                    for _ in range(K):
+                        cn.fwd()
+                g.replay()
+                tg = time_launches(g.replay, 5) / K
+                nbytes = sum(t.numel() * t.element_size() for t in (cn.d["q"], cn.d["k"], cn.d["v"], cn.out, cn.lse))
+                detail[cn.w.name].update({"fwd_us_graph": tg * 1e6, "bytes": nbytes, "gbs_graph": nbytes / tg / 1e9})
+                log(f"[bench] {cn.w.name} forward in a graph {tg * 1e6:.2f} us per call, {nbytes / tg / 1e9:.1f} GB/s")
+                del g
             log(f"[bench] {cn.w.name} forward {tn * 1e6:.1f} us -> {detail[cn.w.name]['fwd_tflops']:.1f} TFLOPS")
             del cn
         torch.cuda.empty_cache()
