@@ -160,8 +160,9 @@ size_t fa_bwd_workspace_bytes(int B, int Sq, int Hq, int D) {
   const size_t rows = (size_t)B * Sq;
   const size_t acc = rows * Hq * D * sizeof(float);
   const size_t dsum = rows * Hq * sizeof(float);
-  // + 256 bytes: the two counters of the main loop's key-block queue
-  return ((acc + 255) & ~(size_t)255) + ((dsum + 255) & ~(size_t)255) + 256;
+  // Dsum and LSE*log2(e) (dsum bytes each), then 256 bytes: the two counters of the main
+  // loop's key-block queue
+  return ((acc + 255) & ~(size_t)255) + 2 * ((dsum + 255) & ~(size_t)255) + 256;
 }
 
 namespace {
@@ -198,7 +199,8 @@ int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, con
   a.dq_acc = static_cast<float*>(workspace);
   a.dsum = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes);
   const size_t dsum_bytes = (rows * Hq * sizeof(float) + 255) & ~(size_t)255;
-  a.work = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + acc_bytes + dsum_bytes);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc_bytes + dsum_bytes);
+  a.work = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + acc_bytes + 2 * dsum_bytes);
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.B = B;

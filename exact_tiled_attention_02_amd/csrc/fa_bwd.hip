@@ -11,8 +11,8 @@
 // flash_attn_func docstring); the causal mask is bottom-right aligned as in the forward.
 //
 // Kernels (all on the caller's stream, in order):
-//   1. preprocess: Dsum = rowsum(dO * O) in fp32 and zeroing of the fp32 dQ accumulator
-//      (memory-bound);
+//   1. preprocess: Dsum = rowsum(dO * O) in fp32, LSE * log2(e), and zeroing of the fp32 dQ
+//      accumulator (memory-bound);
 //   2. main loop, one workgroup per (key block, KV head, sequence), walking the query
 //      blocks that can see its keys for every query head of the group, so dK and dV
 //      accumulate in registers with no atomics.  Per query step: S = Q K^T, P,
@@ -21,8 +21,10 @@
 //      added to the fp32 accumulator with atomics.  Head dimensions up to 128 use 256
 //      keys per workgroup (8 wavefronts of 32 keys); D = 256 uses 128 keys (4
 //      wavefronts), which its register footprint requires;
-//   3. finalize: fp32 accumulator -> dQ in the input dtype.
-// The softmax scale is folded into dS once, so neither dK nor dQ is rescaled later.
+//   3. finalize: scale * fp32 accumulator -> dQ in the input dtype.
+// The main loops form dS / scale (one multiply less per score) and apply the softmax scale
+// once to dK at its store and to dQ in the finalize; the preprocess also writes
+// LSE * log2(e) per (row, head), the exp2 offset of P in the D <= 128 main loop.
 // Sliding window and ALiBi (flash_attn_func docstring, window_size and alibi_slopes): the
 // kept keys of query i are [lo(i), hi(i)] as in the forward (KeyWindow); the main loops
 // visit only the query rows that keep a key of their block, and the ALiBi bias
@@ -74,7 +76,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   // reduce over the CH lanes of this pair (CH is a power of two <= 32, lanes contiguous)
 #pragma unroll
   for (int m = CH / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  if (live && ch == 0) a.dsum[pair] = s;
+  if (live && ch == 0) {
+    a.dsum[pair] = s;
+    // LSE * log2(e) in the same [row, head] layout (the exp2 offset the main loop needs)
+    const size_t row = pair / a.Hq;
+    const int h = (int)(pair % a.Hq);
+    size_t li;
+    if constexpr (VARLEN) {
+      li = (size_t)h * rows + row;  // lse [Hq, total_q]
+    } else {
+      li = ((row / a.Sq) * a.Hq + h) * a.Sq + row % a.Sq;  // lse [B, Hq, Sq]
+    }
+    a.lse2[pair] = a.lse[li] * 1.4426950408889634f;
+  }
   if (blockIdx.x == 0 && tid == 0) {  // the main loop's key-block queue starts empty
     a.work[0] = 0;
     a.work[1] = 0;
@@ -243,7 +257,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       s = mfma32x32x16<BF16>(qa, kf[st], s);
       dp = mfma32x32x16<BF16>(ga, vf[st], dp);
     }
-    // P and dS (scale folded in).
+    // P and dS / scale (the scale is applied to dK at its store and to dQ in the finalize).
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rl = 8 * (r >> 2) + 4 * lh + (r & 3);
@@ -254,7 +268,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       if constexpr (ALIBI) bias = fmaf(-sl, fabsf((float)(row + diag - my_key)), bias);
       const float p = keep ? fast_exp2(fmaf(s[r], c, bias)) : 0.f;
       s[r] = p;
-      dp[r] = a.scale * p * (dp[r] - dsum_s[buf][rl]);
+      dp[r] = p * (dp[r] - dsum_s[buf][rl]);  // dS / scale
     }
     Frag8 pf[2], dsf[2];
 #pragma unroll
@@ -337,8 +351,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       for (int gq = 0; gq < 4; ++gq) {
         const int col = d * 32 + 8 * gq + 4 * lh;
         u32x2 wk, wv;
-        wk.x = pack2<BF16>(dkt[d][4 * gq + 0], dkt[d][4 * gq + 1]);
-        wk.y = pack2<BF16>(dkt[d][4 * gq + 2], dkt[d][4 * gq + 3]);
+        wk.x = pack2<BF16>(dkt[d][4 * gq + 0] * a.scale, dkt[d][4 * gq + 1] * a.scale);
+        wk.y = pack2<BF16>(dkt[d][4 * gq + 2] * a.scale, dkt[d][4 * gq + 3] * a.scale);
         wv.x = pack2<BF16>(dvt[d][4 * gq + 0], dvt[d][4 * gq + 1]);
         wv.y = pack2<BF16>(dvt[d][4 * gq + 2], dvt[d][4 * gq + 3]);
         *(u32x2*)(dkp + col) = wk;
@@ -415,14 +429,6 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   const int diag = Lk - Lq;
   const float c = a.scale_log2;
   constexpr float kLog2e = 1.4426950408889634f;
-  size_t lse_row0, lse_hs;
-  if constexpr (VARLEN) {
-    lse_hs = (size_t)load_uniform(a.cu_q + a.B);
-    lse_row0 = (size_t)q_start;
-  } else {
-    lse_hs = (size_t)a.Sq;
-    lse_row0 = (size_t)b * a.Hq * a.Sq;
-  }
 
   // Query rows that keep a key of this block, [i_begin, i_end), and the kept range of
   // each row (KeyWindow; without a mask every row keeps [0, Lk - 1]).
@@ -469,7 +475,8 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
     }
     const uint32_t rr = (uint32_t)min(lane & 31, Lq - 1 - i0);
     if (wave == kK2Waves - 1)
-      lds_buffer_load4(make_rsrc(a.lse + lse_row0 + (size_t)h * lse_hs + i0, 0xffffffffu), rr * 4u, lsed);
+      lds_buffer_load4(make_rsrc(a.lse2 + (size_t)(q_start + i0) * a.Hq + h, 0xffffffffu), rr * (uint32_t)a.Hq * 4u,
+                       lsed);
     if (wave == kK2Waves - 2)
       lds_buffer_load4(make_rsrc(a.dsum + (size_t)(q_start + i0) * a.Hq + h, 0xffffffffu), rr * (uint32_t)a.Hq * 4u,
                        dsumd);
@@ -585,11 +592,11 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g4 + j;
-        float bias = -l4[j] * kLog2e;
+        float bias = -l4[j];  // LSE * log2(e), from the preprocess
         if constexpr (ALIBI) bias = fmaf(-sl, fabsf(abase + (float)(8 * g4 + j)), bias);
         const float p = fast_exp2(fmaf(s[r], c, bias));
         s[r] = p;
-        dp[r] = a.scale * p * (dp[r] - d4[j]);
+        dp[r] = p * (dp[r] - d4[j]);  // dS / scale
       }
     }
     Frag8 pf[2], dsf[2];
@@ -733,8 +740,8 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
       for (int gq = 0; gq < 4; ++gq) {
         const int col = d * 32 + 8 * gq + 4 * lh;
         u32x2 wk, wv;
-        wk.x = pack2<BF16>(dkt[d][4 * gq + 0], dkt[d][4 * gq + 1]);
-        wk.y = pack2<BF16>(dkt[d][4 * gq + 2], dkt[d][4 * gq + 3]);
+        wk.x = pack2<BF16>(dkt[d][4 * gq + 0] * a.scale, dkt[d][4 * gq + 1] * a.scale);
+        wk.y = pack2<BF16>(dkt[d][4 * gq + 2] * a.scale, dkt[d][4 * gq + 3] * a.scale);
         wv.x = pack2<BF16>(dvt[d][4 * gq + 0], dvt[d][4 * gq + 1]);
         wv.y = pack2<BF16>(dvt[d][4 * gq + 2], dvt[d][4 * gq + 3]);
         *(u32x2*)(dkp + col) = wk;
@@ -1017,10 +1024,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     const float* f0 = (const float*)&x0;
     const float* f1 = (const float*)&x1;
     u32x4 o;
-    o.x = pack2<BF16>(f0[0], f0[1]);
-    o.y = pack2<BF16>(f0[2], f0[3]);
-    o.z = pack2<BF16>(f1[0], f1[1]);
-    o.w = pack2<BF16>(f1[2], f1[3]);
+    const float sc = a.scale;  // the main loops accumulate dS K with dS / scale
+    o.x = pack2<BF16>(f0[0] * sc, f0[1] * sc);
+    o.y = pack2<BF16>(f0[2] * sc, f0[3] * sc);
+    o.z = pack2<BF16>(f1[0] * sc, f1[1] * sc);
+    o.w = pack2<BF16>(f1[2] * sc, f1[3] * sc);
     store16((uint16_t*)a.dq + i * 8, o);
   }
 }

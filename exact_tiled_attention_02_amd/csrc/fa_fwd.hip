@@ -507,7 +507,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hk = h / (a.Hq / a.Hkv);
   const size_t q_rs = (size_t)a.Hq * D;
   const size_t k_rs = (size_t)a.Hkv * D;
-  const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
   const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
   const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
 

@@ -90,9 +90,9 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse
               int dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: an fp32 dQ accumulator and an fp32 row
- * statistic (sum_d dO*O) for B*Sq rows of Hq heads (for varlen, B*Sq bounds total_q),
- * plus 256 bytes for the work queue of the main loop.  Returns 0 for invalid sizes.
+ * Bytes of device workspace fa_bwd needs: an fp32 dQ accumulator and two fp32 row
+ * statistics (sum_d dO*O and LSE*log2(e)) for B*Sq rows of Hq heads (for varlen, B*Sq
+ * bounds total_q), plus 256 bytes for the work queue of the main loop.  Returns 0 for invalid sizes.
  * A workspace serves one backward at a time: calls that share one must not overlap.
  */
 size_t fa_bwd_workspace_bytes(int B, int Sq, int Hq, int D);
@@ -144,12 +144,12 @@ int fa_bwd_ex(const void* dout, const void* q, const void* k, const void* v,
 
 /*
  * One stage of fa_bwd, for callers that schedule or time the stages themselves.
- * stage 1: preprocess -- per (row, head) Dsum = sum_d dout*out into the workspace and
- *          zeroing of the workspace's fp32 dQ accumulator (memory-bound);
- * stage 2: main loop -- dk, dv written, dQ (times scale) added into the accumulator
+ * stage 1: preprocess -- per (row, head) Dsum = sum_d dout*out and LSE*log2(e) into the
+ *          workspace, and zeroing of the workspace's fp32 dQ accumulator (memory-bound);
+ * stage 2: main loop -- dk, dv written, dQ / scale added into the accumulator
  *          (its key-block queue is emptied by stage 1 and again at its own end, so it
  *          may be repeated on its own after a complete stage 1 or stage 2);
- * stage 3: finalize -- dq = accumulator converted to the input dtype.
+ * stage 3: finalize -- dq = scale * accumulator, in the input dtype.
  * fa_bwd is stages 1, 2, 3 in this order on one stream; a stage reads what the earlier
  * stages left in the workspace.  Arguments, checks and errors as for fa_bwd; a stage
  * outside 1..3 returns FA_ERR_INVALID_ARGUMENT.
