@@ -820,8 +820,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     phase_barrier();
   };
 
-  wait_all_memory();
-  __syncthreads();
+  // Q and stage 0 have landed (stage 1, issued last, may still be in flight: the wait at
+  // the end of the first M phase covers it), everywhere after the barrier.
+  if (n > 0) {
+    wait_vmcnt<2 * NI>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
   if (grp == 1) phase_barrier();
   using F = std::false_type;
   using T = std::true_type;
@@ -1259,8 +1265,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     phase_barrier();
   };
 
-  wait_all_memory();
-  __syncthreads();
+  // Q and each group's first item have landed, everywhere after the barrier (group 0's
+  // item 2, issued last, may still be in flight: the wait at the end of its first M phase
+  // covers it).
+  if (n > 0 && grp == 0) {
+    wait_vmcnt<2 * NI>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
   if (grp == 1) phase_barrier();
   using F = std::false_type;
   using T = std::true_type;
