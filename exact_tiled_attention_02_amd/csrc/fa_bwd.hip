@@ -11,8 +11,8 @@
 // flash_attn_func docstring); the causal mask is bottom-right aligned as in the forward.
 //
 // Kernels (all on the caller's stream, in order):
-//   1. preprocess: Dsum = rowsum(dO * O) in fp32, LSE * log2(e), and zeroing of the fp32 dQ
-//      accumulator (memory-bound);
+//   1. preprocess: -Dsum = -rowsum(dO * O) in fp32 (the D <= 128 main loop starts dP from
+//      it), LSE * log2(e), and zeroing of the fp32 dQ accumulator (memory-bound);
 //   2. main loop, one workgroup per (key block, KV head, sequence), walking the query
 //      blocks that can see its keys for every query head of the group, so dK and dV
 //      accumulate in registers with no atomics.  Per query step: S = Q K^T, P,
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
   for (int m = CH / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
   if (live && ch == 0) {
-    a.dsum[pair] = s;
+    a.dsum[pair] = -s;  // stored negated: the D <= 128 main loop starts dP from it
     // LSE * log2(e) in the same [row, head] layout (the exp2 offset the main loop needs)
     const size_t row = pair / a.Hq;
     const int h = (int)(pair % a.Hq);
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       if constexpr (ALIBI) bias = fmaf(-sl, fabsf((float)(row + diag - my_key)), bias);
       const float p = keep ? fast_exp2(fmaf(s[r], c, bias)) : 0.f;
       s[r] = p;
-      dp[r] = p * (dp[r] - dsum_s[buf][rl]);  // dS / scale
+      dp[r] = p * (dp[r] + dsum_s[buf][rl]);  // dS / scale (the workspace holds -Dsum)
     }
     Frag8 pf[2], dsf[2];
 #pragma unroll
@@ -549,7 +549,15 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
       const int kw0 = k0 + wave * 32;
       live = !mask || (kw0 <= kw.hi(min(i0 + kK2BQ, Lq) - 1) && kw0 + 31 >= kw.lo(i0));
     }
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // dP starts from -Dsum of the step's rows (register r holds row 8 (r / 4) + 4 lh + r % 4),
+    // so that the products leave dP - Dsum.
+    f32x16 s = f32x16{}, dp;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 d4 = *(const f32x4*)(dsum_c + 8 * g4 + 4 * lh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dp[4 * g4 + j] = d4[j];
+    }
     if (live) {
       // The row reads run SPD k-steps ahead of their products, written out in that order
       // and fenced for the machine scheduler (which would sink each read down to its
@@ -588,7 +596,6 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x4 l4 = *(const f32x4*)(lse_c + 8 * g4 + 4 * lh);
-      const f32x4 d4 = *(const f32x4*)(dsum_c + 8 * g4 + 4 * lh);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g4 + j;
@@ -596,7 +603,7 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
         if constexpr (ALIBI) bias = fmaf(-sl, fabsf(abase + (float)(8 * g4 + j)), bias);
         const float p = fast_exp2(fmaf(s[r], c, bias));
         s[r] = p;
-        dp[r] = p * (dp[r] - d4[j]);  // dS / scale
+        dp[r] = p * dp[r];  // dS / scale = P (dP - Dsum)
       }
     }
     Frag8 pf[2], dsf[2];
@@ -962,7 +969,7 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
           float bias = -lse2;
           if constexpr (ALIBI) bias = fmaf(-sl2, fabsf(abase + (float)(sub * 32 + 8 * (r >> 2) + (r & 3))), bias);
           const float p = fast_exp2(fmaf(s[sub][r], c, bias));
-          s[sub][r] = a.scale * p * (dp[sub][r] - dsum);
+          s[sub][r] = a.scale * p * (dp[sub][r] + dsum);  // the workspace holds -Dsum
         }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {

@@ -144,7 +144,7 @@ int fa_bwd_ex(const void* dout, const void* q, const void* k, const void* v,
 
 /*
  * One stage of fa_bwd, for callers that schedule or time the stages themselves.
- * stage 1: preprocess -- per (row, head) Dsum = sum_d dout*out and LSE*log2(e) into the
+ * stage 1: preprocess -- per (row, head) -Dsum = -sum_d dout*out and LSE*log2(e) into the
  *          workspace, and zeroing of the workspace's fp32 dQ accumulator (memory-bound);
  * stage 2: main loop -- dk, dv written, dQ / scale added into the accumulator
  *          (its key-block queue is emptied by stage 1 and again at its own end, so it
