@@ -537,48 +537,12 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   wait_all_memory();
   __syncthreads();
 
-  // dQ of a step is formed at its end by the wavefronts on duty.  kDefer (D = 64): it is
-  // added to the accumulator at the start of the next step, right after that step's
-  // prefetch, so that the wait for the prefetch leaves these atomics in flight (vmcnt
-  // counts in issue order, and every duty step issues exactly 16 of them) and their latency
-  // overlaps a whole step (5 % faster at D = 64; at D = 128 the 16 registers it keeps live
-  // across the step spill, 4-6 % slower).  Otherwise the atomics go out at once and the
-  // next step's end waits for them.
-  constexpr bool kDefer = D <= 64;
-  f32x16 dq_p;
-  bool dq_pend = false;  // uniform per wavefront
-  int dq_i0 = 0, dq_h = 0;
-  auto dq_atomics = [&]() __attribute__((always_inline)) {
-    const auto dqr = make_rsrc(a.dq_acc + ((size_t)(q_start + dq_i0) * a.Hq + dq_h) * D, 0xffffffffu);
-    const uint32_t rs4 = (uint32_t)a.Hq * D * 4u;  // bytes per row
-    const uint32_t col4 = (uint32_t)((wave % ND) * 32 + li) * 4u;
-    if (__builtin_expect(dq_i0 + kK2BQ <= Lq, 1)) {
-      // The row offset of register r is uniform (scalar offset); the lane's row half and
-      // column form the lane offset.
-      const uint32_t voff = 4u * lh * rs4 + col4;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq_p[r], dqr, (int)voff, (int)((8 * (r >> 2) + (r & 3)) * rs4),
-                                                      0);
-    } else {
-      // Rows past the end of the sequence carry exact zeros (their P is masked to 0); they
-      // go to the last row, so that every lane issues all 16 atomics.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = min(4 * lh + 8 * (r >> 2) + (r & 3), Lq - 1 - dq_i0);
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq_p[r], dqr, (int)((uint32_t)rr * rs4 + col4), 0, 0);
-      }
-    }
-  };
   auto step = [&](int it, int h, int i0, int h_next, int i0_next, bool mask, const uint16_t* __restrict__ Q,
                   const uint16_t* __restrict__ dO, const float* __restrict__ lse_c, const float* __restrict__ dsum_c,
                   uint16_t* __restrict__ Qn, uint16_t* __restrict__ dOn, float* __restrict__ lse_n,
                   float* __restrict__ dsum_n, uint16_t* __restrict__ dSc) {
     const float sl = sl_next;
     if (it + 1 < nsteps) fetch(h_next, i0_next, Qn, dOn, lse_n, dsum_n);
-    if constexpr (DQ && kDefer) {
-      if (dq_pend) dq_atomics();
-    }
 
     bool live = true;  // some key of this wavefront is kept by some row of the step
     if constexpr (MASKED) {
@@ -689,50 +653,7 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
       });
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (DQ && kDefer) {
-      // This wavefront's prefetch of the next step has landed (the atomics issued after it,
-      // if any, may still be in flight).  After the barrier every wavefront's dS is in
-      // dSc, nobody reads this step's Q / dO / LSE / Dsum tiles any more, and the next
-      // step's tiles are in LDS everywhere -- so no second barrier closes the step: the
-      // wavefronts that compute this step's dQ overlap with the others starting the next
-      // step, which writes its dS into the other buffer.
-      if (dq_pend) {
-        wait_vmcnt<16>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      lds_barrier();
-      // dQ[32 rows][d-block] = dS[32 rows][256 keys] K[256 keys][d-block]: groups of ND
-      // wavefronts take turns by step, one d-block per wavefront.
-      dq_pend = wave / ND == it % (kK2Waves / ND);
-      if (dq_pend) {
-        dq_i0 = i0;
-        dq_h = h;
-        bool any = true;
-        if (mask) any = k0 <= kw.hi(min(i0 + kK2BQ, Lq) - 1) && k_last >= kw.lo(i0);
-        dq_p = f32x16{};
-        if (any) {
-          // Operand reads QPD key steps ahead, in fenced order (as for S and dP above).
-          constexpr int QPD = 3, NKS = kK2Keys / 16;
-          Frag8 sa[QPD], kb2[QPD];
-          auto issue = [&](auto ks_tag) __attribute__((always_inline)) {
-            constexpr int ks = decltype(ks_tag)::value, sl = ks % QPD;
-            sa[sl].v = load16(&dSc[li * SSTR + ks * 16 + lh * 8]);
-            const u32x2 lo = lds_read_tr16(Ks + ks * 16 * D + ktr[0]);
-            const u32x2 hi = lds_read_tr16(Ks + ks * 16 * D + ktr[1]);
-            kb2[sl].v = u32x4{lo.x, lo.y, hi.x, hi.y};
-          };
-          static_for<0, QPD>([&](auto ks) __attribute__((always_inline)) { issue(ks); });
-          static_for<0, NKS>([&](auto ks_tag) __attribute__((always_inline)) {
-            constexpr int ks = decltype(ks_tag)::value, sl = ks % QPD;
-            __builtin_amdgcn_sched_barrier(0);
-            dq_p = mfma32x32x16<BF16>(sa[sl], kb2[sl], dq_p);
-            if constexpr (ks + QPD < NKS) issue(Idx<ks + QPD>{});
-          });
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    } else if constexpr (DQ) {
+    if constexpr (DQ) {
       // This wavefront's prefetch of the next step has landed (and the dQ atomics it issued
       // before that prefetch have completed).  After the barrier every wavefront's dS is in
       // dSc, nobody reads this step's Q / dO / LSE / Dsum tiles any more, and the next
@@ -815,9 +736,6 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
       q_n = qb_begin;
       ++h_n;
     }
-  }
-  if constexpr (DQ && kDefer) {
-    if (dq_pend) dq_atomics();  // the last step's dQ
   }
 
   if (key_ok) {
