@@ -101,6 +101,12 @@ def test_workspace_bytes(L):
     assert n >= 2 * 4096 * 16 * 128 * 4 + 2 * 4096 * 16 * 4
     assert n % 256 == 0
     assert L.fa_bwd_workspace_bytes(0, 1, 1, 1) == 0
+    # documented layout: fp32 dQ accumulator, -Dsum and LSE*log2(e) per (row, head), each
+    # 256-byte aligned, then 256 bytes of queue counters
+    al = lambda x: (x + 255) // 256 * 256
+    for B, S, H, D in ((2, 4096, 16, 128), (3, 77, 6, 64), (1, 1, 1, 256)):
+        rows = B * S
+        assert L.fa_bwd_workspace_bytes(B, S, H, D) == al(rows * H * D * 4) + 2 * al(rows * H * 4) + 256
 
 
 def test_python_status_mapping(L):
