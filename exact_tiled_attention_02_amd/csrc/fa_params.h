@@ -37,7 +37,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dq_acc;  // fp32 [rows, Hq, D], rows = B*Sq (padded) or >= total_q (varlen)
-  float* dsum;    // fp32 [rows, Hq]
+  float* dsum;    // fp32 [rows, Hq]: -Dsum = -rowsum(dO * O) (preprocess)
   float* lse2;    // fp32 [rows, Hq]: LSE * log2(e), the exp2 offset of P (preprocess)
   const int32_t* cu_q;
   const int32_t* cu_k;
