@@ -121,6 +121,24 @@ def test_xcd_order_padded(D, causal):
     _full_check(W(f"xcd_padded_d{D}_c{int(causal)}", 2, 16, 4, 520, 520, D, "fp16", causal, seed=22))
 
 
+@pytest.mark.parametrize("D", [128, 256])
+def test_xcd_order_sequence_major_varlen(D):
+    # At least four blocks per CU on every XCD (Hq = 8: one head per XCD), so the XCDs run
+    # their sequences longest first, ranked on the device: equal lengths, an empty sequence
+    # and lengths off the block grid. Non-causal: the order does not depend on the mask, and
+    # rows that see hundreds of keys keep the bf16 bar on the kernel rather than on the
+    # output rounding of rows that see one or two.
+    rng = np.random.default_rng(25)
+    lq = [int(x) for x in rng.integers(700, 1100, 40)]
+    lq[3] = lq[7] = lq[11] = 900  # ties
+    lq[5] = 0
+    _full_check(W(f"xcd_seqmajor_varlen_d{D}", None, 8, 2, None, None, D, "bf16", False, seed=25, lengths=(lq, list(lq))))
+
+
+def test_xcd_order_sequence_major_padded():
+    _full_check(W("xcd_seqmajor_padded", 64, 8, 2, 520, 520, 128, "fp16", False, seed=26))
+
+
 def test_xcd_order_many_sequences():
     # Non-causal with at least 32 keys per sequence: every output row averages many values,
     # so |O| stays far below 2 and the bf16 bar measures the kernel, not the output
