@@ -55,7 +55,7 @@ constexpr int kFwdBN = 64;              // keys per tile
 // order of w within its XCD), and every XCD has an L2 of its own.  When Hq is a multiple
 // of 8, XCD x takes the query heads [x Hq/8, (x+1) Hq/8) of every sequence: an equal
 // share of the work, with the query heads of a KV head kept together.  Within the XCD:
-//   * few blocks (under four per CU): query blocks longest first over all of the XCD's
+//   * few blocks (at most four per CU): query blocks longest first over all of the XCD's
 //     (sequence, head) pairs, which balances the CUs best;
 //   * otherwise sequence by sequence, longest sequence first, the query blocks of a
 //     sequence longest first with the heads of a block adjacent.  The workgroups resident
@@ -63,7 +63,7 @@ constexpr int kFwdBN = 64;              // keys per tile
 //     L2 fetches once for all of them (packed batches of short sequences gain ~25 %).
 // Otherwise (and for more than 64 packed sequences): query blocks longest first over all
 // (sequence, head) pairs of the grid.  Blocks past a packed sequence's end report no work.
-constexpr int kSeqMajorMinBlocks = 4 * 32;  // per XCD: four rounds of its 32 CUs
+constexpr int kQbMajorMaxBlocks = 4 * 32;  // per XCD: four rounds of its 32 CUs
 
 template <int BM, bool VARLEN>
 __device__ __forceinline__ bool fwd_block(const FwdArgs& a, int& b, int& h, int& qb) {
@@ -82,7 +82,7 @@ __device__ __forceinline__ bool fwd_block(const FwdArgs& a, int& b, int& h, int&
       for (int o = 32; o >= 1; o >>= 1) total += __shfl_xor(total, o);
       total = __builtin_amdgcn_readfirstlane(total);  // equal in every lane
     }
-    if (total < kSeqMajorMinBlocks) {
+    if (total <= kQbMajorMaxBlocks) {
       const int per = a.B * hx;
       qb = nqb - 1 - t / per;
       b = (t % per) / hx;
