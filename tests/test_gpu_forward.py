@@ -121,7 +121,7 @@ def test_xcd_order_padded(D, causal):
     _full_check(W(f"xcd_padded_d{D}_c{int(causal)}", 2, 16, 4, 520, 520, D, "fp16", causal, seed=22))
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_xcd_order_sequence_major_varlen(D):
     # At least four blocks per CU on every XCD (Hq = 8: one head per XCD), so the XCDs run
     # their sequences longest first, ranked on the device: equal lengths, an empty sequence
@@ -137,6 +137,13 @@ def test_xcd_order_sequence_major_varlen(D):
 
 def test_xcd_order_sequence_major_padded():
     _full_check(W("xcd_seqmajor_padded", 64, 8, 2, 520, 520, 128, "fp16", False, seed=26))
+
+
+def test_xcd_order_sequence_major_boundary():
+    # 15 sequences x 9 query blocks = 135 blocks per XCD, just past four per CU: the first
+    # shape that runs sequence-major. Causal with Sk = 2 Sq (bottom-right aligned), so each
+    # row sees more than 1,100 keys.
+    _full_check(W("xcd_seqmajor_boundary", 15, 8, 2, 1100, 2200, 64, "fp16", True, seed=27))
 
 
 def test_xcd_order_many_sequences():
