@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "fa_params.h"
@@ -85,6 +86,30 @@ int hip_status(hipError_t e, const char* what) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// FA_DEBUG_CHECKS=1 in the environment turns on the device-side argument checks.
+bool debug_checks_on() {
+  const char* e = std::getenv("FA_DEBUG_CHECKS");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
+// With the checks on: the device flag every kernel of the call reads, after launching the
+// check of the varlen offsets (when given).  Returns FA_OK (flag null when checks are off)
+// or an error status.
+int debug_setup(const int32_t* cu_q, const int32_t* cu_k, int B, int Sq, int Sk, hipStream_t stream,
+                const int** flag_out) {
+  *flag_out = nullptr;
+  if (!debug_checks_on()) return FA_OK;
+  int* flag = nullptr;
+  int st = hip_status(fa::debug_flag(&flag), "FA_DEBUG_CHECKS flag");
+  if (st != FA_OK) return st;
+  if (cu_q != nullptr) {
+    st = hip_status(fa::launch_check_varlen(cu_q, cu_k, B, Sq, Sk, flag, stream), "FA_DEBUG_CHECKS launch");
+    if (st != FA_OK) return st;
+  }
+  *flag_out = flag;
+  return FA_OK;
+}
+
 // Factor applied to raw scores before exp2: scale * log2(e), but at least 1e-30 so that
 // it is strictly positive.  The kernels then mask a score by setting it to -inf
 // (exp2(-inf * c) = 0 needs c > 0).  For scale = 0 the clamp changes nothing: every
@@ -112,6 +137,32 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
+int fa_debug_status(hipStream_t stream) {
+  g_last_error.clear();
+  int* flag = nullptr;
+  int st = hip_status(fa::debug_flag(&flag), "FA_DEBUG_CHECKS flag");
+  if (st != FA_OK) return st;
+  int code = 0;
+  if ((st = hip_status(hipMemcpyAsync(&code, flag, sizeof code, hipMemcpyDeviceToHost, stream), "read flag")) ||
+      (st = hip_status(hipStreamSynchronize(stream), "synchronise")))
+    return st;
+  if (code == 0) return FA_OK;
+  const int zero = 0;
+  if ((st = hip_status(hipMemcpyAsync(flag, &zero, sizeof zero, hipMemcpyHostToDevice, stream), "clear flag")) ||
+      (st = hip_status(hipStreamSynchronize(stream), "synchronise")))
+    return st;
+  std::string msg = "device-side argument check failed (code " + std::to_string(code) + "):";
+  if (code & fa::kDbgSeqlensStart) msg += " cu_seqlens does not start at 0;";
+  if (code & fa::kDbgSeqlensOrder) msg += " cu_seqlens decreases;";
+  if (code & fa::kDbgSeqlensQ) msg += " a query sequence is longer than max_seqlen_q;";
+  if (code & fa::kDbgSeqlensK) msg += " a key sequence is longer than max_seqlen_k;";
+  if (code & fa::kDbgCacheSeqlens) msg += " cache_seqlens outside [0, capacity];";
+  if (code & fa::kDbgCacheIndex) msg += " cache_batch_idx outside the cache;";
+  if (code & fa::kDbgBlockTable) msg += " a block-table entry outside the block pool;";
+  g_last_error = msg;
+  return FA_ERR_INVALID_ARGUMENT;
+}
+
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Sq, int Sk, int Hq,
               int Hkv, int D, float scale, int causal, int window_left, int window_right, const float* alibi_slopes,
               int alibi_batch_stride, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
@@ -124,6 +175,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse
       (st = check_ptr(out, "out")) || (st = check_ptr(lse, "lse")))
     return st;
   fa::FwdArgs a{};
+  if ((st = debug_setup(cu_seqlens_q, cu_seqlens_k, B, Sq, Sk, stream, &a.dbg))) return st;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -185,6 +237,7 @@ int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, con
     return fail(FA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)", need,
                 workspace_bytes, workspace);
   fa::BwdArgs a{};
+  if ((st = debug_setup(cu_seqlens_q, cu_seqlens_k, B, Sq, Sk, stream, &a.dbg))) return st;
   a.dout = dout;
   a.q = q;
   a.k = k;
@@ -369,6 +422,13 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
     return fail(FA_ERR_WORKSPACE, "%d splits need %zu bytes of workspace, 16-byte aligned (got %zu at %p)",
                 num_splits, need, workspace_bytes, workspace);
   fa::DecodeArgs a{};
+  if ((st = debug_setup(nullptr, nullptr, B, Sq, cap, stream, &a.dbg))) return st;
+  if (a.dbg != nullptr && (cache_seqlens || cache_batch_idx || block_table)) {
+    st = hip_status(fa::launch_check_kvcache(cache_seqlens, cache_batch_idx, block_table, B, cache_batch, cap, page,
+                                             paged ? max_blocks_per_seq : 0, const_cast<int*>(a.dbg), stream),
+                    "FA_DEBUG_CHECKS launch");
+    if (st != FA_OK) return st;
+  }
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;

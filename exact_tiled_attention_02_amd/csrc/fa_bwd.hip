@@ -48,14 +48,15 @@ constexpr int kBwdBQ = 32;              // query rows per inner step
 
 template <int D, bool BF16, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
+  if (debug_stop(a.dbg)) return;
   constexpr int CH = D / 8;              // 16-byte chunks per (row, head)
   constexpr int PAIRS = 256 / CH;        // (row, head) pairs per workgroup
   const int tid = threadIdx.x;
   const int pair_local = tid / CH;
   const int ch = tid % CH;
   const size_t pair = (size_t)blockIdx.x * PAIRS + pair_local;
-  size_t rows = (size_t)a.B * a.Sq;
-  if constexpr (VARLEN) rows = (size_t)load_uniform(a.cu_q + a.B);
+  size_t rows = (size_t)a.B * a.Sq;  // the workspace's rows (a bound on total_q)
+  if constexpr (VARLEN) rows = min(rows, (size_t)max(load_uniform(a.cu_q + a.B), 0));
   const bool live = pair < rows * a.Hq;
   float s = 0.f;
   if (live) {
@@ -99,6 +100,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool DQ, bool ALIBI>
 __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
+  if (debug_stop(a.dbg)) return;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
   constexpr int SSTR = kBwdBN + 8;  // dS tile [query row][key], padded
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = i0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < Lq) {
+        if (row < Lq && (size_t)(q_start + row) < (size_t)a.B * a.Sq) {  // inside the accumulator
           float* dst = a.dq_acc + ((size_t)(q_start + row) * a.Hq + h) * D + d * 32 + li;
           unsafeAtomicAdd(dst, dq[r]);
         }
@@ -450,6 +452,13 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   const int nsteps = G * nqs;
   float sl_next = 0.f;  // ALiBi slope (exp2 units) of the step fetched last
 
+  // Extents of the arrays the buffer resources below address: q / dout hold total_q rows
+  // (B * Sq when padded), the workspace arrays B * Sq rows (a bound on total_q).  Every
+  // lane offset stays inside them for valid cu_seqlens; with invalid ones the hardware
+  // range check drops what falls outside instead of touching other memory.
+  const size_t q_rows = VARLEN ? (size_t)load_uniform(a.cu_q + a.B) : (size_t)a.B * a.Sq;
+  const size_t ws_rows = (size_t)a.B * a.Sq;
+
   // Q / dO tile: QT/8 chunks, one direct load per lane for D = 128 (half the lanes
   // for D = 64).
   constexpr int QCH = QT / 8;
@@ -464,22 +473,21 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
                    float* __restrict__ dsumd) {
     // Buffer-form direct loads from the step's first row (the flat form would make the
     // compiler wait for every LDS read with lgkmcnt(0)).  The lane offsets address clamped
-    // rows only, so the resources need no range.
+    // rows of the sequence.
     const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * D;
     if (qloader) {
       uint32_t off = qoff;
       if (i0 + kK2BQ > Lq)
         off = (uint32_t)(min(qr, Lq - 1 - i0) * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8) * 2u;
-      lds_buffer_load16(make_rsrc((const uint16_t*)a.q + base, 0xffffffffu), off, Qd + wave * 64 * 8);
-      lds_buffer_load16(make_rsrc((const uint16_t*)a.dout + base, 0xffffffffu), off, dOd + wave * 64 * 8);
+      const uint32_t qbytes = bytes_left(q_rows * q_rs, base, 2u);
+      lds_buffer_load16(make_rsrc((const uint16_t*)a.q + base, qbytes), off, Qd + wave * 64 * 8);
+      lds_buffer_load16(make_rsrc((const uint16_t*)a.dout + base, qbytes), off, dOd + wave * 64 * 8);
     }
     const uint32_t rr = (uint32_t)min(lane & 31, Lq - 1 - i0);
-    if (wave == kK2Waves - 1)
-      lds_buffer_load4(make_rsrc(a.lse2 + (size_t)(q_start + i0) * a.Hq + h, 0xffffffffu), rr * (uint32_t)a.Hq * 4u,
-                       lsed);
-    if (wave == kK2Waves - 2)
-      lds_buffer_load4(make_rsrc(a.dsum + (size_t)(q_start + i0) * a.Hq + h, 0xffffffffu), rr * (uint32_t)a.Hq * 4u,
-                       dsumd);
+    const size_t sbase = (size_t)(q_start + i0) * a.Hq + h;
+    const uint32_t sbytes = bytes_left(ws_rows * a.Hq, sbase, 4u);
+    if (wave == kK2Waves - 1) lds_buffer_load4(make_rsrc(a.lse2 + sbase, sbytes), rr * (uint32_t)a.Hq * 4u, lsed);
+    if (wave == kK2Waves - 2) lds_buffer_load4(make_rsrc(a.dsum + sbase, sbytes), rr * (uint32_t)a.Hq * 4u, dsumd);
     // Issued before the step's dQ atomics, so the end-of-step vmcnt wait covers it too.
     if constexpr (ALIBI) sl_next = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
   };
@@ -690,10 +698,15 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
           __builtin_amdgcn_sched_barrier(0);
           // Buffer atomics from the step's first row: the row offset of register r is
           // uniform (scalar offset), the lane's row half and column form the lane offset.
-          const auto dqr = make_rsrc(a.dq_acc + ((size_t)(q_start + i0) * a.Hq + h) * D, 0xffffffffu);
+          // The resource spans the rest of the accumulator, and rows past its B * Sq rows
+          // (possible only with invalid cu_seqlens) are skipped: the scalar offset is not
+          // range-checked by the hardware.
+          const size_t acc0 = ((size_t)(q_start + i0) * a.Hq + h) * D;
+          const auto dqr = make_rsrc(a.dq_acc + acc0, bytes_left(ws_rows * a.Hq * D, acc0, 4u));
           const uint32_t rs4 = (uint32_t)a.Hq * D * 4u;  // bytes per row
           const uint32_t voff = 4u * lh * rs4 + (uint32_t)(dblk * 32 + li) * 4u;
-          if (__builtin_expect(i0 + kK2BQ <= Lq, 1)) {
+          const int lim = (int)min((size_t)Lq, ws_rows - min(ws_rows, (size_t)q_start));  // rows < lim are stored
+          if (__builtin_expect(i0 + kK2BQ <= lim, 1)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[r], dqr, (int)voff, (int)((8 * (r >> 2) + (r & 3)) * rs4),
@@ -702,7 +715,7 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int rr = 8 * (r >> 2) + (r & 3);
-              if (i0 + 4 * lh + rr < Lq)
+              if (i0 + 4 * lh + rr < lim)
                 __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[r], dqr, (int)voff, (int)(rr * rs4), 0);
             }
           }
@@ -768,6 +781,7 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
 // again, so a main loop launched on its own (after a complete one) finds it empty too.
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool DQ, bool ALIBI>
 __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
+  if (debug_stop(a.dbg)) return;
   __shared__ int next;
   const int nblocks = (a.Sk + kK2Keys - 1) / kK2Keys * a.B * a.Hkv;
   for (;;) {
@@ -803,6 +817,7 @@ constexpr int kDqBN = 64;
 
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
+  if (debug_stop(a.dbg)) return;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
   constexpr int TILE = kDqBN * D;
@@ -1021,9 +1036,10 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
 
 template <bool BF16, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+  if (debug_stop(a.dbg)) return;
   // 8 elements per thread
-  size_t rows = (size_t)a.B * a.Sq;
-  if constexpr (VARLEN) rows = (size_t)load_uniform(a.cu_q + a.B);
+  size_t rows = (size_t)a.B * a.Sq;  // the workspace's rows (a bound on total_q)
+  if constexpr (VARLEN) rows = min(rows, (size_t)max(load_uniform(a.cu_q + a.B), 0));
   const size_t n8 = rows * a.Hq * a.D / 8;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
     const u32x4 x0 = load16(a.dq_acc + i * 8);

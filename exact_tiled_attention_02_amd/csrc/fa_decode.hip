@@ -57,6 +57,7 @@ __device__ __forceinline__ KeyRange kept_keys(int s, int Lk, int Sq, int causal,
 
 template <int D, bool BF16, bool PAGED, bool ALIBI>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
+  if (debug_stop(a.dbg)) return;
   constexpr int STAGES = decode_stages(D);
   constexpr int NS = D / 16;            // 16-wide slices of the head dimension
   constexpr int ND = D / 32;            // 32-wide output blocks
@@ -378,6 +379,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Merge of the split partials: one wavefront per output row (b, s, h).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  if (debug_stop(a.dbg)) return;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int nrows = a.B * a.Sq * a.Hq;

@@ -79,6 +79,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the value sit in vector registers and every buffer access becomes a loop over lanes.
 __device__ __forceinline__ int load_uniform(const int32_t* p) { return __builtin_amdgcn_readfirstlane(*p); }
 
+// True when the device-side argument checks (FA_DEBUG_CHECKS=1) have flagged an error
+// earlier on the stream: the kernel then returns before doing anything.  `flag` is null
+// when the checks are off.
+__device__ __forceinline__ bool debug_stop(const int* flag) {
+  return flag != nullptr && __builtin_amdgcn_readfirstlane(*flag) != 0;
+}
+
 // 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): lane l of the
 // wavefront writes lds_base + 16*l.  lds_base must be the same in every lane.
 __device__ __forceinline__ void lds_direct_load16(const void* gptr, void* lds_base) {
@@ -90,6 +97,14 @@ __device__ __forceinline__ void lds_direct_load16(const void* gptr, void* lds_ba
 // be formed.
 __device__ __forceinline__ void lds_direct_load16(const void* base, uint32_t byte_off, void* lds_base) {
   lds_direct_load16((const char*)base + byte_off, lds_base);
+}
+
+// Bytes from element `first` to the end of an array of `total` elements of `esize` bytes,
+// clamped to the 32-bit extent of a buffer resource (0 when `first` is past the end).
+__device__ __forceinline__ uint32_t bytes_left(size_t total, size_t first, uint32_t esize) {
+  if (first >= total) return 0u;
+  const size_t b = (total - first) * esize;
+  return b < 0xffffffffu ? (uint32_t)b : 0xffffffffu;
 }
 
 // Buffer resource for raw (unstructured) buffer loads over [base, base + bytes): offsets

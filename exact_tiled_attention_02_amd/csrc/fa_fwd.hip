@@ -123,6 +123,7 @@ __device__ __forceinline__ bool fwd_block(const FwdArgs& a, int& b, int& h, int&
 
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+  if (debug_stop(a.dbg)) return;
   constexpr int NS = D / 16;  // 16-wide slices of the head dimension (QK^T depth)
   constexpr int ND = D / 32;  // 32-wide blocks of the head dimension (output tiles)
   constexpr int TILE = kFwdBN * D;  // elements per K or V tile
@@ -465,6 +466,7 @@ constexpr int kPPBN = 64;             // keys per tile
 
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(FwdArgs a) {
+  if (debug_stop(a.dbg)) return;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
   constexpr int TILE = kPPBN * D;
@@ -945,6 +947,7 @@ constexpr int kKPBN = 32;                   // keys per tile
 
 template <bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kp_kernel(FwdArgs a) {
+  if (debug_stop(a.dbg)) return;
   constexpr int D = 256;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;

@@ -7,7 +7,17 @@
 
 namespace fa {
 
+// Codes of the device-side argument checks (FA_DEBUG_CHECKS=1), OR-ed into the flag.
+constexpr int kDbgSeqlensStart = 1;   // cu_seqlens_q[0] or cu_seqlens_k[0] is not 0
+constexpr int kDbgSeqlensOrder = 2;   // cu_seqlens decreases somewhere
+constexpr int kDbgSeqlensQ = 4;       // a query sequence is longer than max_seqlen_q (Sq)
+constexpr int kDbgSeqlensK = 8;       // a key sequence is longer than max_seqlen_k (Sk)
+constexpr int kDbgCacheSeqlens = 16;  // cache_seqlens outside [0, capacity]
+constexpr int kDbgCacheIndex = 32;    // cache_batch_idx outside [0, cache_batch)
+constexpr int kDbgBlockTable = 64;    // a block-table entry outside [0, num_blocks)
+
 struct FwdArgs {
+  const int* dbg;  // device flag of the argument checks (null: checks off); set = do nothing
   const void* q;
   const void* k;
   const void* v;
@@ -27,6 +37,7 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
+  const int* dbg;  // as in FwdArgs
   const void* dout;
   const void* q;
   const void* k;
@@ -56,6 +67,7 @@ struct BwdArgs {
 
 // Decode against a read-only KV cache (few query rows, long cache), split over the keys.
 struct DecodeArgs {
+  const int* dbg;       // as in FwdArgs
   const void* q;        // [B, Sq, Hq, D]
   const void* k;        // cache: [cache_batch, cap, Hkv, D], or pages [num_blocks, page, Hkv, D]
   const void* v;
@@ -79,6 +91,15 @@ struct DecodeArgs {
   int chunk_tiles;        // 32-key tiles per split; splits * chunk_tiles covers every range
   int row_groups;         // ceil(Sq * Hq / Hkv / 32)
 };
+
+// Device address of this device's argument-check flag (created on first use).
+hipError_t debug_flag(int** out);
+// One-workgroup check kernels (FA_DEBUG_CHECKS=1): OR a kDbg* code into *flag.
+hipError_t launch_check_varlen(const int32_t* cu_q, const int32_t* cu_k, int B, int Sq, int Sk, int* flag,
+                               hipStream_t stream);
+hipError_t launch_check_kvcache(const int32_t* cache_seqlens, const int32_t* batch_idx, const int32_t* block_table,
+                                int B, int cache_batch, int cap, int page, int max_blocks, int* flag,
+                                hipStream_t stream);
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

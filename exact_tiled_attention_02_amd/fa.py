@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
+        L.fa_debug_status.argtypes = [vp]
+        L.fa_debug_status.restype = i
         _lib = L
     return _lib
 
@@ -74,6 +76,12 @@ def check(status: int) -> None:
     raise RuntimeError(msg)
 
 
+def fa_debug_status(stream=None) -> None:
+    """Report the device-side argument checks that FA_DEBUG_CHECKS=1 enables: synchronises
+    ``stream`` and raises ValueError naming the failed checks (and clears them), if any."""
+    check(lib().fa_debug_status(_stream(stream)))
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -81,6 +89,13 @@ def _ptr(t):
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _expect(t, shape, name):
+    """The C ABI cannot see tensor sizes: every tensor's shape is checked here, before a
+    pointer reaches a kernel that would read or write past its end."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k):
@@ -91,13 +106,15 @@ def _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k):
             raise ValueError("padded q/k/v are (batch, seqlen, heads, headdim)")
         B, Sq, Hq, D = q.shape
         Sk, Hkv = k.shape[1], k.shape[2]
+        if k.shape[0] != B or k.shape[3] != D:
+            raise ValueError(f"k has shape {tuple(k.shape)}: batch and head dimension must match q {tuple(q.shape)}")
     else:
         if q.dim() != 3 or k.dim() != 3:
             raise ValueError("varlen q/k/v are (total, heads, headdim)")
         if max_seqlen_q is None or max_seqlen_k is None:
             raise ValueError("varlen calls need max_seqlen_q and max_seqlen_k")
         for c in (cu_seqlens_q, cu_seqlens_k):
-            if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous() or not c.is_cuda:
+            if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
                 raise ValueError("cu_seqlens must be contiguous 1-D int32 GPU tensors")
         B = cu_seqlens_q.numel() - 1
         if cu_seqlens_k.numel() != B + 1:
@@ -105,6 +122,14 @@ def _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k):
         Sq, Sk = int(max_seqlen_q), int(max_seqlen_k)
         Hq, D = q.shape[1], q.shape[2]
         Hkv = k.shape[1]
+        if k.shape[2] != D:
+            raise ValueError(f"k has shape {tuple(k.shape)}: head dimension must match q {tuple(q.shape)}")
+        # Each sequence is at most max_seqlen long, so B * max_seqlen bounds the packed rows
+        # the kernels may address; more rows than that cannot be covered by the launch.
+        if q.shape[0] > B * Sq or k.shape[0] > B * Sk:
+            raise ValueError("packed q/k hold more rows than batch * max_seqlen")
+    if q.device != k.device:
+        raise ValueError("q and k live on different devices")
     return B, Sq, Sk, Hq, Hkv, D
 
 
@@ -120,6 +145,25 @@ def _dtype(*ts):
         if not t.is_cuda:
             raise ValueError("tensors must live in GPU memory")
     return _DTYPE_CODE[d]
+
+
+def _same_device(q, *ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or t.device != q.device):
+            raise ValueError(f"a tensor lives on {t.device}, q on {q.device}")
+
+
+def _check_shapes(q, k, lse, cu_seqlens_q, **like):
+    """v and dk/dv must have k's shape; out, dout and dq q's; lse the shape lse_shape()
+    gives; every tensor on q's device."""
+    _expect(lse, lse_shape(q, cu_seqlens_q), "lse")
+    for name, t in like.items():
+        _expect(t, k.shape if name in ("v", "dk", "dv") else q.shape, name)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    for name, t in list(like.items()) + [("lse", lse)]:
+        if t.device != q.device:
+            raise ValueError(f"{name} lives on {t.device}, q on {q.device}")
 
 
 def _alibi_stride(alibi_slopes, B, Hq):
@@ -146,9 +190,9 @@ def fa_fwd(q, k, v, out, lse, causal: bool = False, scale: float | None = None, 
     ``window_size`` = (left, right) sliding window (-1: unbounded); ``alibi_slopes`` fp32
     (Hq,) or (B, Hq).  Without either this is the C ``fa_fwd``, else ``fa_fwd_ex``."""
     B, Sq, Sk, Hq, Hkv, D = _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    _check_shapes(q, k, lse, cu_seqlens_q, v=v, out=out)
     dt = _dtype(q, k, v, out)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    _same_device(q, cu_seqlens_q, cu_seqlens_k, alibi_slopes)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if _plain(window_size, alibi_slopes):
@@ -182,11 +226,11 @@ def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: bool = False,
 def _bwd_args(dout, q, k, v, out, lse, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
               max_seqlen_k):
     B, Sq, Sk, Hq, Hkv, D = _geometry(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    _check_shapes(q, k, lse, cu_seqlens_q, v=v, out=out, dout=dout, dq=dq, dk=dk, dv=dv)
     dt = _dtype(q, k, v, out, dout, dq, dk, dv)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous float32 GPU tensor")
-    if not workspace.is_cuda:
-        raise ValueError("workspace must live in GPU memory")
+    _same_device(q, cu_seqlens_q, cu_seqlens_k)
+    if not workspace.is_cuda or workspace.device != q.device:
+        raise ValueError("workspace must live in GPU memory on q's device")
     return B, Sq, Sk, Hq, Hkv, D, dt
 
 
@@ -331,11 +375,16 @@ def fa_fwd_kvcache(q, k_cache, v_cache, out, lse, cache_seqlens=None, cache_batc
     tensors or None.  ``alibi_slopes``: fp32 (Hq,) or (B, Hq).  With more than one split
     ``workspace`` (uint8 GPU tensor) must hold fa_fwd_kvcache_workspace_bytes(...)."""
     B, Sq, Hq, Hkv, D, cache_batch, cache_seqlen, max_blocks = _kvcache_geometry(q, k_cache, block_table)
-    dt = _dtype(q, k_cache, v_cache, out)
     if tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("k_cache and v_cache differ in shape")
+    _expect(out, q.shape, "out")
+    _expect(lse, (B, Hq, Sq), "lse")
+    dt = _dtype(q, k_cache, v_cache, out)
     if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
         raise ValueError("lse must be a contiguous float32 GPU tensor")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("lse", lse)):
+        if t.device != q.device:
+            raise ValueError(f"{name} lives on {t.device}, q on {q.device}")
     _int32_vec(cache_seqlens, B, "cache_seqlens")
     _int32_vec(cache_batch_idx, B, "cache_batch_idx")
     stride = _alibi_stride(alibi_slopes, B, Hq)

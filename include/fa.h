@@ -31,13 +31,23 @@
  *   D: 64, 128 or 256.
  *
  * Ownership: the caller owns every buffer; the library allocates no device memory and
- * keeps no mutable global state except a thread-local last-error message.
+ * keeps no mutable global state except a thread-local last-error message and, on each
+ * device, the 4-byte flag of the device-side checks described next (a static device
+ * variable of the library, zero unless FA_DEBUG_CHECKS=1 found an error).
  *
  * Errors: arguments are checked on the host before anything is launched; on error the
  * call returns a non-zero fa_status and writes nothing.  Work is enqueued on `stream`
  * (NULL = the default stream) and runs asynchronously; device faults surface at the
  * caller's next synchronisation.  No call synchronises the host or allocates memory,
  * so all of them may be captured into a HIP graph.
+ *
+ * Device-side preconditions -- values the host cannot read without a synchronisation:
+ * cu_seqlens_q / cu_seqlens_k start at 0, never decrease, and no sequence is longer than
+ * Sq / Sk (so total_q <= B * Sq, the rows a backward workspace holds); the indices,
+ * lengths and block-table entries of fa_fwd_kvcache address existing cache entries.  They
+ * are the caller's contract.  With FA_DEBUG_CHECKS=1 in the environment every call that
+ * depends on them first checks them on the device, and if one fails every kernel on that
+ * device does nothing until fa_debug_status() reports the failure (see there).
  */
 #ifndef FA_H_
 #define FA_H_
@@ -99,8 +109,14 @@ size_t fa_bwd_workspace_bytes(int B, int Sq, int Hq, int D);
 
 /*
  * Backward: given dout = dL/dO and the forward's own out and lse, writes
- * dq = dL/dQ, dk = dL/dK, dv = dL/dV (input dtype).  For GQA, dk/dv of a KV head sum
- * over its query heads.  The probabilities are recomputed from lse (no score matrix is
+ * dq = dL/dQ, dk = dL/dK, dv = dL/dV (input dtype).  The method is the recompute-from-LSE
+ * backward of the release notes "v1.4 - FlashAttention Fork" (section 4.1: the stored LSE,
+ * times log2(e), is the exp2 offset that recovers P = exp(scale * q.k - LSE) tile by tile)
+ * with the gradient of the definition above: dV = P^T dO, dP = dO V^T, Dsum_i =
+ * sum_d dO_id O_id, dS = P * (dP - Dsum), dQ = scale dS K, dK = scale dS^T Q; the
+ * kernels-community/flash-attn2 repository card ("Low-level ops") describes the same
+ * split: a forward that returns (out, LSE) and a backward the caller drives with them.
+ * For GQA, dk/dv of a KV head sum over its query heads.  The probabilities are recomputed from lse (no score matrix is
  * stored).  Other arguments as for fa_fwd.  `workspace` (16-byte aligned) must hold
  * fa_bwd_workspace_bytes(B, Sq, Hq, D) bytes; its contents on entry do not matter.
  * dq, dk, dv are fully overwritten (rows beyond a varlen sequence are not touched).
@@ -219,6 +235,17 @@ int fa_fwd_kvcache_num_splits(int B, int Sq, int Hq, int Hkv, int D, int seqlen_
 
 /* Workspace bytes fa_fwd_kvcache needs for num_splits splits (0 when num_splits <= 1). */
 size_t fa_fwd_kvcache_workspace_bytes(int B, int Sq, int Hq, int D, int num_splits);
+
+/*
+ * Result of the device-side argument checks (FA_DEBUG_CHECKS=1) on the current device:
+ * synchronises `stream`, then returns FA_OK if no check has failed since the last report,
+ * else FA_ERR_INVALID_ARGUMENT with fa_last_error() naming the failed checks, and clears
+ * the flag.  While the flag is set every kernel of the library on that device returns at
+ * once without writing its outputs.  Without FA_DEBUG_CHECKS=1 no check runs and this
+ * returns FA_OK.  Unlike the other calls this one synchronises the host, so it cannot be
+ * captured into a HIP graph.
+ */
+int fa_debug_status(hipStream_t stream);
 
 /* Static description of a status code. */
 const char* fa_status_string(int status);

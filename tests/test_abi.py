@@ -239,3 +239,74 @@ def test_fwd_ex_rejects(L, over, status):
                          ids=lambda x: str(x))
 def test_bwd_ex_rejects(L, over, status):
     assert _bwd_ex(L, **over) == status
+
+
+# ---------------------------------------------------------------------------- binding shape checks
+# The C ABI sees only pointers, so the binding checks every tensor's shape before a call;
+# these errors come before any device check, so host tensors exercise them.
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+def _fwd_tensors(B=2, Sq=8, Sk=12, Hq=4, Hkv=2, D=64):
+    import torch
+    q, k, v = _t(B, Sq, Hq, D), _t(B, Sk, Hkv, D), _t(B, Sk, Hkv, D)
+    return dict(q=q, k=k, v=v, out=_t(B, Sq, Hq, D), lse=torch.zeros(B, Hq, Sq))
+
+
+@pytest.mark.parametrize("bad", ["k_batch", "k_dim", "v", "out", "lse"])
+def test_binding_forward_shapes(bad):
+    import torch
+    t = _fwd_tensors()
+    if bad == "k_batch":
+        t["k"] = t["v"] = _t(3, 12, 2, 64)
+    elif bad == "k_dim":
+        t["k"] = t["v"] = _t(2, 12, 2, 32)
+    elif bad == "v":
+        t["v"] = _t(2, 13, 2, 64)
+    elif bad == "out":
+        t["out"] = _t(2, 8, 4, 32)
+    else:
+        t["lse"] = torch.zeros(2, 8, 4)  # (B, Sq, Hq) instead of (B, Hq, Sq)
+    with pytest.raises(ValueError, match="shape"):
+        fa.fa_fwd(t["q"], t["k"], t["v"], t["out"], t["lse"], causal=True)
+
+
+@pytest.mark.parametrize("bad", ["dout", "dq", "dk", "dv", "lse"])
+def test_binding_backward_shapes(bad):
+    import torch
+    t = _fwd_tensors()
+    g = dict(dout=_t(2, 8, 4, 64), dq=_t(2, 8, 4, 64), dk=_t(2, 12, 2, 64), dv=_t(2, 12, 2, 64))
+    if bad == "lse":
+        t["lse"] = torch.zeros(2, 4, 9)
+    else:
+        g[bad] = _t(2, 8, 2, 64) if bad in ("dout", "dq") else _t(2, 8, 2, 64)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="shape"):
+        fa.fa_bwd(g["dout"], t["q"], t["k"], t["v"], t["out"], t["lse"], g["dq"], g["dk"], g["dv"], ws, causal=True)
+
+
+def test_binding_varlen_shapes():
+    import torch
+    q, k = _t(20, 4, 64), _t(30, 2, 64)
+    cu = torch.tensor([0, 10, 20], dtype=torch.int32)
+    cuk = torch.tensor([0, 15, 30], dtype=torch.int32)
+    lse = torch.zeros(4, 20)
+    kw = dict(cu_seqlens_q=cu, cu_seqlens_k=cuk, max_seqlen_q=10, max_seqlen_k=15)
+    with pytest.raises(ValueError, match="shape"):   # lse is (Hq, total_q)
+        fa.fa_fwd(q, k, k.clone(), q.clone(), torch.zeros(20, 4), **kw)
+    with pytest.raises(ValueError, match="head dimension"):
+        fa.fa_fwd(q, _t(30, 2, 32), _t(30, 2, 32), q.clone(), lse, **kw)
+    with pytest.raises(ValueError, match="more rows"):  # 20 packed rows > 2 sequences of at most 8
+        fa.fa_fwd(q, k, k.clone(), q.clone(), lse, **dict(kw, max_seqlen_q=8))
+
+
+def test_binding_kvcache_shapes():
+    import torch
+    q, kc = _t(2, 1, 8, 64), _t(2, 256, 2, 64)
+    with pytest.raises(ValueError, match="shape"):
+        fa.fa_fwd_kvcache(q, kc, kc.clone(), _t(2, 1, 8, 32), torch.zeros(2, 8, 1))
+    with pytest.raises(ValueError, match="shape"):
+        fa.fa_fwd_kvcache(q, kc, kc.clone(), _t(2, 1, 8, 64), torch.zeros(2, 1, 8))
