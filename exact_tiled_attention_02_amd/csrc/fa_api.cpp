@@ -368,11 +368,18 @@ size_t fa_fwd_kvcache_workspace_bytes(int B, int Sq, int Hq, int D, int num_spli
   return ((rows * D * sizeof(float) + 255) & ~(size_t)255) + ((rows * sizeof(float) + 255) & ~(size_t)255);
 }
 
-int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse, int B, int Sq,
-                   int Hq, int Hkv, int D, int cache_batch, int cache_seqlen, const int32_t* cache_seqlens,
-                   const int32_t* cache_batch_idx, const int32_t* block_table, int max_blocks_per_seq, float scale,
-                   int causal, int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride,
-                   int num_splits, int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_fwd_kvcache; with noalloc the split partials go to the library's static scratch
+// array instead of `workspace` (fa_fwd_kvcache_noalloc).
+int kvcache_impl(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse, int B, int Sq,
+                 int Hq, int Hkv, int D, int cache_batch, int cache_seqlen, const int32_t* cache_seqlens,
+                 const int32_t* cache_batch_idx, const int32_t* block_table, int max_blocks_per_seq, float scale,
+                 int causal, int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride,
+                 int num_splits, int dtype, void* workspace, size_t workspace_bytes, bool noalloc,
+                 hipStream_t stream) {
   g_last_error.clear();
   const bool paged = block_table != nullptr;
   const long long cap_ll = paged ? (long long)max_blocks_per_seq * cache_seqlen : (long long)cache_seqlen;
@@ -410,14 +417,29 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
   const int span = decode_span_tiles(cap, Sq, causal, window_left, window_right);
   // With a window the span (and so the heuristic count) can only shrink, so a workspace
   // sized by fa_fwd_kvcache_num_splits is always large enough.
-  if (num_splits == 0)
+  const int min_splits = paged ? decode_min_splits(span, page) : 1;
+  if (num_splits == 0) {
     num_splits = decode_splits_heuristic((long long)B * Hkv * decode_row_groups(Sq, Hq, Hkv), span, page);
-  if (paged && num_splits < decode_min_splits(span, page))
+    // Without a workspace: as many splits as the scratch array holds (one split needs none).
+    if (noalloc)
+      while (num_splits > min_splits &&
+             fa_fwd_kvcache_workspace_bytes(B, Sq, Hq, D, num_splits) > FA_KVCACHE_NOALLOC_MAX_BYTES)
+        --num_splits;
+  }
+  if (paged && num_splits < min_splits)
     return fail(FA_ERR_INVALID_ARGUMENT, "a paged cache of %d keys in pages of %d needs num_splits >= %d", cap, page,
-                decode_min_splits(span, page));
+                min_splits);
   const double items = (double)B * Hkv * num_splits * decode_row_groups(Sq, Hq, Hkv);
   if (items > 2.0e9) return fail(FA_ERR_INVALID_ARGUMENT, "too many work items");
   const size_t need = fa_fwd_kvcache_workspace_bytes(B, Sq, Hq, D, num_splits);
+  if (noalloc && need > 0) {
+    if (need > FA_KVCACHE_NOALLOC_MAX_BYTES)
+      return fail(FA_ERR_WORKSPACE,
+                  "%d splits need %zu bytes of partial results, more than the %u bytes of the static scratch array",
+                  num_splits, need, (unsigned)FA_KVCACHE_NOALLOC_MAX_BYTES);
+    if ((st = hip_status(fa::kvcache_scratch(&workspace), "kvcache scratch array"))) return st;
+    workspace_bytes = FA_KVCACHE_NOALLOC_MAX_BYTES;
+  }
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
     return fail(FA_ERR_WORKSPACE, "%d splits need %zu bytes of workspace, 16-byte aligned (got %zu at %p)",
                 num_splits, need, workspace_bytes, workspace);
@@ -464,6 +486,31 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
   a.chunk_tiles = decode_chunk(span, num_splits);
   a.row_groups = decode_row_groups(Sq, Hq, Hkv);
   return hip_status(fa::launch_decode(a, stream), "fa_fwd_kvcache launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse, int B, int Sq,
+                   int Hq, int Hkv, int D, int cache_batch, int cache_seqlen, const int32_t* cache_seqlens,
+                   const int32_t* cache_batch_idx, const int32_t* block_table, int max_blocks_per_seq, float scale,
+                   int causal, int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride,
+                   int num_splits, int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return kvcache_impl(q, k_cache, v_cache, out, lse, B, Sq, Hq, Hkv, D, cache_batch, cache_seqlen, cache_seqlens,
+                      cache_batch_idx, block_table, max_blocks_per_seq, scale, causal, window_left, window_right,
+                      alibi_slopes, alibi_batch_stride, num_splits, dtype, workspace, workspace_bytes, false, stream);
+}
+
+int fa_fwd_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse, int B,
+                           int Sq, int Hq, int Hkv, int D, int cache_batch, int cache_seqlen,
+                           const int32_t* cache_seqlens, const int32_t* cache_batch_idx, const int32_t* block_table,
+                           int max_blocks_per_seq, float scale, int causal, int window_left, int window_right,
+                           const float* alibi_slopes, int alibi_batch_stride, int num_splits, int dtype,
+                           hipStream_t stream) {
+  return kvcache_impl(q, k_cache, v_cache, out, lse, B, Sq, Hq, Hkv, D, cache_batch, cache_seqlen, cache_seqlens,
+                      cache_batch_idx, block_table, max_blocks_per_seq, scale, causal, window_left, window_right,
+                      alibi_slopes, alibi_batch_stride, num_splits, dtype, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

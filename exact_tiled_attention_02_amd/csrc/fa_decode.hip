@@ -28,8 +28,10 @@
 //   * the block table of a paged cache is read once into a register per lane (page p of
 //     the split in lane p) and picked per tile with v_readlane, so no memory access sits
 //     between two tile loads.
+#include <mutex>
 #include <type_traits>
 
+#include "fa.h"
 #include "fa_device.h"
 #include "fa_params.h"
 
@@ -462,6 +464,35 @@ hipError_t launch_decode_dt(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+namespace {
+
+// Partial results of fa_fwd_kvcache_noalloc, for callers that cannot allocate: a static
+// array of the library, one copy on each device it runs on, held until the process ends.
+// Host code must not use this name as an address (on the host it is only a stand-in for
+// the symbol): the device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) unsigned char scratch[FA_KVCACHE_NOALLOC_MAX_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device ordinal
+
+}  // namespace
+
+hipError_t kvcache_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   switch (a.D) {

@@ -101,6 +101,10 @@ hipError_t launch_check_kvcache(const int32_t* cache_seqlens, const int32_t* bat
                                 int B, int cache_batch, int cap, int page, int max_blocks, int* flag,
                                 hipStream_t stream);
 
+// Device address of this device's static scratch array of fa_fwd_kvcache_noalloc
+// (FA_KVCACHE_NOALLOC_MAX_BYTES, looked up once per device on first use).
+hipError_t kvcache_scratch(void** out);
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // stage_mask bit 0: preprocess, bit 1: main loop with dQ atomics, bit 2: finalize,

@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, i, f, i, i, i, vp, i, i, i,
                                      vp, sz, vp]
         L.fa_fwd_kvcache.restype = i
+        L.fa_fwd_kvcache_noalloc.argtypes = L.fa_fwd_kvcache.argtypes[:-3] + [vp]
+        L.fa_fwd_kvcache_noalloc.restype = i
         L.fa_fwd_kvcache_num_splits.argtypes = [i, i, i, i, i, i, i]
         L.fa_fwd_kvcache_num_splits.restype = i
         L.fa_fwd_kvcache_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -399,6 +401,33 @@ def fa_fwd_kvcache(q, k_cache, v_cache, out, lse, cache_seqlens=None, cache_batc
                                _ptr(block_table), max_blocks, float(scale), int(bool(causal)), wl, wr,
                                _ptr(alibi_slopes), stride, int(num_splits), dt, _ptr(workspace), ws_bytes,
                                _stream(stream)))
+
+
+def fa_fwd_kvcache_noalloc(q, k_cache, v_cache, out, lse, cache_seqlens=None, cache_batch_idx=None,
+                           block_table=None, causal: bool = False, scale: float | None = None, window_size=(-1, -1),
+                           alibi_slopes=None, num_splits: int = 0, stream=None) -> None:
+    """:func:`fa_fwd_kvcache` without a workspace (the C ``fa_fwd_kvcache_noalloc``): the
+    split partials go to the library's static per-device scratch array, so neither the
+    library nor this call allocates; calls that overlap on one GPU must not be issued."""
+    B, Sq, Hq, Hkv, D, cache_batch, cache_seqlen, max_blocks = _kvcache_geometry(q, k_cache, block_table)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache differ in shape")
+    _expect(out, q.shape, "out")
+    _expect(lse, (B, Hq, Sq), "lse")
+    dt = _dtype(q, k_cache, v_cache, out)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 GPU tensor")
+    _int32_vec(cache_seqlens, B, "cache_seqlens")
+    _int32_vec(cache_batch_idx, B, "cache_batch_idx")
+    _same_device(q, k_cache, v_cache, out, lse, cache_seqlens, cache_batch_idx, block_table, alibi_slopes)
+    stride = _alibi_stride(alibi_slopes, B, Hq)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    check(lib().fa_fwd_kvcache_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, Sq, Hq, Hkv,
+                                       D, cache_batch, cache_seqlen, _ptr(cache_seqlens), _ptr(cache_batch_idx),
+                                       _ptr(block_table), max_blocks, float(scale), int(bool(causal)),
+                                       int(window_size[0]), int(window_size[1]), _ptr(alibi_slopes), stride,
+                                       int(num_splits), dt, _stream(stream)))
 
 
 def forward_kvcache(q, k_cache, v_cache, cache_seqlens=None, cache_batch_idx=None, block_table=None,

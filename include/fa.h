@@ -32,8 +32,9 @@
  *
  * Ownership: the caller owns every buffer; the library allocates no device memory and
  * keeps no mutable global state except a thread-local last-error message and, on each
- * device, the 4-byte flag of the device-side checks described next (a static device
- * variable of the library, zero unless FA_DEBUG_CHECKS=1 found an error).
+ * device, two static device arrays of its own: the 4-byte flag of the device-side checks
+ * described next (zero unless FA_DEBUG_CHECKS=1 found an error) and the scratch array of
+ * fa_fwd_kvcache_noalloc.
  *
  * Errors: arguments are checked on the host before anything is launched; on error the
  * call returns a non-zero fa_status and writes nothing.  Work is enqueued on `stream`
@@ -235,6 +236,31 @@ int fa_fwd_kvcache_num_splits(int B, int Sq, int Hq, int Hkv, int D, int seqlen_
 
 /* Workspace bytes fa_fwd_kvcache needs for num_splits splits (0 when num_splits <= 1). */
 size_t fa_fwd_kvcache_workspace_bytes(int B, int Sq, int Hq, int D, int num_splits);
+
+/* Size of the static scratch array of fa_fwd_kvcache_noalloc, per device. */
+#define FA_KVCACHE_NOALLOC_MAX_BYTES (64u << 20)
+
+/*
+ * fa_fwd_kvcache without a workspace, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The split partials go to a static device array of the library,
+ * FA_KVCACHE_NOALLOC_MAX_BYTES bytes on each device it runs on, held until the process
+ * ends; this call allocates nothing.  num_splits = 0 picks the fa_fwd_kvcache count,
+ * lowered until the partials fit the array (one split needs none); an explicit count
+ * whose partials (fa_fwd_kvcache_workspace_bytes) exceed it returns FA_ERR_WORKSPACE, as
+ * does a paged cache whose smallest allowed count does not fit.  Every partial is written
+ * by the split kernel before the merge reads it, so the array's contents on entry do not
+ * matter.  All calls on one device share its array: calls that overlap in time on one
+ * GPU (streams without an ordering between them) race and must not be issued.  Other
+ * arguments, results and errors as for fa_fwd_kvcache.
+ */
+int fa_fwd_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                           int B, int Sq, int Hq, int Hkv, int D, int cache_batch, int cache_seqlen,
+                           const int32_t* cache_seqlens, const int32_t* cache_batch_idx,
+                           const int32_t* block_table, int max_blocks_per_seq,
+                           float scale, int causal, int window_left, int window_right,
+                           const float* alibi_slopes, int alibi_batch_stride,
+                           int num_splits, int dtype, hipStream_t stream);
 
 /*
  * Result of the device-side argument checks (FA_DEBUG_CHECKS=1) on the current device:
