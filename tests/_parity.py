@@ -22,6 +22,7 @@ LSE_TOL = 1e-3  # max abs error of the LSE
 GRAD_TOL = {"bf16": 5e-2, "fp16": 5e-2 / 8}
 
 THREADS = min(16, os.cpu_count() or 1)
+REPORT: list = []  # full-tensor errors, printed in the session's terminal summary
 MANT_BITS = {"bf16": 8, "fp16": 11}  # significand bits including the implicit one
 
 

@@ -7,7 +7,7 @@ from threadpoolctl import threadpool_limits
 
 from exact_tiled_attention_02_amd import fa, synth
 from oracle import attention_fp64 as orc
-from tests._parity import GRAD_TOL, THREADS, dev, f64, say
+from tests._parity import GRAD_TOL, REPORT, THREADS, dev, f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -92,7 +92,9 @@ def test_workload5_full():
     say(f"bwd {w.name} (full tensor)")
     _, _, dq, dk, dv = run_fwd_bwd(w, x)
     errs = check_grads(w, x, dq, dk, dv)
-    print(f"workload 5 full-tensor rel-Frobenius (dq, dk, dv) = {errs}")
+    msg = f"workload 5 ({w.name}) backward: rel-Frobenius (dq, dk, dv) = " + ", ".join(f"{e:.3e}" for e in errs)
+    print(msg)
+    REPORT.append(msg)
 
 
 SHAPES = [

@@ -5,8 +5,8 @@ import pytest
 import torch
 
 from exact_tiled_attention_02_amd import synth
-from tests._parity import (check_forward_sampled, compare_forward, f64, oracle_forward, oracle_forward_all_rows,
-                           run_forward, say)
+from tests._parity import (REPORT, check_forward_sampled, compare_forward, f64, oracle_forward,
+                           oracle_forward_all_rows, run_forward, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,24 +30,6 @@ def _full_check(w):
 
 # ---------------------------------------------------------------- the reference workloads
 
-def test_workload1_full():
-    w, x = synth.draw_config(1)
-    say(f"fwd {w.name}")
-    o, lse, _ = run_forward(w, x)
-    o_ref, lse_ref = oracle_forward(w, x)
-    err = compare_forward(w, o, lse, o_ref, lse_ref, where=w.name)
-    print("workload 1 errors", err)
-
-
-def test_workload2_full():
-    w, x = synth.draw_config(2)
-    say(f"fwd {w.name}")
-    o, lse, _ = run_forward(w, x)
-    o_ref, lse_ref = oracle_forward(w, x)
-    err = compare_forward(w, o, lse, o_ref, lse_ref, where=w.name)
-    print("workload 2 errors", err)
-
-
 def _workload_full(n):
     """Workload n at full size: every row of every (sequence, query head) pair of O and
     the LSE against the oracle (evaluated a chunk of rows at a time)."""
@@ -57,9 +39,19 @@ def _workload_full(n):
     o_ref, lse_ref = oracle_forward_all_rows(w, x)
     assert not np.isnan(o_ref).any() and not np.isnan(lse_ref).any(), "oracle left rows unevaluated"
     err = compare_forward(w, o, lse, o_ref, lse_ref, where=f"{w.name} full tensor")
-    print(f"workload {n} full-tensor max |O - O_ref| = {err[0]:.3e}, max |LSE - LSE_ref| = {err[1]:.3e} "
-          f"over {o_ref.size} outputs")
+    msg = (f"workload {n} ({w.name}) forward: max |O - O_ref| = {err[0]:.3e}, max |LSE - LSE_ref| = {err[1]:.3e} "
+           f"over all {o_ref.size} outputs")
+    print(msg)
+    REPORT.append(msg)
     return err
+
+
+def test_workload1_full():
+    _workload_full(1)
+
+
+def test_workload2_full():
+    _workload_full(2)
 
 
 def test_workload3_full():
