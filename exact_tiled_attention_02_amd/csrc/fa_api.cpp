@@ -39,8 +39,8 @@ int check_common(int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, con
                 Hkv, D);
   if (Hq % Hkv != 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "Hq=%d is not divisible by Hkv=%d", Hq, Hkv);
-  if (D != 64 && D != 128 && D != 256)
-    return fail(FA_ERR_UNSUPPORTED, "head dimension %d has no kernel (64, 128, 256)", D);
+  if (fa::tile_headdim(D) == 0)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension %d is not a multiple of 8 in [8, 256]", D);
   if (!std::isfinite(scale) || scale < 0.f)
     return fail(FA_ERR_INVALID_ARGUMENT, "scale must be finite and non-negative (got %g)", (double)scale);
   if ((cu_q == nullptr) != (cu_k == nullptr))
@@ -232,6 +232,9 @@ int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, con
       (st = check_ptr(v, "v")) || (st = check_ptr(out, "out")) || (st = check_ptr(lse, "lse")) ||
       (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
     return st;
+  // The backward main loop addresses a block of 256 keys with 31-bit lane offsets.
+  if ((long long)Hkv * D * 2 * 256 >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "Hkv * D = %lld is too wide for the backward (limit 2^22)", (long long)Hkv * D);
   const size_t need = fa_bwd_workspace_bytes(B, Sq, Hq, D);
   if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu at %p)", need,

@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   if constexpr (VARLEN) rows = min(rows, (size_t)max(load_uniform(a.cu_q + a.B), 0));
   const bool live = pair < rows * a.Hq;
   float s = 0.f;
-  if (live) {
-    const size_t off = pair * D + ch * 8;
+  if (live && ch * 8 < a.D) {  // lanes past the head dimension add nothing
+    const size_t off = pair * a.D + ch * 8;
     const u32x4 o = load16((const uint16_t*)a.out + off);
     const u32x4 g = load16((const uint16_t*)a.dout + off);
 #pragma unroll
@@ -141,10 +141,12 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   if (k0 >= Lk) return;  // uniform
 
   const int G = a.Hq / a.Hkv;
-  const size_t q_rs = (size_t)a.Hq * D;
-  const size_t k_rs = (size_t)a.Hkv * D;
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+  const int Dr = a.D;  // head dimension of the tensors (<= D, the tile width)
+  const int Dc = Dr / 8;
+  const size_t q_rs = (size_t)a.Hq * Dr;
+  const size_t k_rs = (size_t)a.Hkv * Dr;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * Dr;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * Dr;
   const int diag = Lk - Lq;
   const float c = a.scale_log2;
   constexpr float kLog2e = 1.4426950408889634f;
@@ -189,15 +191,15 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     const int g = it / nqs;
     const int h = hk * G + g;
     const int i0 = (qb_begin + it % nqs) * kBwdBQ;
-    const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
-    const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * D;
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * Dr;
+    const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * Dr;
 #pragma unroll
     for (int i = 0; i < QT / 8 / 256; ++i) {
       const int first = (i * kBwdWaves + wave) * 64;
       const int chunk = first + lane;
       const int r = chunk / Swz::CH;
       const int p = chunk % Swz::CH;
-      const uint32_t src = (uint32_t)(min(r, Lq - 1 - i0) * (int)q_rs + Swz::chunk(r, p) * 8) * 2u;
+      const uint32_t src = (uint32_t)(min(r, Lq - 1 - i0) * (int)q_rs + src_chunk(Swz::chunk(r, p), Dc) * 8) * 2u;
       lds_direct_load16(qp + (size_t)i0 * q_rs, src, &Qs[buf][first * 8]);
       lds_direct_load16(dop + (size_t)i0 * q_rs, src, &dOs[buf][first * 8]);
     }
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     const int chunk = first + lane;
     const int r = chunk / Swz::CH;
     const int p = chunk % Swz::CH;
-    lds_direct_load16(kp + (size_t)min(k0 + r, Lk - 1) * k_rs + Swz::chunk(r, p) * 8, &Ks[first * 8]);
+    lds_direct_load16(kp + (size_t)min(k0 + r, Lk - 1) * k_rs + src_chunk(Swz::chunk(r, p), Dc) * 8, &Ks[first * 8]);
   }
 
   // This wavefront's keys as B operands: lane holds K[key][16 s + 8 lh .. +7].
@@ -223,8 +225,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   Frag8 kf[NS], vf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    kf[s].v = key_ok ? load16(kp + (size_t)my_key * k_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
-    vf[s].v = key_ok ? load16(vp + (size_t)my_key * k_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+    // zero past the head dimension (the padded Q / dO chunks re-read chunk 0)
+    const bool in = key_ok && s * 16 + lh * 8 < Dr;
+    kf[s].v = in ? load16(kp + (size_t)my_key * k_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+    vf[s].v = in ? load16(vp + (size_t)my_key * k_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
   }
   f32x16 dkt[ND], dvt[ND];
 #pragma unroll
@@ -333,8 +337,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = i0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < Lq && (size_t)(q_start + row) < (size_t)a.B * a.Sq) {  // inside the accumulator
-          float* dst = a.dq_acc + ((size_t)(q_start + row) * a.Hq + h) * D + d * 32 + li;
+        if (row < Lq && (size_t)(q_start + row) < (size_t)a.B * a.Sq && d * 32 + li < Dr) {  // inside the accumulator
+          float* dst = a.dq_acc + ((size_t)(q_start + row) * a.Hq + h) * Dr + d * 32 + li;
           unsafeAtomicAdd(dst, dq[r]);
         }
       }
@@ -345,8 +349,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
 
   // dK, dV: lane = key, registers = head-dimension entries.
   if (key_ok) {
-    uint16_t* dkp = (uint16_t*)a.dk + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
-    uint16_t* dvp = (uint16_t*)a.dv + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
+    uint16_t* dkp = (uint16_t*)a.dk + (size_t)(k_start + my_key) * k_rs + (size_t)hk * Dr;
+    uint16_t* dvp = (uint16_t*)a.dv + (size_t)(k_start + my_key) * k_rs + (size_t)hk * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
 #pragma unroll
@@ -357,8 +361,10 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
         wk.y = pack2<BF16>(dkt[d][4 * gq + 2] * a.scale, dkt[d][4 * gq + 3] * a.scale);
         wv.x = pack2<BF16>(dvt[d][4 * gq + 0], dvt[d][4 * gq + 1]);
         wv.y = pack2<BF16>(dvt[d][4 * gq + 2], dvt[d][4 * gq + 3]);
-        *(u32x2*)(dkp + col) = wk;
-        *(u32x2*)(dvp + col) = wv;
+        if (col < Dr) {  // four columns, all inside or all past the head dimension
+          *(u32x2*)(dkp + col) = wk;
+          *(u32x2*)(dvp + col) = wv;
+        }
       }
     }
   }
@@ -424,10 +430,12 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   if (k0 >= Lk) return;  // uniform
 
   const int G = a.Hq / a.Hkv;
-  const size_t q_rs = (size_t)a.Hq * D;
-  const size_t k_rs = (size_t)a.Hkv * D;
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+  const int Dr = a.D;  // head dimension of the tensors (<= D, the tile width)
+  const int Dc = Dr / 8;
+  const size_t q_rs = (size_t)a.Hq * Dr;
+  const size_t k_rs = (size_t)a.Hkv * Dr;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * Dr;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * Dr;
   const int diag = Lk - Lq;
   const float c = a.scale_log2;
   constexpr float kLog2e = 1.4426950408889634f;
@@ -466,7 +474,8 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   const int qchunk = wave * 64 + lane;
   const bool qloader = wave * 64 < QCH;  // uniform per wavefront
   const int qr = qchunk / Swz::CH;
-  const uint32_t qoff = (uint32_t)(qr * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8) * 2u;  // bytes
+  // global chunk of this lane's LDS chunk, and its byte offset from the tile's first row
+  const uint32_t qoff = (uint32_t)(qr * (int)q_rs + src_chunk(Swz::chunk(qr, qchunk % Swz::CH), Dc) * 8) * 2u;
   // Steps walk (query head of the group, query block) with the block fastest; the
   // position is carried as counters (no division by the runtime block count).
   auto fetch = [&](int h, int i0, uint16_t* __restrict__ Qd, uint16_t* __restrict__ dOd, float* __restrict__ lsed,
@@ -474,11 +483,14 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
     // Buffer-form direct loads from the step's first row (the flat form would make the
     // compiler wait for every LDS read with lgkmcnt(0)).  The lane offsets address clamped
     // rows of the sequence.
-    const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * D;
+    const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * Dr;
     if (qloader) {
       uint32_t off = qoff;
-      if (i0 + kK2BQ > Lq)
-        off = (uint32_t)(min(qr, Lq - 1 - i0) * (int)q_rs + Swz::chunk(qr, qchunk % Swz::CH) * 8) * 2u;
+      if (i0 + kK2BQ > Lq) {
+        // rows clamped to the sequence; recomputed from the lane id rather than kept live
+        const int qc = opaque(qchunk), r = qc / Swz::CH;
+        off = (uint32_t)(min(r, Lq - 1 - i0) * (int)q_rs + src_chunk(Swz::chunk(r, qc % Swz::CH), Dc) * 8) * 2u;
+      }
       const uint32_t qbytes = bytes_left(q_rows * q_rs, base, 2u);
       lds_buffer_load16(make_rsrc((const uint16_t*)a.q + base, qbytes), off, Qd + wave * 64 * 8);
       lds_buffer_load16(make_rsrc((const uint16_t*)a.dout + base, qbytes), off, dOd + wave * 64 * 8);
@@ -493,13 +505,24 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   };
 
   if (nsteps > 0) fetch(hk * G, qb_begin * kK2BQ, Q0, dO0, lse0, dsum0);
+  // The block's K tile (rows clamped to the sequence) by buffer loads from its first key.
+  // Chunks past the head dimension get an offset beyond the resource's extent, which the
+  // hardware reads as zeros: K is the zero side of S = Q K^T for a padded head dimension.
+  // (Lane offsets of real chunks stay below 256 rows * Hkv * D * 2 < 2^31 bytes, checked
+  // by the host.)
+  {
+    const size_t kfirst = (size_t)(k_start + k0) * k_rs + (size_t)hk * Dr;
+    const size_t k_rows = VARLEN ? (size_t)load_uniform(a.cu_k + a.B) : (size_t)a.B * a.Sk;
+    const auto kr = make_rsrc((const uint16_t*)a.k + kfirst, min(bytes_left(k_rows * k_rs, kfirst, 2u), 0x7fffffffu));
 #pragma unroll
-  for (int i = 0; i < kK2Keys * D / 8 / 512; ++i) {
-    const int first = (i * kK2Waves + wave) * 64;
-    const int chunk = first + lane;
-    const int r = chunk / Swz::CH;
-    const int p = chunk % Swz::CH;
-    lds_direct_load16(kp + (size_t)min(k0 + r, Lk - 1) * k_rs + Swz::chunk(r, p) * 8, Ks + first * 8);
+    for (int i = 0; i < kK2Keys * D / 8 / 512; ++i) {
+      const int first = (i * kK2Waves + wave) * 64;
+      const int chunk = first + lane;
+      const int r = chunk / Swz::CH;
+      const int g = Swz::chunk(r, chunk % Swz::CH);
+      const uint32_t off = g < Dc ? (uint32_t)(min(r, Lk - 1 - k0) * (int)k_rs + g * 8) * 2u : 0x80000000u;
+      lds_buffer_load16(kr, off, Ks + first * 8);
+    }
   }
 
   // This wavefront's keys; V as B operands of dP = dO V^T.
@@ -517,7 +540,8 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   Frag8 vf[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st)
-    vf[st].v = key_ok ? load16(vp + (size_t)my_key * k_rs + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+    vf[st].v = key_ok && st * 16 + lh * 8 < Dr ? load16(vp + (size_t)my_key * k_rs + st * 16 + lh * 8)
+                                               : u32x4{0, 0, 0, 0};  // zero past the head dimension
   f32x16 dkt[ND], dvt[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
@@ -701,12 +725,14 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
           // The resource spans the rest of the accumulator, and rows past its B * Sq rows
           // (possible only with invalid cu_seqlens) are skipped: the scalar offset is not
           // range-checked by the hardware.
-          const size_t acc0 = ((size_t)(q_start + i0) * a.Hq + h) * D;
-          const auto dqr = make_rsrc(a.dq_acc + acc0, bytes_left(ws_rows * a.Hq * D, acc0, 4u));
-          const uint32_t rs4 = (uint32_t)a.Hq * D * 4u;  // bytes per row
+          const size_t acc0 = ((size_t)(q_start + i0) * a.Hq + h) * Dr;
+          const auto dqr = make_rsrc(a.dq_acc + acc0, bytes_left(ws_rows * a.Hq * Dr, acc0, 4u));
+          const uint32_t rs4 = (uint32_t)a.Hq * Dr * 4u;  // bytes per row
           const uint32_t voff = 4u * lh * rs4 + (uint32_t)(dblk * 32 + li) * 4u;
-          const int lim = (int)min((size_t)Lq, ws_rows - min(ws_rows, (size_t)q_start));  // rows < lim are stored
-          if (__builtin_expect(i0 + kK2BQ <= lim, 1)) {
+          // rows < lim are stored; columns past the head dimension are not (a d-block that
+          // reaches past it takes the per-element path)
+          const int lim = (int)min((size_t)Lq, ws_rows - min(ws_rows, (size_t)q_start));
+          if (__builtin_expect(i0 + kK2BQ <= lim && (dblk + 1) * 32 <= Dr, 1)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[r], dqr, (int)voff, (int)((8 * (r >> 2) + (r & 3)) * rs4),
@@ -715,7 +741,7 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int rr = 8 * (r >> 2) + (r & 3);
-              if (i0 + 4 * lh + rr < lim)
+              if (i0 + 4 * lh + rr < lim && dblk * 32 + li < Dr)
                 __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(dq[r], dqr, (int)voff, (int)(rr * rs4), 0);
             }
           }
@@ -752,8 +778,8 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   }
 
   if (key_ok) {
-    uint16_t* dkp = (uint16_t*)a.dk + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
-    uint16_t* dvp = (uint16_t*)a.dv + (size_t)(k_start + my_key) * k_rs + (size_t)hk * D;
+    uint16_t* dkp = (uint16_t*)a.dk + (size_t)(k_start + my_key) * k_rs + (size_t)hk * Dr;
+    uint16_t* dvp = (uint16_t*)a.dv + (size_t)(k_start + my_key) * k_rs + (size_t)hk * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
 #pragma unroll
@@ -764,8 +790,10 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
         wk.y = pack2<BF16>(dkt[d][4 * gq + 2] * a.scale, dkt[d][4 * gq + 3] * a.scale);
         wv.x = pack2<BF16>(dvt[d][4 * gq + 0], dvt[d][4 * gq + 1]);
         wv.y = pack2<BF16>(dvt[d][4 * gq + 2], dvt[d][4 * gq + 3]);
-        *(u32x2*)(dkp + col) = wk;
-        *(u32x2*)(dvp + col) = wv;
+        if (col < Dr) {  // four columns, all inside or all past the head dimension
+          *(u32x2*)(dkp + col) = wk;
+          *(u32x2*)(dvp + col) = wv;
+        }
       }
     }
   }
@@ -856,12 +884,14 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
   if (q0 >= Lq) return;  // uniform
 
   const int hk = h / (a.Hq / a.Hkv);
-  const size_t q_rs = (size_t)a.Hq * D;
-  const size_t k_rs = (size_t)a.Hkv * D;
-  const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
-  const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * D;
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+  const int Dr = a.D;  // head dimension of the tensors (<= D, the tile width)
+  const int Dc = Dr / 8;
+  const size_t q_rs = (size_t)a.Hq * Dr;
+  const size_t k_rs = (size_t)a.Hkv * Dr;
+  const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * Dr;
+  const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * Dr;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * Dr;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * Dr;
 
   const int diag = Lk - Lq;
   KeyWindow kw{Lk, diag, 0, -1, -1};
@@ -883,7 +913,7 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
   for (int i = 0; i < NI; ++i) {
     const int chunk = (i * kDqWaves + wave) * 64 + lane;
     const int r = chunk / Swz::CH;
-    foff[i] = (uint32_t)(r * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
+    foff[i] = (uint32_t)(r * (int)k_rs + src_chunk(Swz::chunk(r, chunk % Swz::CH), Dc) * 8) * 2u;
   }
   auto fetch = [&](int kb, uint16_t* __restrict__ Kd, uint16_t* __restrict__ Vd) {
     const int k0 = kb * kDqBN;
@@ -896,7 +926,7 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
       if (k0 + kDqBN > Lk) {
         const int chunk = first + lane;
         const int r = chunk / Swz::CH;
-        off = (uint32_t)(min(r, Lk - 1 - k0) * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
+        off = (uint32_t)(min(r, Lk - 1 - k0) * (int)k_rs + src_chunk(Swz::chunk(r, chunk % Swz::CH), Dc) * 8) * 2u;
       }
       lds_direct_load16(kt, off, Kd + first * 8);
       lds_direct_load16(vt, off, Vd + first * 8);
@@ -907,8 +937,10 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
   Frag8 qf[NS], gf[NS];
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    qf[st].v = row_ok ? load16(qp + (size_t)my_row * q_rs + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
-    gf[st].v = row_ok ? load16(dop + (size_t)my_row * q_rs + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+    // zero past the head dimension (the padded K / V chunks re-read chunk 0)
+    const bool in = row_ok && st * 16 + lh * 8 < Dr;
+    qf[st].v = in ? load16(qp + (size_t)my_row * q_rs + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+    gf[st].v = in ? load16(dop + (size_t)my_row * q_rs + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
   }
   constexpr float kLog2e = 1.4426950408889634f;
   float lse2 = INFINITY, dsum = 0.f;
@@ -1017,7 +1049,7 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
   }
 
   if (row_ok) {
-    uint16_t* gp = (uint16_t*)a.dq + (size_t)(q_start + my_row) * q_rs + (size_t)h * D;
+    uint16_t* gp = (uint16_t*)a.dq + (size_t)(q_start + my_row) * q_rs + (size_t)h * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
 #pragma unroll
@@ -1026,7 +1058,7 @@ __global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
         u32x2 w;
         w.x = pack2<BF16>(acc[d][4 * g + 0], acc[d][4 * g + 1]);
         w.y = pack2<BF16>(acc[d][4 * g + 2], acc[d][4 * g + 3]);
-        *(u32x2*)(gp + col) = w;
+        if (col < Dr) *(u32x2*)(gp + col) = w;
       }
     }
   }
@@ -1108,7 +1140,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     }
   }
   if (stages & 4) {
-    const size_t n8 = rows * a.Hq * D / 8;
+    const size_t n8 = rows * a.Hq * a.D / 8;
     size_t blocks = (n8 + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL((bwd_dq_kernel<BF16, VARLEN>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
@@ -1143,7 +1175,7 @@ hipError_t launch_bwd_dt(const BwdArgs& a, int st, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, int stage_mask, hipStream_t stream) {
-  switch (a.D) {
+  switch (tile_headdim(a.D)) {
     case 64: return launch_bwd_dt<64>(a, stage_mask, stream);
     case 128: return launch_bwd_dt<128>(a, stage_mask, stream);
     case 256: return launch_bwd_dt<256>(a, stage_mask, stream);

@@ -146,9 +146,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int t0 = min(t_end, t_begin + split * a.chunk_tiles);
   const int t1 = min(t_end, t0 + a.chunk_tiles);
 
-  const size_t rs = (size_t)a.Hkv * D;  // elements between consecutive keys
-  const uint16_t* kbase = (const uint16_t*)a.k + (size_t)hk * D;
-  const uint16_t* vbase = (const uint16_t*)a.v + (size_t)hk * D;
+  const int Dr = a.D;  // head dimension of the tensors (<= D, the tile width)
+  const int Dc = Dr / 8;
+  const size_t rs = (size_t)a.Hkv * Dr;  // elements between consecutive keys
+  const uint16_t* kbase = (const uint16_t*)a.k + (size_t)hk * Dr;
+  const uint16_t* vbase = (const uint16_t*)a.v + (size_t)hk * Dr;
   int bt = 0, pfirst = 0, ipg = 0, ioff = 0;
   if constexpr (PAGED) {
     pfirst = t0 * kDecKeys / a.page;
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   for (int i = 0; i < NI; ++i) {
     const int chunk = i * 64 + lane;
     const int rr = chunk / CH;
-    foff[i] = (uint32_t)(rr * (int)rs + Swz::chunk(rr, chunk % CH) * 8) * 2u;
+    foff[i] = (uint32_t)(rr * (int)rs + src_chunk(Swz::chunk(rr, chunk % CH), Dc) * 8) * 2u;
   }
 
   // Issue the loads of tile t into ring slot k.  Tiles are issued in increasing order,
@@ -206,7 +208,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       for (int i = 0; i < NI; ++i) {
         const int chunk = i * 64 + lane;
         const int rr = chunk / CH;
-        const uint32_t off = (uint32_t)(min(rr, Lk - 1 - k0) * (int)rs + Swz::chunk(rr, chunk % CH) * 8) * 2u;
+        const uint32_t off =
+            (uint32_t)(min(rr, Lk - 1 - k0) * (int)rs + src_chunk(Swz::chunk(rr, chunk % CH), Dc) * 8) * 2u;
         lds_direct_load16(kt, off, dst + i * 512);
         lds_direct_load16(vt, off, dst + TILE + i * 512);
       }
@@ -214,10 +217,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   };
 
   // Q^T operand (B of S^T = K Q^T): lane holds Q[row][16 st + 8 lh .. +7].
-  const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * a.Sq + s) * a.Hq + h) * D;
+  const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(b * a.Sq + s) * a.Hq + h) * Dr;
   Frag8 qf[NS];
 #pragma unroll
-  for (int st = 0; st < NS; ++st) qf[st].v = row_ok ? load16(qp + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+  for (int st = 0; st < NS; ++st)  // zero past the head dimension (padded K chunks re-read chunk 0)
+    qf[st].v = row_ok && st * 16 + lh * 8 < Dr ? load16(qp + st * 16 + lh * 8) : u32x4{0, 0, 0, 0};
   float sl2 = 0.f;  // ALiBi slope in exp2 units
   if constexpr (ALIBI) sl2 = row_ok ? a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e : 0.f;
 
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const size_t lrow = ((size_t)b * a.Hq + h) * a.Sq + s;
   if (!row_ok) return;
   if (a.splits == 1) {
-    uint16_t* op = (uint16_t*)a.out + orow * D;
+    uint16_t* op = (uint16_t*)a.out + orow * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
 #pragma unroll
@@ -347,20 +351,20 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         u32x2 w;
         w.x = pack2<BF16>(acc[d][4 * g + 0] * inv, acc[d][4 * g + 1] * inv);
         w.y = pack2<BF16>(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv);
-        *(u32x2*)(op + d * 32 + 8 * g + 4 * lh) = w;
+        if (d * 32 + 8 * g + 4 * lh < Dr) *(u32x2*)(op + d * 32 + 8 * g + 4 * lh) = w;
       }
     }
     if (lh == 0) a.lse[lrow] = l_tot > 0.f ? lse_nat : INFINITY;
   } else {
     const size_t nrows = (size_t)a.B * a.Sq * a.Hq;
-    float* op = a.o_part + ((size_t)split * nrows + orow) * D;
+    float* op = a.o_part + ((size_t)split * nrows + orow) * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f32x4 w = {acc[d][4 * g + 0] * inv, acc[d][4 * g + 1] * inv, acc[d][4 * g + 2] * inv,
                    acc[d][4 * g + 3] * inv};
-        *(f32x4*)(op + d * 32 + 8 * g + 4 * lh) = w;
+        if (d * 32 + 8 * g + 4 * lh < Dr) *(f32x4*)(op + d * 32 + 8 * g + 4 * lh) = w;
       }
     }
     if (lh == 0) a.lse_part[(size_t)split * nrows + lrow] = l_tot > 0.f ? lse_nat : -INFINITY;
@@ -398,9 +402,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   float mx = -INFINITY;
   for (int r = lane; r < S; r += 64) mx = fmaxf(mx, lp[(size_t)r * nrows]);
   mx = wave_max(mx);
-  uint16_t* op = (uint16_t*)a.out + (size_t)row * D;
+  const int Dr = a.D;  // head dimension (<= D)
+  uint16_t* op = (uint16_t*)a.out + (size_t)row * Dr;
   if (mx == -INFINITY) {  // no split kept a key: zero output, LSE +inf
-    for (int e = lane; e < D; e += 64) op[e] = 0;
+    for (int e = lane; e < Dr; e += 64) op[e] = 0;
     if (lane == 0) a.lse[lrow] = INFINITY;
     return;
   }
@@ -414,12 +419,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int RPI = 64 / C4;  // splits per pass
   const int c4 = lane % C4;
   const int rsub = lane / C4;
-  const float* pp = a.o_part + (size_t)row * D + c4 * 4;
+  const bool col_ok = c4 * 4 < Dr;  // lanes past the head dimension add zeros and store nothing
+  const float* pp = a.o_part + (size_t)row * Dr + c4 * 4;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int r = rsub; r < S; r += RPI) {
     const float w = __expf(lp[(size_t)r * nrows] - L);
-    const f32x4 x = *(const f32x4*)(pp + (size_t)r * nrows * D);
+    const f32x4 x = col_ok ? *(const f32x4*)(pp + (size_t)r * nrows * Dr) : f32x4{0.f, 0.f, 0.f, 0.f};
     o += w * x;
   }
 #pragma unroll
@@ -427,7 +433,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] += __shfl_xor(o[e], off);
   }
-  if (rsub == 0) {
+  if (rsub == 0 && col_ok) {
     u32x2 w;
     w.x = pack2<BF16>(o[0], o[1]);
     w.y = pack2<BF16>(o[2], o[3]);
@@ -495,7 +501,7 @@ hipError_t kvcache_scratch(void** out) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  switch (a.D) {
+  switch (tile_headdim(a.D)) {
     case 64: return launch_decode_dt<64>(a, stream);
     case 128: return launch_decode_dt<128>(a, stream);
     case 256: return launch_decode_dt<256>(a, stream);

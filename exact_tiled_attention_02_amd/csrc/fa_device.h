@@ -183,6 +183,15 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Head dimensions that are not a tile size: a kernel instantiated for tile width D
+// (64, 128 or 256) serves any head dimension Dr <= D with Dr % 8 == 0.  Rows in LDS keep D
+// elements; the 16-byte chunks past Dr / 8 are padding.  One operand of every product over
+// the head dimension holds zeros there (the query side of S in the forward, the key and
+// value side in the backward), and the other re-reads chunk 0 of the same row
+// (src_chunk), so the padding adds exact zeros and no load leaves the row; products whose
+// output columns fall in the padding are never stored.
+__device__ __forceinline__ int src_chunk(int g, int dc) { return g < dc ? g : 0; }
+
 // Combine a value with the one held by lane l^32 (the other half of the wavefront).
 __device__ __forceinline__ float pair_max(float x) {
   const uint32_t b = __builtin_bit_cast(uint32_t, x);

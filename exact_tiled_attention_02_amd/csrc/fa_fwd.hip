@@ -163,11 +163,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   if (q0 >= Lq) return;  // uniform over the workgroup
 
   const int hk = h / (a.Hq / a.Hkv);
-  const size_t q_rs = (size_t)a.Hq * D;
-  const size_t k_rs = (size_t)a.Hkv * D;
-  const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * D;
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+  const int Dr = a.D;  // head dimension of the tensors (<= D, the tile width)
+  const int Dc = Dr / 8;
+  const size_t q_rs = (size_t)a.Hq * Dr;
+  const size_t k_rs = (size_t)a.Hkv * Dr;
+  const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * Dr;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * Dr;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * Dr;
 
   // Kept keys of row i: [kw.lo(i), kw.hi(i)], both non-decreasing in i.  Without a mask
   // every row keeps [0, Lk - 1].
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   for (int i = 0; i < NI; ++i) {
     const int chunk = (i * kFwdWaves + wave) * 64 + lane;
     const int r = chunk / Swz::CH;
-    foff[i] = (uint32_t)(r * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
+    foff[i] = (uint32_t)(r * (int)k_rs + src_chunk(Swz::chunk(r, chunk % Swz::CH), Dc) * 8) * 2u;
   }
   auto fetch = [&](int kb, auto buf_tag) {
     uint16_t* Kd = decltype(buf_tag)::value ? K1 : K0;
@@ -218,7 +220,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const int first = (i * kFwdWaves + wave) * 64;
         const int chunk = first + lane;
         const int r = chunk / Swz::CH;
-        const uint32_t off = (uint32_t)(min(r, Lk - 1 - k0) * (int)k_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
+        const uint32_t off =
+            (uint32_t)(min(r, Lk - 1 - k0) * (int)k_rs + src_chunk(Swz::chunk(r, chunk % Swz::CH), Dc) * 8) * 2u;
         lds_direct_load16(kt, off, Kd + first * 8);
         lds_direct_load16(vt, off, Vd + first * 8);
       }
@@ -246,7 +249,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   Frag8 qf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    qf[s].v = row_ok ? load16(qp + (size_t)my_row * q_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
+    // zero past the head dimension: the padded K chunks re-read chunk 0 (src_chunk)
+    qf[s].v = row_ok && s * 16 + lh * 8 < Dr ? load16(qp + (size_t)my_row * q_rs + s * 16 + lh * 8)
+                                             : u32x4{0, 0, 0, 0};
   }
 
   f32x16 acc[ND];
@@ -412,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const float l_tot = pair_sum(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * D;
+    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
 #pragma unroll
@@ -421,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         u32x2 w;
         w.x = pack2<BF16>(acc[d][4 * g + 0] * inv, acc[d][4 * g + 1] * inv);
         w.y = pack2<BF16>(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv);
-        *(u32x2*)(op + col) = w;
+        if (col < Dr) *(u32x2*)(op + col) = w;  // four columns, all inside or all past Dr
       }
     }
     if (lh == 0) {
@@ -507,10 +512,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (q0 >= Lq) return;  // uniform over the workgroup
 
   const int hk = h / (a.Hq / a.Hkv);
-  const size_t q_rs = (size_t)a.Hq * D;
-  const size_t k_rs = (size_t)a.Hkv * D;
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+  const int Dr = a.D;  // head dimension of the tensors (<= D, the tile width)
+  const int Dc = Dr / 8;
+  const size_t q_rs = (size_t)a.Hq * Dr;
+  const size_t k_rs = (size_t)a.Hkv * Dr;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * Dr;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * Dr;
 
   const int diag = Lk - Lq;
   KeyWindow kw{Lk, diag, 0, -1, -1};
@@ -552,7 +559,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // span less than 4 GiB, which the host checks); a tile's first row goes in the scalar
   // offset, the row and column within the tile in the lane offset.
   const uint32_t krs2 = (uint32_t)k_rs * 2u;
-  const size_t kv_first = (size_t)k_start * k_rs + (size_t)hk * D;
+  const size_t kv_first = (size_t)k_start * k_rs + (size_t)hk * Dr;
   const size_t kv_rest = ((size_t)(VARLEN ? load_uniform(a.cu_k + a.B) : a.B * a.Sk) * k_rs - kv_first) * 2u;
   const uint32_t kv_bytes = (uint32_t)(kv_rest < 0xffffffffu ? kv_rest : 0xffffffffu);
   const auto kr = make_rsrc(kp, kv_bytes);
@@ -564,7 +571,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < NI; ++i) {
     const int chunk = (i * kPPWaves + wave) * 64 + lane;
     lrow[i] = chunk / Swz::CH;
-    lcol[i] = (uint32_t)(Swz::chunk(lrow[i], chunk % Swz::CH) * 16);
+    lcol[i] = (uint32_t)(src_chunk(Swz::chunk(lrow[i], chunk % Swz::CH), Dc) * 16);
   }
   // First keys of the K and V tiles of stage st (wavefront-uniform), computed before the
   // M phase that precedes the X phase issuing the loads.
@@ -604,7 +611,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint16_t* Qw = Qs + wave * 32 * D;
   {
     const int base_row = min(wave_row0, Lq - 1);
-    const size_t qfirst = (size_t)(q_start + base_row) * q_rs + (size_t)h * D;
+    const size_t qfirst = (size_t)(q_start + base_row) * q_rs + (size_t)h * Dr;
     const size_t qrest = ((size_t)(VARLEN ? load_uniform(a.cu_q + a.B) : a.B * a.Sq) * q_rs - qfirst) * 2u;
     const auto qr = make_rsrc((const uint16_t*)a.q + qfirst, (uint32_t)(qrest < 0xffffffffu ? qrest : 0xffffffffu));
 #pragma unroll
@@ -612,8 +619,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int chunk = i * 64 + lane;
       const int r = chunk / Swz::CH;
       const int row = min(wave_row0 + r, Lq - 1) - base_row;
-      const uint32_t off = (uint32_t)(row * (int)q_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
-      lds_buffer_load16(qr, off, Qw + i * 64 * 8);
+      const int g = Swz::chunk(r, chunk % Swz::CH);
+      const uint32_t off = (uint32_t)(row * (int)q_rs + g * 8) * 2u;
+      if (g < Dc) {
+        lds_buffer_load16(qr, off, Qw + i * 64 * 8);
+      } else {
+        store16(Qw + (i * 64 + lane) * 8, u32x4{0, 0, 0, 0});  // past the head dimension
+      }
     }
   }
   if (n > 0) {
@@ -895,7 +907,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float l_tot = pair_sum(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * D;
+    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
 #pragma unroll
@@ -904,7 +916,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         u32x2 w;
         w.x = pack2<BF16>(acc[d][4 * g + 0] * inv, acc[d][4 * g + 1] * inv);
         w.y = pack2<BF16>(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv);
-        *(u32x2*)(op + col) = w;
+        if (col < Dr) *(u32x2*)(op + col) = w;  // four columns, all inside or all past Dr
       }
     }
     if (lh == 0) {
@@ -988,10 +1000,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (q0 >= Lq) return;  // uniform over the workgroup
 
   const int hk = h / (a.Hq / a.Hkv);
-  const size_t q_rs = (size_t)a.Hq * D;
-  const size_t k_rs = (size_t)a.Hkv * D;
-  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * D;
+  const int Dr = a.D;  // head dimension of the tensors (<= D, the tile width)
+  const int Dc = Dr / 8;
+  const size_t q_rs = (size_t)a.Hq * Dr;
+  const size_t k_rs = (size_t)a.Hkv * Dr;
+  const uint16_t* kp = (const uint16_t*)a.k + (size_t)k_start * k_rs + (size_t)hk * Dr;
+  const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * Dr;
 
   const int diag = Lk - Lq;
   KeyWindow kw{Lk, diag, 0, -1, -1};
@@ -1031,7 +1045,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NI = TILE / 8 / (64 * 4);
   static_assert(NI >= 1 && (TILE / 8) % (64 * 4) == 0, "whole chunks per lane");
   const uint32_t krs2 = (uint32_t)k_rs * 2u;
-  const size_t kv_first = (size_t)k_start * k_rs + (size_t)hk * D;
+  const size_t kv_first = (size_t)k_start * k_rs + (size_t)hk * Dr;
   const size_t kv_rest = ((size_t)(VARLEN ? load_uniform(a.cu_k + a.B) : a.B * a.Sk) * k_rs - kv_first) * 2u;
   const uint32_t kv_bytes = (uint32_t)(kv_rest < 0xffffffffu ? kv_rest : 0xffffffffu);
   const auto kr = make_rsrc(kp, kv_bytes);
@@ -1039,7 +1053,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Row and swizzled column (bytes) of this lane's chunk i of a tile.
   auto lrow = [&](int i) __attribute__((always_inline)) { return ((i * 4 + pr) * 64 + lane) / Swz::CH; };
   auto lcol = [&](int i) __attribute__((always_inline)) {
-    return (uint32_t)(Swz::chunk(lrow(i), lane % Swz::CH) * 16);
+    return (uint32_t)(src_chunk(Swz::chunk(lrow(i), lane % Swz::CH), Dc) * 16);
   };
   uint32_t loff[NI];
 #pragma unroll
@@ -1066,7 +1080,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int row = ((i * 4 + pr) * 64 + ln) / Swz::CH;
-        const uint32_t col = (uint32_t)(Swz::chunk(row, ln % Swz::CH) * 16);
+        const uint32_t col = (uint32_t)(src_chunk(Swz::chunk(row, ln % Swz::CH), Dc) * 16);
         lds_buffer_load16(kr, __umul24((uint32_t)min(row, klim), krs2) + col, Kd + (i * 4 + pr) * 64 * 8,
                           (uint32_t)src.kk0 * krs2);
         lds_buffer_load16(vr, __umul24((uint32_t)min(row, vlim), krs2) + col, Vd + (i * 4 + pr) * 64 * 8,
@@ -1089,7 +1103,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint16_t* Qw = Qs + pr * 32 * D;
   {
     const int base_row = min(wave_row0, Lq - 1);
-    const size_t qfirst = (size_t)(q_start + base_row) * q_rs + (size_t)h * D;
+    const size_t qfirst = (size_t)(q_start + base_row) * q_rs + (size_t)h * Dr;
     const size_t qrest = ((size_t)(VARLEN ? load_uniform(a.cu_q + a.B) : a.B * a.Sq) * q_rs - qfirst) * 2u;
     const auto qr = make_rsrc((const uint16_t*)a.q + qfirst, (uint32_t)(qrest < 0xffffffffu ? qrest : 0xffffffffu));
 #pragma unroll
@@ -1097,8 +1111,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int chunk = (i * 2 + grp) * 64 + lane;
       const int r = chunk / Swz::CH;
       const int row = min(wave_row0 + r, Lq - 1) - base_row;
-      const uint32_t off = (uint32_t)(row * (int)q_rs + Swz::chunk(r, chunk % Swz::CH) * 8) * 2u;
-      lds_buffer_load16(qr, off, Qw + (i * 2 + grp) * 64 * 8);
+      const int g = Swz::chunk(r, chunk % Swz::CH);
+      const uint32_t off = (uint32_t)(row * (int)q_rs + g * 8) * 2u;
+      if (g < Dc) {
+        lds_buffer_load16(qr, off, Qw + (i * 2 + grp) * 64 * 8);
+      } else {
+        store16(Qw + ((i * 2 + grp) * 64 + lane) * 8, u32x4{0, 0, 0, 0});  // past the head dimension
+      }
     }
   }
   if (n > 0) {
@@ -1387,7 +1406,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (row_ok) {
     const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
     const float w0 = a0 * inv, w1 = a1 * inv;
-    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * D;
+    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
       __builtin_amdgcn_sched_barrier(0);  // one d-block at a time: no hoisted reads
@@ -1398,7 +1417,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         u32x2 w;
         w.x = pack2<BF16>(acc[d][4 * g + 0] * w0 + o1[0] * w1, acc[d][4 * g + 1] * w0 + o1[1] * w1);
         w.y = pack2<BF16>(acc[d][4 * g + 2] * w0 + o1[2] * w1, acc[d][4 * g + 3] * w0 + o1[3] * w1);
-        *(u32x2*)(op + col) = w;
+        if (col < Dr) *(u32x2*)(op + col) = w;
       }
     }
     if (lh == 0) {
@@ -1420,7 +1439,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   // The ping-pong kernels address a sequence's K/V rows with 32-bit byte offsets and a
   // K/V row stride below 2^24 bytes.
   const bool offsets_fit =
-      (uint64_t)a.Sk * a.Hkv * D * 2u < (1ull << 32) - (1ull << 20) && (uint64_t)a.Hkv * D * 2u < (1ull << 24);
+      (uint64_t)a.Sk * a.Hkv * a.D * 2u < (1ull << 32) - (1ull << 20) && (uint64_t)a.Hkv * a.D * 2u < (1ull << 24);
   if constexpr (D == 256) {
     if (offsets_fit) {
       const int nqb = (a.Sq + kKPBM - 1) / kKPBM;
@@ -1468,7 +1487,7 @@ hipError_t launch_fwd_dt(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  switch (a.D) {
+  switch (tile_headdim(a.D)) {
     case 64: return launch_fwd_dt<64>(a, stream);
     case 128: return launch_fwd_dt<128>(a, stream);
     case 256: return launch_fwd_dt<256>(a, stream);

@@ -105,6 +105,12 @@ hipError_t launch_check_kvcache(const int32_t* cache_seqlens, const int32_t* bat
 // (FA_KVCACHE_NOALLOC_MAX_BYTES, looked up once per device on first use).
 hipError_t kvcache_scratch(void** out);
 
+// Tile width of the kernels that serve head dimension D (D % 8 == 0, 8 <= D <= 256): the
+// next of 64, 128, 256; 0 for anything else.
+constexpr int tile_headdim(int D) {
+  return (D <= 0 || D > 256 || D % 8 != 0) ? 0 : D <= 64 ? 64 : D <= 128 ? 128 : 256;
+}
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // stage_mask bit 0: preprocess, bit 1: main loop with dQ atomics, bit 2: finalize,

@@ -28,7 +28,10 @@
  *     B = number of sequences; Sq / Sk = upper bounds of the per-sequence lengths (they
  *     size the launch grid).  total_q is read on the device; the host never syncs.
  *   dtype: FA_DTYPE_FP16 or FA_DTYPE_BF16 for every 16-bit tensor; accumulation is fp32.
- *   D: 64, 128 or 256.
+ *   D (head dimension): any multiple of 8 from 8 to 256.  The kernels are built for tile
+ *   widths 64, 128 and 256; another D runs in the next wider one, its padding never read
+ *   into a result and never written (flash_attn_func docstring and README "Installation
+ *   and features": head dimensions up to 256).
  *
  * Ownership: the caller owns every buffer; the library allocates no device memory and
  * keeps no mutable global state except a thread-local last-error message and, on each

@@ -62,7 +62,8 @@ def _bwd(L, **over):
 
 INVALID = [
     (dict(Hq=6, Hkv=4), 1),                # heads not divisible
-    (dict(D=96), 2),                       # no kernel for this head dimension
+    (dict(D=100), 2),                      # head dimension not a multiple of 8
+    (dict(D=264), 2),                      # head dimension above 256
     (dict(D=512), 2),
     (dict(D=0), 1),
     (dict(dtype=7), 2),                    # unknown dtype
@@ -149,7 +150,7 @@ def _kvc(L, **over):
 
 KVC_INVALID = [
     (dict(Hq=6, Hkv=4), 1),
-    (dict(D=80), 2),
+    (dict(D=84), 2),
     (dict(dtype=3), 2),
     (dict(B=0), 1),
     (dict(Sq=0), 1),
