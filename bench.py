@@ -42,15 +42,19 @@ def log(*a):
 class Case:
     """Device-resident inputs and outputs of one workload."""
 
-    def __init__(self, n: int, with_bwd: bool):
+    def __init__(self, n, with_bwd: bool):
+        """``n``: a reference workload number, or a synth.Workload."""
         import torch
         from exact_tiled_attention_02_amd import fa, synth
-        self.w, x = synth.draw_config(n)
+        if isinstance(n, int):
+            self.w, x = synth.draw_config(n)
+        else:
+            self.w, x = n, synth.make_inputs(n)
         self.w.backward = with_bwd
         d = {k: v.cuda() for k, v in x.items()}
         if with_bwd and "do" not in d:
             import numpy as np
-            rng = np.random.default_rng(1000 + n)
+            rng = np.random.default_rng(1000 + self.w.seed)
             d["do"] = synth._cast(rng.standard_normal(tuple(d["q"].shape), dtype=np.float32), self.w.dtype).cuda()
         self.d = d
         self.out = torch.empty_like(d["q"])
@@ -314,6 +318,26 @@ def main():
                 del g
             log(f"[bench] {cn.w.name} forward {tn * 1e6:.1f} us -> {detail[cn.w.name]['fwd_tflops']:.1f} TFLOPS")
             del cn
+        torch.cuda.empty_cache()
+
+    if not args.skip_gqa:
+        # head dimension 256 forward + backward: B=1, H=16, S=8192, causal, bf16
+        from exact_tiled_attention_02_amd import synth
+        c6 = Case(synth.Workload("fwdbwd_causal_b1_h16_s8192_d256_bf16", 1, 16, 16, 8192, 8192, 256, "bf16", True,
+                                 backward=True, seed=6), with_bwd=True)
+        for _ in range(max(1, W // 4)):
+            c6.step()
+        n = max(3, K // 4)
+        t6f = time_launches(c6.fwd, n)
+        t6b = time_launches(lambda: c6.bwd_stage(0), n)
+        detail[c6.w.name] = {
+            "fwd_tflops": c6.fwd_flops / t6f / 1e12, "fwd_pct_peak": 100 * c6.fwd_flops / t6f / 1e12 / PEAK_TFLOPS,
+            "bwd_tflops": c6.bwd_flops / t6b / 1e12, "bwd_pct_peak": 100 * c6.bwd_flops / t6b / 1e12 / PEAK_TFLOPS,
+            "fwd_us": t6f * 1e6, "bwd_us": t6b * 1e6,
+        }
+        log(f"[bench] D=256 S=8192 forward {t6f * 1e6:.1f} us -> {detail[c6.w.name]['fwd_tflops']:.1f} TFLOPS; "
+            f"backward {t6b * 1e6:.1f} us -> {detail[c6.w.name]['bwd_tflops']:.1f} TFLOPS")
+        del c6
         torch.cuda.empty_cache()
 
     if not args.skip_decode:

@@ -210,26 +210,35 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   };
 
   if (nsteps > 0) fetch(0, 0);
-  // K tile (all 128 keys) in LDS for dQ = dS K.
+  // K tile (all 128 keys, rows clamped to the sequence) in LDS, for S = Q K^T (row reads)
+  // and dQ = dS K (transposed reads), by buffer loads from the block's first key; chunks
+  // past the head dimension get an offset beyond the resource's extent and read as zeros
+  // (lane offsets of real chunks stay below 128 rows * Hkv * D * 2 < 2^31 bytes).
+  {
+    const size_t kfirst = (size_t)(k_start + k0) * k_rs + (size_t)hk * Dr;
+    const size_t k_rows = VARLEN ? (size_t)load_uniform(a.cu_k + a.B) : (size_t)a.B * a.Sk;
+    const auto kr = make_rsrc((const uint16_t*)a.k + kfirst, min(bytes_left(k_rows * k_rs, kfirst, 2u), 0x7fffffffu));
 #pragma unroll
-  for (int i = 0; i < kBwdBN * D / 8 / 256; ++i) {
-    const int first = (i * kBwdWaves + wave) * 64;
-    const int chunk = first + lane;
-    const int r = chunk / Swz::CH;
-    const int p = chunk % Swz::CH;
-    lds_direct_load16(kp + (size_t)min(k0 + r, Lk - 1) * k_rs + src_chunk(Swz::chunk(r, p), Dc) * 8, &Ks[first * 8]);
+    for (int i = 0; i < kBwdBN * D / 8 / 256; ++i) {
+      const int first = (i * kBwdWaves + wave) * 64;
+      const int chunk = first + lane;
+      const int r = chunk / Swz::CH;
+      const int g = Swz::chunk(r, chunk % Swz::CH);
+      const uint32_t off = g < Dc ? (uint32_t)(min(r, Lk - 1 - k0) * (int)k_rs + g * 8) * 2u : 0x80000000u;
+      lds_buffer_load16(kr, off, &Ks[first * 8]);
+    }
   }
 
-  // This wavefront's keys as B operands: lane holds K[key][16 s + 8 lh .. +7].
+  // This wavefront's values as B operands of dP = dO V^T: lane holds V[key][16 s + 8 lh ..
+  // +7], zero past the head dimension (the padded Q / dO chunks re-read chunk 0).  Its
+  // keys for S come from the K tile in LDS (registers for both would not fit beside the
+  // 256 accumulators of dK and dV).
   const bool key_ok = my_key < Lk;
-  Frag8 kf[NS], vf[NS];
+  Frag8 vf[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    // zero past the head dimension (the padded Q / dO chunks re-read chunk 0)
-    const bool in = key_ok && s * 16 + lh * 8 < Dr;
-    kf[s].v = in ? load16(kp + (size_t)my_key * k_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
-    vf[s].v = in ? load16(vp + (size_t)my_key * k_rs + s * 16 + lh * 8) : u32x4{0, 0, 0, 0};
-  }
+  for (int s = 0; s < NS; ++s)
+    vf[s].v = key_ok && s * 16 + lh * 8 < Dr ? load16(vp + (size_t)my_key * k_rs + s * 16 + lh * 8)
+                                             : u32x4{0, 0, 0, 0};
   f32x16 dkt[ND], dvt[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) {
@@ -256,11 +265,12 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      Frag8 qa, ga;
+      Frag8 qa, ga, kf;
       const int off = Swz::row_elem(li, st * 2 + lh);
       qa.v = load16(Q + off);
       ga.v = load16(dO + off);
-      s = mfma32x32x16<BF16>(qa, kf[st], s);
+      kf.v = load16(Ks + wave * 32 * D + off);  // key row wave*32 + li: the same swizzle as row li
+      s = mfma32x32x16<BF16>(qa, kf, s);
       dp = mfma32x32x16<BF16>(ga, vf[st], dp);
     }
     // P and dS / scale (the scale is applied to dK at its store and to dQ in the finalize).
