@@ -244,6 +244,8 @@ def main():
     ap.add_argument("--skip-decode", action="store_true", help="skip the KV-cache decode detail")
     ap.add_argument("--copy-calibration", action="store_true", help="only run a 512 MiB device copy (counter scale)")
     ap.add_argument("--sweep", action="store_true", help="only run the head-dim / seqlen sweep (one JSON line each)")
+    ap.add_argument("--atomic-rate", action="store_true",
+                    help="only run the fp32 atomic-rate measurement program (one JSON line per variant)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -251,6 +253,10 @@ def main():
     if args.sweep:
         sweep(args.steps, args.warmup)
         return
+    if args.atomic_rate:
+        import subprocess
+        prog = os.path.join(ROOT, "exact_tiled_attention_02_amd", "atomic_rate")
+        sys.exit(subprocess.run([prog]).returncode)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "
               f"see the design notes on sharding)", file=sys.stderr)
@@ -374,6 +380,9 @@ def main():
     pre_bytes = B * S * H * (2 * D * 2 + D * 4 + 4)   # read O, dO (16-bit); write fp32 acc zeros + Dsum
     fin_bytes = B * S * H * D * (4 + 2)               # read fp32 acc, write dQ
     main_tflops = c5.bwd_flops / t_main / 1e12
+    # fp32 dQ atomics of the main loop: one per (query row, head, column, 256-key block the row sees)
+    kb = 256
+    n_atomics = B * H * D * sum(S - min(S, j * kb) for j in range((S + kb - 1) // kb))
     detail[c5.w.name] = {
         "fwd_tflops": c5.fwd_flops / t_fwd / 1e12,
         "fwd_pct_peak": 100 * c5.fwd_flops / t_fwd / 1e12 / PEAK_TFLOPS,
@@ -382,6 +391,7 @@ def main():
         "fwd_us": t_fwd * 1e6, "bwd_pre_us": t_pre * 1e6, "bwd_main_us": t_main * 1e6, "bwd_fin_us": t_fin * 1e6,
         "bwd_pre_gbs": pre_bytes / t_pre / 1e9, "bwd_fin_gbs": fin_bytes / t_fin / 1e9,
         "bwd_deterministic_us": t_det * 1e6, "bwd_deterministic_tflops": c5.bwd_flops / t_det / 1e12,
+        "bwd_main_dq_atomics": n_atomics,
     }
     del c5
     torch.cuda.empty_cache()

@@ -854,7 +854,7 @@ constexpr int kDqBM = 32 * kDqWaves;
 constexpr int kDqBN = 64;
 
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
-__global__ __launch_bounds__(256) void bwd_dq_pass_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_pass_kernel(BwdArgs a) {
   if (debug_stop(a.dbg)) return;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
