@@ -219,6 +219,16 @@ size_t fa_bwd_workspace_bytes(int B, int Sq, int Hq, int D) {
 
 namespace {
 
+// Stages of a whole backward: preprocess (1), then either the main loop with dQ atomics (2)
+// and the finalize (4), or the main loop without dQ followed by the dQ pass (8).  Above a
+// 128-wide tile the atomic route is the slower one (its main loop covers 128 keys per
+// workgroup, so it issues one fp32 atomic per dQ element per 128 keys, and the memory-side
+// atomic rate bounds it: B=1 H=16 S=8192 D=256 causal 5.3 ms against 3.1 ms for the two
+// passes), so there the two-pass route serves the default backward too.
+int full_bwd_stages(int D, bool deterministic) {
+  return deterministic || fa::tile_headdim(D) > 128 ? (1 | 8) : 7;
+}
+
 int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, const void* v, const void* out,
              const float* lse, void* dq, void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv, int D,
              float scale, int causal, int window_left, int window_right, const float* alibi_slopes,
@@ -283,8 +293,8 @@ int fa_bwd(const void* dout, const void* q, const void* k, const void* v, const 
            void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, int causal,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, void* workspace,
            size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(7, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1, -1, nullptr, 0,
-                  cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
+  return bwd_impl(full_bwd_stages(D, false), dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale,
+                  causal, -1, -1, nullptr, 0, cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_deterministic(const void* dout, const void* q, const void* k, const void* v, const void* out,
@@ -312,7 +322,7 @@ int fa_bwd_ex(const void* dout, const void* q, const void* k, const void* v, con
               int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride,
               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, int deterministic,
               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(deterministic ? (1 | 8) : 7, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale,
+  return bwd_impl(full_bwd_stages(D, deterministic != 0), dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale,
                   causal, window_left, window_right, alibi_slopes, alibi_batch_stride, cu_seqlens_q, cu_seqlens_k,
                   dtype, workspace, workspace_bytes, stream);
 }

@@ -124,8 +124,9 @@ size_t fa_bwd_workspace_bytes(int B, int Sq, int Hq, int D);
  * stored).  Other arguments as for fa_fwd.  `workspace` (16-byte aligned) must hold
  * fa_bwd_workspace_bytes(B, Sq, Hq, D) bytes; its contents on entry do not matter.
  * dq, dk, dv are fully overwritten (rows beyond a varlen sequence are not touched).
- * dq is accumulated with fp32 atomics, so the result may differ in the last bits from
- * run to run; the forward is bitwise deterministic.
+ * For D <= 128, dq is accumulated with fp32 atomics, so the result may differ in the last
+ * bits from run to run; for D > 128 fa_bwd runs the scheme of fa_bwd_deterministic, which
+ * is the faster one there.  The forward is bitwise deterministic.
  */
 int fa_bwd(const void* dout, const void* q, const void* k, const void* v,
            const void* out, const float* lse, void* dq, void* dk, void* dv,
@@ -139,7 +140,7 @@ int fa_bwd(const void* dout, const void* q, const void* k, const void* v,
  * atomics, so dq, dk and dv are bitwise identical from run to run (the pages' README
  * offers a deterministic backward: changelog entry 2.4 and the `deterministic`
  * argument of the flash_attn_func docstring).  It recomputes the scores and dP once more,
- * so it is slower than fa_bwd.
+ * so for D <= 128 it is slower than fa_bwd; for D > 128 the two calls run the same kernels.
  */
 int fa_bwd_deterministic(const void* dout, const void* q, const void* k, const void* v,
                          const void* out, const float* lse, void* dq, void* dk, void* dv,
@@ -170,9 +171,11 @@ int fa_bwd_ex(const void* dout, const void* q, const void* k, const void* v,
  *          (its key-block queue is emptied by stage 1 and again at its own end, so it
  *          may be repeated on its own after a complete stage 1 or stage 2);
  * stage 3: finalize -- dq = scale * accumulator, in the input dtype.
- * fa_bwd is stages 1, 2, 3 in this order on one stream; a stage reads what the earlier
- * stages left in the workspace.  Arguments, checks and errors as for fa_bwd; a stage
- * outside 1..3 returns FA_ERR_INVALID_ARGUMENT.
+ * For D <= 128, fa_bwd is stages 1, 2, 3 in this order on one stream; a stage reads what
+ * the earlier stages left in the workspace.  (For D > 128 fa_bwd takes the atomic-free
+ * route of fa_bwd_deterministic instead; stages 1, 2, 3 still compute the same gradients
+ * there, with atomics.)  Arguments, checks and errors as for fa_bwd; a stage outside 1..3
+ * returns FA_ERR_INVALID_ARGUMENT.
  */
 int fa_bwd_stage(int stage, const void* dout, const void* q, const void* k, const void* v,
                  const void* out, const float* lse, void* dq, void* dk, void* dv,

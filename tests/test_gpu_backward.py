@@ -202,6 +202,19 @@ def test_main_loop_repeated_alone(shape):
         check_grads(w, x, dq1, dk1, dv1)
 
 
+@pytest.mark.parametrize("D", [256, 192])
+def test_staged_atomic_route_wide_heads(D):
+    """Above a 128-wide tile fa_bwd takes the atomic-free route; stages 1, 2, 3 still run
+    the main loop with dQ atomics there, and give the same gradients."""
+    w = W(f"bwd_staged_d{D}", 2, 4, 2, 300, 333, D, "bf16", True, seed=33)
+    say(f"bwd staged atomic route D={D}")
+    x, d, (dq, dk, dv), args = _setup(w)
+    for stage in (1, 2, 3):
+        fa.fa_bwd_stage(stage, *args, causal=True)
+    torch.cuda.synchronize()
+    print(check_grads(w, x, dq, dk, dv))
+
+
 def test_backward_graph_replays():
     """The whole backward captured in a HIP graph (no memset nodes; the queue counters are
     reset by the kernels themselves) and replayed several times, with eager work between
