@@ -246,6 +246,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="only run the head-dim / seqlen sweep (one JSON line each)")
     ap.add_argument("--atomic-rate", action="store_true",
                     help="only run the fp32 atomic-rate measurement program (one JSON line per variant)")
+    ap.add_argument("--lds-rate", action="store_true",
+                    help="only run the LDS read-rate measurement program (one JSON line per read form)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -253,9 +255,9 @@ def main():
     if args.sweep:
         sweep(args.steps, args.warmup)
         return
-    if args.atomic_rate:
+    if args.atomic_rate or args.lds_rate:
         import subprocess
-        prog = os.path.join(ROOT, "exact_tiled_attention_02_amd", "atomic_rate")
+        prog = os.path.join(ROOT, "exact_tiled_attention_02_amd", "atomic_rate" if args.atomic_rate else "lds_rate")
         sys.exit(subprocess.run([prog]).returncode)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "

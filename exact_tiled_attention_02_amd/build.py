@@ -16,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa.so")
 ATOMIC_RATE = os.path.join(PKG, "atomic_rate")
+LDS_RATE = os.path.join(PKG, "lds_rate")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_check.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -56,8 +57,9 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     tmp = LIB + ".tmp"
     logs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs))
     os.replace(tmp, LIB)
-    # the measurement program of the fp32 atomic rate (not part of the library)
-    logs.append(_run([HIPCC] + FLAGS + ["-x", "hip", os.path.join(CSRC, "atomic_rate.hip"), "-o", ATOMIC_RATE]))
+    # the measurement programs of the fp32 atomic rate and the LDS read rate (not part of the library)
+    for src, prog in (("atomic_rate.hip", ATOMIC_RATE), ("lds_rate.hip", LDS_RATE)):
+        logs.append(_run([HIPCC] + FLAGS + ["-x", "hip", os.path.join(CSRC, src), "-o", prog]))
     if verbose:
         for log in logs:
             if log.strip():
