@@ -138,8 +138,11 @@ __device__ __forceinline__ void lds_direct_load4(const void* gptr, void* lds_bas
 // (including direct global->LDS loads).
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Wait until at most N vector-memory operations of this wavefront are outstanding
-// (they complete in issue order), leaving LDS and export counters alone.
+// Wait until at most N vector-memory operations of this wavefront are outstanding,
+// leaving LDS and export counters alone.  Loads complete in issue order among themselves,
+// so with only loads in flight N > 0 means "all but the last N have landed".  Stores and
+// atomics share the counter but are not ordered against loads: while any is in flight,
+// only N = 0 says which loads have landed.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
