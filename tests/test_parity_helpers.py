@@ -3,6 +3,7 @@ chunked all-rows evaluation must give exactly the oracle's whole-head forward, a
 report of elements over the bar must count and measure them."""
 
 import numpy as np
+import torch
 
 from exact_tiled_attention_02_amd import synth
 from oracle import attention_fp64 as orc
@@ -44,3 +45,22 @@ def test_excess_report_counts_and_ulps():
     assert r.startswith("2 elements over 0.01 (2 with |O_ref| >= 4)")
     assert "1.00..2.00 ulp" in r
     assert excess_report(ref, ref, 1e-2, "bf16") == "no element over the bar"
+
+
+def test_lowp_baseline_formula_in_fp64():
+    """The low-precision baseline's graph, run in fp64, is the oracle's definition: same
+    mask alignment, GQA map, scale and gradients (so only its roundings differ)."""
+    from tests._lowp_baseline import attention_lowp
+    rng = np.random.default_rng(7)
+    for (B, Hq, Hkv, Sq, Sk, D, causal) in [(2, 4, 2, 9, 6, 8, True), (1, 3, 1, 5, 11, 16, True),
+                                            (1, 2, 2, 7, 7, 8, False)]:
+        q = rng.standard_normal((B, Sq, Hq, D))
+        k = rng.standard_normal((B, Sk, Hkv, D))
+        v = rng.standard_normal((B, Sk, Hkv, D))
+        do = rng.standard_normal((B, Sq, Hq, D))
+        o, g = attention_lowp(*(torch.from_numpy(a) for a in (q, k, v, do)), causal=causal)
+        o_ref, _ = orc.forward(q, k, v, causal=causal)
+        g_ref = orc.backward(do, q, k, v, causal=causal)
+        assert np.abs(o.numpy() - o_ref).max() < 1e-12
+        for a, b in zip(g, g_ref):
+            assert np.abs(a.numpy() - b).max() < 1e-11
