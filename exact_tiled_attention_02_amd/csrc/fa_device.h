@@ -57,6 +57,20 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
+// acc + lo + hi of two packed 16-bit values, in fp32 (one v_dot2 against (1, 1)).
+template <bool BF16>
+__device__ __forceinline__ float sum2(uint32_t two, float acc) {
+  if constexpr (BF16) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, two), one, acc, false);
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, two), one, acc, false);
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ float to_f32(uint16_t bits) {
   if constexpr (BF16) {

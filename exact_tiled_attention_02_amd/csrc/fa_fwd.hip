@@ -465,6 +465,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 // after which stage j+2 may be read.  The query rows live in LDS too (each wavefront its
 // own 32 rows, read with the same offsets as a K tile), which leaves the registers to the
 // accumulators and to operand reads issued a few products ahead.
+// How far a row maximum may outgrow the exponent reference (exp2 units) before the
+// reference moves and the accumulator is rescaled: probabilities stay below 2^8.
+constexpr float kLazyRef = 8.f;
 constexpr int kPPWaves = 8;
 constexpr int kPPBM = 32 * kPPWaves;  // query rows per workgroup
 constexpr int kPPBN = 64;             // keys per tile
@@ -636,8 +639,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x16 acc[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;  // exponent reference of this lane's row (exp2 units / c)
+  float l_run = 0.f;        // sum of the probabilities in fp32 (for the LSE)
+  float lr_run = 0.f;       // sum of the same probabilities rounded to 16 bits (for O)
   const float c = a.scale_log2;
   constexpr float kLog2e = 1.4426950408889634f;
   float sl2 = 0.f;
@@ -657,13 +661,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x16 s[2];           // S^T of the current tile: M phase -> X phase
   Frag8 pf[4];           // P^T of the previous tile: X phase -> next M phase
   bool pv_live = false;  // pf holds probabilities to add
-  // Where the output accumulator is rescaled when a row maximum grows: at D = 64 in the
-  // next M phase, among its S^T products (that phase has half the products of the X phase's
-  // length, and the multiplies fit between them; 5 % faster), at D = 128 in the X phase,
-  // only when some row's factor differs from 1 (the M phase has no room there: 3-5 %
-  // slower when moved).  Multiplying by exactly 1.0f changes nothing either way.
-  constexpr bool kRescaleInM = D <= 64;
-  float alpha_p = 1.f;   // kRescaleInM: rescale of the accumulator due before that product
 
   // M phase on stage buffer BI: S^T(j) (when the tile is live for this wavefront) and the
   // P V product of the previous tile.  Alone on the matrix pipe, the wavefront has to hide
@@ -725,25 +722,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr bool FUSED = decltype(fused_tag)::value;
     const uint16_t* K = kbuf(bi);
     const uint16_t* V = vbuf(bi);
-    // kRescaleInM: the previous X phase's factor is applied here, among the S^T products.
     if constexpr (FUSED) {
       s_part(K);
-      if constexpr (kRescaleInM) {
-#pragma unroll
-        for (int d = 0; d < ND; ++d) acc[d] *= alpha_p;
-      }
       pv_part(V);
-      read_schedule(Idx<2 * NS + 4 * ND>{}, Idx<3 * NS + 8 * ND>{}, Idx<0>{}, Idx<kRescaleInM ? 16 * ND : 0>{});
+      read_schedule(Idx<2 * NS + 4 * ND>{}, Idx<3 * NS + 8 * ND>{}, Idx<0>{}, Idx<0>{});
     } else {
       if (s_live) {
         s_part(K);
         read_schedule(Idx<2 * NS>{}, Idx<3 * NS>{}, Idx<0>{}, Idx<0>{});
       }
       if (pv_live) {
-        if constexpr (kRescaleInM) {
-#pragma unroll
-          for (int d = 0; d < ND; ++d) acc[d] *= alpha_p;
-        }
         pv_part(V);
         read_schedule(Idx<4 * ND>{}, Idx<8 * ND>{}, Idx<1>{}, Idx<0>{});
       }
@@ -760,7 +748,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr bool MASK = decltype(mask_tag)::value;
     load_stage(next, kbuf(bi), vbuf(bi));
     pv_live = live;
-    alpha_p = 1.f;
     if (!live) return;
     if constexpr (ALIBI) {
       const float base = (float)(k0 + 4 * lh - row_diag);
@@ -787,12 +774,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
     mx = pair_max(mx);
-    const float m_use = (mx == -INFINITY) ? 0.f : mx;
-    float alpha;
+    // The exponent reference m_run moves only when the row maximum outgrows it by more
+    // than kLazyRef (exp2 units), or from -inf at the row's first kept key; otherwise the
+    // probabilities stay relative to it (at most 2^kLazyRef) and the accumulator needs no
+    // rescale.  (Both sides -inf: NaN compares false, the row stays empty.)
+    const bool move = (ALIBI ? mx - m_run : (mx - m_run) * c) > kLazyRef;
+    const float m_new = move ? mx : m_run;
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    float alpha = 1.f;
     float ls = 0.f;
     if constexpr (ALIBI) {
-      alpha = fast_exp2(m_run - m_use);
-      m_run = mx;
+      if (move) alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -802,8 +795,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           ls += p;
         }
     } else {
-      alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
-      m_run = mx;
+      if (move) alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
+      m_run = m_new;
       const float mc = m_use * c;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
@@ -823,27 +816,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     l_run = l_run * alpha + ls;
-    if constexpr (kRescaleInM) {
-      alpha_p = alpha;  // applied to the accumulator in the next M phase
-    } else if (__builtin_expect(__any(alpha != 1.f), 0)) {
+    if (__builtin_expect(__any(alpha != 1.f), 0)) {
 #pragma unroll
       for (int d = 0; d < ND; ++d) acc[d] *= alpha;
     }
+    float lrs = 0.f;  // sum of the rounded probabilities, the weights the P V product uses
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int sub = t >> 1, r0 = (t & 1) * 8;
       pf[t].v = u32x4{pack2<BF16>(s[sub][r0 + 0], s[sub][r0 + 1]), pack2<BF16>(s[sub][r0 + 2], s[sub][r0 + 3]),
                       pack2<BF16>(s[sub][r0 + 4], s[sub][r0 + 5]), pack2<BF16>(s[sub][r0 + 6], s[sub][r0 + 7])};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) lrs = sum2<BF16>(pf[t].v[w], lrs);
       pin(pf[t].v);
     }
-    if constexpr (kRescaleInM) {
-      pin(alpha_p);
-    } else {
+    lr_run = lr_run * alpha + lrs;
 #pragma unroll
-      for (int d = 0; d < ND; ++d) pin(acc[d]);
-    }
+    for (int d = 0; d < ND; ++d) pin(acc[d]);
     pin(m_run);
     pin(l_run);
+    pin(lr_run);
   };
 
   // Tile j of the processing order, stage buffer BI = j % 3.  The wait at the end of the
@@ -905,8 +897,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (grp == 0) phase_barrier();
 
   const float l_tot = pair_sum(l_run);
+  const float lr_tot = pair_sum(lr_run);
   if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // O is normalised by the sum of the weights its product used (the rounded P): then
+    // one dominant key yields exactly its value however far the reference lags behind.
+    const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
     uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
