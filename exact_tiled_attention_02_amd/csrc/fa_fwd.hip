@@ -1127,8 +1127,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x16 acc[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;  // exponent reference of this lane's row (exp2 units / c)
+  float l_run = 0.f;        // sum of the probabilities in fp32 (for the LSE)
+  float lr_run = 0.f;       // sum of the same probabilities rounded to 16 bits (for O)
   const float c = a.scale_log2;
   constexpr float kLog2e = 1.4426950408889634f;
   float sl2 = 0.f;
@@ -1247,12 +1248,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = pair_max(mx);
-    const float m_use = (mx == -INFINITY) ? 0.f : mx;
-    float alpha;
+    // Lazy exponent reference, as in the ping-pong kernel: it moves only when the row
+    // maximum outgrows it by more than kLazyRef (exp2 units) or leaves -inf.
+    const bool move = (ALIBI ? mx - m_run : (mx - m_run) * c) > kLazyRef;
+    const float m_new = move ? mx : m_run;
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    float alpha = 1.f;
     float ls = 0.f;
     if constexpr (ALIBI) {
-      alpha = fast_exp2(m_run - m_use);
-      m_run = mx;
+      if (move) alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(s[r] - m_use);
@@ -1260,8 +1265,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         ls += p;
       }
     } else {
-      alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
-      m_run = mx;
+      if (move) alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
+      m_run = m_new;
       const float mc = m_use * c;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -1275,17 +1280,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int d = 0; d < ND; ++d) acc[d] *= alpha;
     }
+    float lrs = 0.f;  // sum of the rounded probabilities, the weights the P V product uses
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int r0 = t * 8;
       pf[t].v = u32x4{pack2<BF16>(s[r0 + 0], s[r0 + 1]), pack2<BF16>(s[r0 + 2], s[r0 + 3]),
                       pack2<BF16>(s[r0 + 4], s[r0 + 5]), pack2<BF16>(s[r0 + 6], s[r0 + 7])};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) lrs = sum2<BF16>(pf[t].v[w], lrs);
       pin(pf[t].v);
     }
+    lr_run = lr_run * alpha + lrs;
 #pragma unroll
     for (int d = 0; d < ND; ++d) pin(acc[d]);
     pin(m_run);
     pin(l_run);
+    pin(lr_run);
   };
 
   // Step i of this group: tile j = 2 i + grp of the processing order, item j, buffer
@@ -1355,6 +1365,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // once all wavefronts are past the barrier): group 1 writes its accumulator, max and
   // sum; group 0 rescales both to the larger max, adds, and stores.
   const float l_tot = pair_sum(l_run);
+  const float lr_tot = pair_sum(lr_run);
   __syncthreads();
   float* xa;
   float* xb;
@@ -1371,7 +1382,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     xa = (float*)Qs;
     xb = (float*)Qs + TILE / 2;
   }
-  float* xs = (float*)Qs + TILE + pr * 128;  // max, sum of the pair's group-1 wavefront
+  float* xs = (float*)Qs + TILE + pr * 192;  // max, sums of the pair's group-1 wavefront
   if (grp == 1) {
 #pragma unroll
     for (int d = 0; d < ND; ++d)
@@ -1382,10 +1393,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     xs[lane] = m_run;
     xs[64 + lane] = l_tot;
+    xs[128 + lane] = lr_tot;
   }
   __syncthreads();
   if (grp == 1) return;
-  const float m1 = xs[lane], l1 = xs[64 + lane];
+  const float m1 = xs[lane], l1 = xs[64 + lane], lr1 = xs[128 + lane];
   const float m = fmaxf(m_run, m1);
   float a0 = 0.f, a1 = 0.f;
   if (m != -INFINITY) {
@@ -1398,8 +1410,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   const float l_all = l_tot * a0 + l1 * a1;
+  const float lr_all = lr_tot * a0 + lr1 * a1;
   if (row_ok) {
-    const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
+    // O is normalised by the sum of the weights its products used (the rounded P).
+    const float inv = lr_all > 0.f ? 1.f / lr_all : 0.f;
     const float w0 = a0 * inv, w1 = a1 * inv;
     uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * Dr;
 #pragma unroll
