@@ -925,10 +925,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_pass_kernel(BwdArgs a) {
     const int r = chunk / Swz::CH;
     foff[i] = (uint32_t)(r * (int)k_rs + src_chunk(Swz::chunk(r, chunk % Swz::CH), Dc) * 8) * 2u;
   }
+  // Buffer-form direct loads from the tile's first key (the flat form would make the
+  // compiler wait for every LDS read of the loop with lgkmcnt(0)).
+  const size_t k_rows = VARLEN ? (size_t)load_uniform(a.cu_k + a.B) : (size_t)a.B * a.Sk;
   auto fetch = [&](int kb, uint16_t* __restrict__ Kd, uint16_t* __restrict__ Vd) {
     const int k0 = kb * kDqBN;
-    const uint16_t* kt = kp + (size_t)k0 * k_rs;
-    const uint16_t* vt = vp + (size_t)k0 * k_rs;
+    const size_t kfirst = (size_t)(k_start + k0) * k_rs + (size_t)hk * Dr;
+    const uint32_t kbytes = bytes_left(k_rows * k_rs, kfirst, 2u);
+    const auto kr = make_rsrc((const uint16_t*)a.k + kfirst, kbytes);
+    const auto vr = make_rsrc((const uint16_t*)a.v + kfirst, kbytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int first = (i * kDqWaves + wave) * 64;
@@ -938,8 +943,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_pass_kernel(BwdArgs a) {
         const int r = chunk / Swz::CH;
         off = (uint32_t)(min(r, Lk - 1 - k0) * (int)k_rs + src_chunk(Swz::chunk(r, chunk % Swz::CH), Dc) * 8) * 2u;
       }
-      lds_direct_load16(kt, off, Kd + first * 8);
-      lds_direct_load16(vt, off, Vd + first * 8);
+      lds_buffer_load16(kr, off, Kd + first * 8);
+      lds_buffer_load16(vr, off, Vd + first * 8);
     }
   };
   if (kb_begin < kb_end) fetch(kb_begin, K0, V0);
@@ -998,15 +1003,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_pass_kernel(BwdArgs a) {
       for (int sub = 0; sub < 2; ++sub) {
         s[sub] = f32x16{};
         dp[sub] = f32x16{};
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
+      }
+      {
+        // S^T and dP^T: op o = (sub, st), its K and V row reads issued RA ops ahead in
+        // fenced order (left to itself the scheduler sinks each read down to its product).
+        constexpr int RA = 2, NO = 2 * NS;
+        Frag8 kf[RA], vf[RA];
+        auto issue = [&](auto o_tag) __attribute__((always_inline)) {
+          constexpr int o = decltype(o_tag)::value, sl = o % RA, sub = o / NS, st = o % NS;
           const int ro = (sub * 32 + li) * D + ((st * 2) ^ ryo) * 8;
-          Frag8 kf, vf;
-          kf.v = load16(K + ro);
-          vf.v = load16(V + ro);
-          s[sub] = mfma32x32x16<BF16>(kf, qf[st], s[sub]);
-          dp[sub] = mfma32x32x16<BF16>(vf, gf[st], dp[sub]);
-        }
+          kf[sl].v = load16(K + ro);
+          vf[sl].v = load16(V + ro);
+        };
+        static_for<0, RA>([&](auto o) __attribute__((always_inline)) { issue(o); });
+        static_for<0, NO>([&](auto o_tag) __attribute__((always_inline)) {
+          constexpr int o = decltype(o_tag)::value, sl = o % RA, sub = o / NS, st = o % NS;
+          __builtin_amdgcn_sched_barrier(0);
+          s[sub] = mfma32x32x16<BF16>(kf[sl], qf[st], s[sub]);
+          dp[sub] = mfma32x32x16<BF16>(vf[sl], gf[st], dp[sub]);
+          if constexpr (o + RA < NO) issue(Idx<o + RA>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (__builtin_expect(mask, 0)) {
 #pragma unroll
@@ -1035,16 +1052,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_pass_kernel(BwdArgs a) {
                         pack2<BF16>(s[sub][r0 + 4], s[sub][r0 + 5]), pack2<BF16>(s[sub][r0 + 6], s[sub][r0 + 7])};
       }
       const int b0 = opaque(trb[0]), b1 = opaque(trb[1]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
+      {
+        // dQ^T += K^T dS^T: op o = (t, d), transposed K reads RA ops ahead, fenced.
+        constexpr int RA = 2, NO = 4 * ND;
+        Frag8 kt[RA];
+        auto issue = [&](auto o_tag) __attribute__((always_inline)) {
+          constexpr int o = decltype(o_tag)::value, sl = o % RA, t = o / ND, d = o % ND;
           const u32x2 lo = lds_read_tr16(K + b0 + 32 * (d ^ trx[0]) + t * 16 * D);
           const u32x2 hi = lds_read_tr16(K + b1 + 32 * (d ^ trx[1]) + t * 16 * D);
-          Frag8 kt;
-          kt.v = u32x4{lo.x, lo.y, hi.x, hi.y};
-          acc[d] = mfma32x32x16<BF16>(kt, df[t], acc[d]);
-        }
+          kt[sl].v = u32x4{lo.x, lo.y, hi.x, hi.y};
+        };
+        static_for<0, RA>([&](auto o) __attribute__((always_inline)) { issue(o); });
+        static_for<0, NO>([&](auto o_tag) __attribute__((always_inline)) {
+          constexpr int o = decltype(o_tag)::value, sl = o % RA, t = o / ND, d = o % ND;
+          __builtin_amdgcn_sched_barrier(0);
+          acc[d] = mfma32x32x16<BF16>(kt[sl], df[t], acc[d]);
+          if constexpr (o + RA < NO) issue(Idx<o + RA>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     wait_all_memory();
