@@ -107,11 +107,17 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   constexpr int QT = kBwdBQ * D;    // elements of a Q or dO tile
   using Swz = DualSwizzle<D>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBwdBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][QT];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][QT];
+  // Step buffers as distinct LDS objects (double-buffered by step), so that the compiler
+  // can tell the reads of one step from the direct loads in flight into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t dO0[QT];
+  __shared__ __attribute__((aligned(16))) uint16_t dO1[QT];
   __shared__ __attribute__((aligned(16))) uint16_t dSs[kBwdBQ * SSTR];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][64];
-  __shared__ __attribute__((aligned(16))) float dsum_s[2][64];
+  __shared__ __attribute__((aligned(16))) float lse0[64];
+  __shared__ __attribute__((aligned(16))) float lse1[64];
+  __shared__ __attribute__((aligned(16))) float dsum0[64];
+  __shared__ __attribute__((aligned(16))) float dsum1[64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -185,14 +191,25 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   const int nsteps = G * nqs;
   float sl_next = 0.f;  // ALiBi slope (exp2 units) of the step fetched last
 
-  // Direct global->LDS fetch of step it's Q, dO tiles and per-row LSE, Dsum.  Rows past
-  // the end of the sequence re-read its last row (they are masked to P = 0).
-  auto fetch = [&](int it, int buf) {
+  // Extents of the arrays the fetch addresses: q / dout hold total_q rows (B * Sq when
+  // padded), the LSE Hq * total_q (B * Hq * Sq) values, Dsum B * Sq rows of Hq.
+  const size_t q_rows = VARLEN ? (size_t)load_uniform(a.cu_q + a.B) : (size_t)a.B * a.Sq;
+  const size_t lse_total = VARLEN ? (size_t)a.Hq * q_rows : (size_t)a.B * a.Hq * a.Sq;
+  const size_t ws_rows = (size_t)a.B * a.Sq;
+
+  // Direct global->LDS fetch of step it's Q, dO tiles and per-row LSE, Dsum, in the buffer
+  // form (the flat form would make the compiler wait for every LDS read of the loop with
+  // lgkmcnt(0)).  Rows past the end of the sequence re-read its last row (they are masked
+  // to P = 0).
+  auto fetch = [&](int it, uint16_t* __restrict__ Qd, uint16_t* __restrict__ dOd, float* __restrict__ lsed,
+                   float* __restrict__ dsumd) {
     const int g = it / nqs;
     const int h = hk * G + g;
     const int i0 = (qb_begin + it % nqs) * kBwdBQ;
-    const uint16_t* qp = (const uint16_t*)a.q + (size_t)q_start * q_rs + (size_t)h * Dr;
-    const uint16_t* dop = (const uint16_t*)a.dout + (size_t)q_start * q_rs + (size_t)h * Dr;
+    const size_t base = (size_t)(q_start + i0) * q_rs + (size_t)h * Dr;
+    const uint32_t qbytes = bytes_left(q_rows * q_rs, base, 2u);
+    const auto qr = make_rsrc((const uint16_t*)a.q + base, qbytes);
+    const auto gr = make_rsrc((const uint16_t*)a.dout + base, qbytes);
 #pragma unroll
     for (int i = 0; i < QT / 8 / 256; ++i) {
       const int first = (i * kBwdWaves + wave) * 64;
@@ -200,16 +217,23 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       const int r = chunk / Swz::CH;
       const int p = chunk % Swz::CH;
       const uint32_t src = (uint32_t)(min(r, Lq - 1 - i0) * (int)q_rs + src_chunk(Swz::chunk(r, p), Dc) * 8) * 2u;
-      lds_direct_load16(qp + (size_t)i0 * q_rs, src, &Qs[buf][first * 8]);
-      lds_direct_load16(dop + (size_t)i0 * q_rs, src, &dOs[buf][first * 8]);
+      lds_buffer_load16(qr, src, Qd + first * 8);
+      lds_buffer_load16(gr, src, dOd + first * 8);
     }
-    const int row = min(i0 + (lane & 31), Lq - 1);
-    if (wave == 0) lds_direct_load4(a.lse + lse_row0 + (size_t)h * lse_hs + row, &lse_s[buf][0]);
-    if (wave == 1) lds_direct_load4(a.dsum + (size_t)(q_start + row) * a.Hq + h, &dsum_s[buf][0]);
+    const uint32_t rr = (uint32_t)(min(i0 + (lane & 31), Lq - 1) - i0);
+    if (wave == 0) {
+      const size_t lbase = lse_row0 + (size_t)h * lse_hs + i0;
+      lds_buffer_load4(make_rsrc(a.lse + lbase, bytes_left(lse_total, lbase, 4u)), rr * 4u, lsed);
+    }
+    if (wave == 1) {
+      const size_t dbase = (size_t)(q_start + i0) * a.Hq + h;
+      lds_buffer_load4(make_rsrc(a.dsum + dbase, bytes_left(ws_rows * a.Hq, dbase, 4u)), rr * (uint32_t)a.Hq * 4u,
+                       dsumd);
+    }
     if constexpr (ALIBI) sl_next = a.alibi[(size_t)b * a.alibi_bstride + h] * kLog2e;
   };
 
-  if (nsteps > 0) fetch(0, 0);
+  if (nsteps > 0) fetch(0, Q0, dO0, lse0, dsum0);
   // K tile (all 128 keys, rows clamped to the sequence) in LDS, for S = Q K^T (row reads)
   // and dQ = dS K (transposed reads), by buffer loads from the block's first key; chunks
   // past the head dimension get an offset beyond the resource's extent and read as zeros
@@ -252,39 +276,57 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   wait_all_memory();
   __syncthreads();
 
-  for (int it = 0; it < nsteps; ++it) {
-    const int buf = it & 1;
+  auto step = [&](int it, const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
+                  const float* __restrict__ lse_c, const float* __restrict__ dsum_c, uint16_t* __restrict__ Qn,
+                  uint16_t* __restrict__ dOn, float* __restrict__ lse_n, float* __restrict__ dsum_n) {
     const int h = hk * G + it / nqs;
     const int i0 = (qb_begin + it % nqs) * kBwdBQ;
     const float sl = sl_next;
-    if (it + 1 < nsteps) fetch(it + 1, buf ^ 1);
-    const uint16_t* Q = Qs[buf];
-    const uint16_t* dO = dOs[buf];
+    if (it + 1 < nsteps) fetch(it + 1, Qn, dOn, lse_n, dsum_n);
 
-    // S = Q K^T and dP = dO V^T (query rows x keys); lane = key, registers = rows.
+    // S = Q K^T and dP = dO V^T (query rows x keys); lane = key, registers = rows.  The
+    // row reads run RA k-steps ahead of their products, in fenced order (left to itself
+    // the scheduler sinks each read down to its product); with the dQ product (the staged
+    // atomic route) one step ahead, as more registers would spill.
     f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      Frag8 qa, ga, kf;
-      const int off = Swz::row_elem(li, st * 2 + lh);
-      qa.v = load16(Q + off);
-      ga.v = load16(dO + off);
-      kf.v = load16(Ks + wave * 32 * D + off);  // key row wave*32 + li: the same swizzle as row li
-      s = mfma32x32x16<BF16>(qa, kf, s);
-      dp = mfma32x32x16<BF16>(ga, vf[st], dp);
+    {
+      constexpr int RA = DQ ? 1 : 2;
+      Frag8 qa[RA], ga[RA], kf[RA];
+      auto issue = [&](auto st_tag) __attribute__((always_inline)) {
+        constexpr int st = decltype(st_tag)::value, sl2 = st % RA;
+        const int off = Swz::row_elem(li, st * 2 + lh);
+        qa[sl2].v = load16(Q + off);
+        ga[sl2].v = load16(dO + off);
+        kf[sl2].v = load16(Ks + wave * 32 * D + off);  // key row wave*32 + li: the same swizzle as row li
+      };
+      static_for<0, RA>([&](auto st) __attribute__((always_inline)) { issue(st); });
+      static_for<0, NS>([&](auto st_tag) __attribute__((always_inline)) {
+        constexpr int st = decltype(st_tag)::value, sl2 = st % RA;
+        __builtin_amdgcn_sched_barrier(0);
+        s = mfma32x32x16<BF16>(qa[sl2], kf[sl2], s);
+        dp = mfma32x32x16<BF16>(ga[sl2], vf[st], dp);
+        if constexpr (st + RA < NS) issue(Idx<st + RA>{});
+      });
+      __builtin_amdgcn_sched_barrier(0);
     }
     // P and dS / scale (the scale is applied to dK at its store and to dQ in the finalize).
+    // Register r = 4 g4 + j holds row 8 g4 + 4 lh + j: its LSE and -Dsum come as vectors.
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rl = 8 * (r >> 2) + 4 * lh + (r & 3);
-      const int row = i0 + rl;
-      bool keep = key_ok && row < Lq;
-      if constexpr (MASKED) keep = keep && row >= rmin && row <= rmax;
-      float bias = -lse_s[buf][rl] * kLog2e;
-      if constexpr (ALIBI) bias = fmaf(-sl, fabsf((float)(row + diag - my_key)), bias);
-      const float p = keep ? fast_exp2(fmaf(s[r], c, bias)) : 0.f;
-      s[r] = p;
-      dp[r] = p * (dp[r] + dsum_s[buf][rl]);  // dS / scale (the workspace holds -Dsum)
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 l4 = *(const f32x4*)(lse_c + 8 * g4 + 4 * lh);
+      const f32x4 d4 = *(const f32x4*)(dsum_c + 8 * g4 + 4 * lh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g4 + j;
+        const int row = i0 + 8 * g4 + 4 * lh + j;
+        bool keep = key_ok && row < Lq;
+        if constexpr (MASKED) keep = keep && row >= rmin && row <= rmax;
+        float bias = -l4[j] * kLog2e;
+        if constexpr (ALIBI) bias = fmaf(-sl, fabsf((float)(row + diag - my_key)), bias);
+        const float p = keep ? fast_exp2(fmaf(s[r], c, bias)) : 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] + d4[j]);  // dS / scale (the workspace holds -Dsum)
+      }
     }
     Frag8 pf[2], dsf[2];
 #pragma unroll
@@ -307,11 +349,12 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
         dSs[(rl0 + 1) * SSTR + wave * 32 + li] = (uint16_t)(two >> 16);
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS.
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
+    // dV^T += dO^T P and dK^T += Q^T dS over ops (t, d), transposed reads RA ops ahead.
+    {
+      constexpr int RA = DQ ? 1 : 2, NO = 2 * ND;
+      Frag8 ga[RA], qa[RA];
+      auto issue = [&](auto o_tag) __attribute__((always_inline)) {
+        constexpr int o = decltype(o_tag)::value, sl2 = o % RA, t = o / ND, d = o % ND;
         const int row = t * 16 + tr_row;
         const int col = d * 32 + tr_col;
         const int o_lo = Swz::elem(row, col), o_hi = Swz::elem(row + 8, col);
@@ -319,12 +362,18 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
         const u32x2 g_hi = lds_read_tr16(dO + o_hi);
         const u32x2 q_lo = lds_read_tr16(Q + o_lo);
         const u32x2 q_hi = lds_read_tr16(Q + o_hi);
-        Frag8 ga, qa;
-        ga.v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
-        qa.v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
-        dvt[d] = mfma32x32x16<BF16>(ga, pf[t], dvt[d]);
-        dkt[d] = mfma32x32x16<BF16>(qa, dsf[t], dkt[d]);
-      }
+        ga[sl2].v = u32x4{g_lo.x, g_lo.y, g_hi.x, g_hi.y};
+        qa[sl2].v = u32x4{q_lo.x, q_lo.y, q_hi.x, q_hi.y};
+      };
+      static_for<0, RA>([&](auto o) __attribute__((always_inline)) { issue(o); });
+      static_for<0, NO>([&](auto o_tag) __attribute__((always_inline)) {
+        constexpr int o = decltype(o_tag)::value, sl2 = o % RA, t = o / ND, d = o % ND;
+        __builtin_amdgcn_sched_barrier(0);
+        dvt[d] = mfma32x32x16<BF16>(ga[sl2], pf[t], dvt[d]);
+        dkt[d] = mfma32x32x16<BF16>(qa[sl2], dsf[t], dkt[d]);
+        if constexpr (o + RA < NO) issue(Idx<o + RA>{});
+      });
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (DQ) __syncthreads();  // dS of all four wavefronts is in LDS
 
@@ -355,6 +404,11 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     }
     wait_all_memory();  // the prefetched step has landed in LDS
     __syncthreads();    // every wavefront is done with this step's tiles and dS
+  };
+  for (int it = 0; it < nsteps; ++it) {
+    const bool odd = it & 1;
+    step(it, odd ? Q1 : Q0, odd ? dO1 : dO0, odd ? lse1 : lse0, odd ? dsum1 : dsum0, odd ? Q0 : Q1, odd ? dO0 : dO1,
+         odd ? lse0 : lse1, odd ? dsum0 : dsum1);
   }
 
   // dK, dV: lane = key, registers = head-dimension entries.
