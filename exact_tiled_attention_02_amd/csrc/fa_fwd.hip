@@ -661,6 +661,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f32x16 s[2];           // S^T of the current tile: M phase -> X phase
   Frag8 pf[4];           // P^T of the previous tile: X phase -> next M phase
   bool pv_live = false;  // pf holds probabilities to add
+  // D = 128: lazy exponent reference (kLazyRef), the accumulator rescaled in the X phase
+  // when the reference moves, O divided by the sum of the rounded P.  D = 64: the reference
+  // follows every new row maximum and the rescale goes into the next M phase, among its
+  // S^T products (that phase has half the products of the X phase's length and room for
+  // the multiplies; with the lazy reference the extra row sum cost more than it saved
+  // there), O divided by the fp32 sum.  Multiplying by exactly 1.0f changes nothing.
+  constexpr bool kLazy = D > 64;
+  constexpr bool kRescaleInM = !kLazy;
+  float alpha_p = 1.f;  // kRescaleInM: rescale of the accumulator due before that product
 
   // M phase on stage buffer BI: S^T(j) (when the tile is live for this wavefront) and the
   // P V product of the previous tile.  Alone on the matrix pipe, the wavefront has to hide
@@ -724,14 +733,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t* V = vbuf(bi);
     if constexpr (FUSED) {
       s_part(K);
+      if constexpr (kRescaleInM) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d) acc[d] *= alpha_p;
+      }
       pv_part(V);
-      read_schedule(Idx<2 * NS + 4 * ND>{}, Idx<3 * NS + 8 * ND>{}, Idx<0>{}, Idx<0>{});
+      read_schedule(Idx<2 * NS + 4 * ND>{}, Idx<3 * NS + 8 * ND>{}, Idx<0>{}, Idx<kRescaleInM ? 16 * ND : 0>{});
     } else {
       if (s_live) {
         s_part(K);
         read_schedule(Idx<2 * NS>{}, Idx<3 * NS>{}, Idx<0>{}, Idx<0>{});
       }
       if (pv_live) {
+        if constexpr (kRescaleInM) {
+#pragma unroll
+          for (int d = 0; d < ND; ++d) acc[d] *= alpha_p;
+        }
         pv_part(V);
         read_schedule(Idx<4 * ND>{}, Idx<8 * ND>{}, Idx<1>{}, Idx<0>{});
       }
@@ -748,6 +765,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr bool MASK = decltype(mask_tag)::value;
     load_stage(next, kbuf(bi), vbuf(bi));
     pv_live = live;
+    alpha_p = 1.f;
     if (!live) return;
     if constexpr (ALIBI) {
       const float base = (float)(k0 + 4 * lh - row_diag);
@@ -774,18 +792,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
     mx = pair_max(mx);
-    // The exponent reference m_run moves only when the row maximum outgrows it by more
-    // than kLazyRef (exp2 units), or from -inf at the row's first kept key; otherwise the
-    // probabilities stay relative to it (at most 2^kLazyRef) and the accumulator needs no
-    // rescale.  (Both sides -inf: NaN compares false, the row stays empty.)
-    const bool move = (ALIBI ? mx - m_run : (mx - m_run) * c) > kLazyRef;
-    const float m_new = move ? mx : m_run;
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    float alpha = 1.f;
+    // kLazy: the exponent reference m_run moves only when the row maximum outgrows it by
+    // more than kLazyRef (exp2 units), or from -inf at the row's first kept key; otherwise
+    // the probabilities stay relative to it (at most 2^kLazyRef) and the accumulator
+    // needs no rescale.  (Both sides -inf: NaN compares false, the row stays empty.)
+    // Otherwise the reference is the running row maximum itself.
+    float m_use, alpha = 1.f;
+    if constexpr (kLazy) {
+      const bool move = (ALIBI ? mx - m_run : (mx - m_run) * c) > kLazyRef;
+      const float m_new = move ? mx : m_run;
+      m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      if (move) alpha = ALIBI ? fast_exp2(m_run - m_use) : (m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_use) * c));
+      m_run = m_new;
+    } else {
+      m_use = (mx == -INFINITY) ? 0.f : mx;
+      alpha = ALIBI ? fast_exp2(m_run - m_use) : (m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_use) * c));
+      m_run = mx;
+    }
     float ls = 0.f;
     if constexpr (ALIBI) {
-      if (move) alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -795,8 +820,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           ls += p;
         }
     } else {
-      if (move) alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - m_use) * c);
-      m_run = m_new;
       const float mc = m_use * c;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
@@ -816,7 +839,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     l_run = l_run * alpha + ls;
-    if (__builtin_expect(__any(alpha != 1.f), 0)) {
+    if constexpr (kRescaleInM) {
+      alpha_p = alpha;  // applied to the accumulator in the next M phase
+    } else if (__builtin_expect(__any(alpha != 1.f), 0)) {
 #pragma unroll
       for (int d = 0; d < ND; ++d) acc[d] *= alpha;
     }
@@ -826,16 +851,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int sub = t >> 1, r0 = (t & 1) * 8;
       pf[t].v = u32x4{pack2<BF16>(s[sub][r0 + 0], s[sub][r0 + 1]), pack2<BF16>(s[sub][r0 + 2], s[sub][r0 + 3]),
                       pack2<BF16>(s[sub][r0 + 4], s[sub][r0 + 5]), pack2<BF16>(s[sub][r0 + 6], s[sub][r0 + 7])};
+      if constexpr (kLazy) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) lrs = sum2<BF16>(pf[t].v[w], lrs);
+        for (int w = 0; w < 4; ++w) lrs = sum2<BF16>(pf[t].v[w], lrs);
+      }
       pin(pf[t].v);
     }
-    lr_run = lr_run * alpha + lrs;
+    if constexpr (kLazy) lr_run = lr_run * alpha + lrs;
+    if constexpr (kRescaleInM) {
+      pin(alpha_p);
+    } else {
 #pragma unroll
-    for (int d = 0; d < ND; ++d) pin(acc[d]);
+      for (int d = 0; d < ND; ++d) pin(acc[d]);
+    }
     pin(m_run);
     pin(l_run);
-    pin(lr_run);
+    if constexpr (kLazy) pin(lr_run);
   };
 
   // Tile j of the processing order, stage buffer BI = j % 3.  The wait at the end of the
@@ -897,11 +928,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (grp == 0) phase_barrier();
 
   const float l_tot = pair_sum(l_run);
-  const float lr_tot = pair_sum(lr_run);
+  const float lr_tot = kLazy ? pair_sum(lr_run) : 0.f;
   if (row_ok) {
-    // O is normalised by the sum of the weights its product used (the rounded P): then
-    // one dominant key yields exactly its value however far the reference lags behind.
-    const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
+    // kLazy: O is normalised by the sum of the weights its product used (the rounded P),
+    // so that one dominant key yields exactly its value however far the reference lags.
+    const float den = kLazy ? lr_tot : l_tot;
+    const float inv = den > 0.f ? 1.f / den : 0.f;
     uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * Dr;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
