@@ -105,6 +105,26 @@ def time_launches(fn, n, pre=None, post=None):
     return total / n
 
 
+def time_graph(fn, reps, n):
+    """Device time (s) per call of fn(), from n replays of a HIP graph that holds reps
+    calls.  For kernels of a few microseconds, where an event pair around one call from
+    Python also times the host's launch path (argument checks, ctypes)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    t = time_launches(g.replay, n) / reps
+    del g
+    return t
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_main_fwdbwd_b2_h16_s4096_d128_bf16.json")
 BWD_SOURCE = os.path.join(ROOT, "exact_tiled_attention_02_amd", "csrc", "fa_bwd.hip")
 
@@ -281,9 +301,11 @@ def main():
         n = max(3, K // 4)
         for _ in range(max(1, W // 4)):
             c3.bwd_stage(0)
-        t3p = time_launches(lambda: c3.bwd_stage(1), n)
+        # preprocess and finalize: device time from a graph of 10 calls; the main loop
+        # (milliseconds) per launch, each after a preprocess that resets its key-block queue
+        t3p = time_graph(lambda: c3.bwd_stage(1), 10, n)
         t3m = time_launches(lambda: c3.bwd_stage(2), n, pre=lambda: c3.bwd_stage(1))
-        t3f = time_launches(lambda: c3.bwd_stage(3), n)
+        t3f = time_graph(lambda: c3.bwd_stage(3), 10, n)
         detail[c3.w.name] = {
             "fwd_tflops": c3.fwd_flops / t3 / 1e12, "fwd_pct_peak": 100 * c3.fwd_flops / t3 / 1e12 / PEAK_TFLOPS,
             "fwd_us": t3 * 1e6,
@@ -309,21 +331,10 @@ def main():
             if n == 1:
                 # A call this small is bound by the host (argument checks, ctypes): time K
                 # launches captured in one HIP graph as well, which leaves the device time.
-                g = torch.cuda.CUDAGraph()
-                s = torch.cuda.Stream()
-                s.wait_stream(torch.cuda.current_stream())
-                with torch.cuda.stream(s):
-                    cn.fwd()
-                torch.cuda.current_stream().wait_stream(s)
-                with torch.cuda.graph(g):
-                    for _ in range(K):
-                        cn.fwd()
-                g.replay()
-                tg = time_launches(g.replay, 5) / K
+                tg = time_graph(cn.fwd, K, 5)
                 nbytes = sum(t.numel() * t.element_size() for t in (cn.d["q"], cn.d["k"], cn.d["v"], cn.out, cn.lse))
                 detail[cn.w.name].update({"fwd_us_graph": tg * 1e6, "bytes": nbytes, "gbs_graph": nbytes / tg / 1e9})
                 log(f"[bench] {cn.w.name} forward in a graph {tg * 1e6:.2f} us per call, {nbytes / tg / 1e9:.1f} GB/s")
-                del g
             log(f"[bench] {cn.w.name} forward {tn * 1e6:.1f} us -> {detail[cn.w.name]['fwd_tflops']:.1f} TFLOPS")
             del cn
         torch.cuda.empty_cache()
@@ -372,11 +383,14 @@ def main():
     value = step_flops / (ms * 1e-3) / 1e12
     log(f"[bench] step {ms:.3f} ms -> {value:.1f} TFLOPS")
 
-    # per-kernel durations (HIP events on the launch stream)
+    # per-kernel durations (HIP events on the launch stream); the preprocess and finalize
+    # (~15-25 us) also as device time from a graph of 10 calls, which the backward figure uses
     t_fwd = time_launches(c5.fwd, K)
-    t_pre = time_launches(lambda: c5.bwd_stage(1), K)
+    t_pre_launch = time_launches(lambda: c5.bwd_stage(1), K)
     t_main = time_launches(lambda: c5.bwd_stage(2), K, pre=lambda: c5.bwd_stage(1), post=lambda: c5.bwd_stage(3))
-    t_fin = time_launches(lambda: c5.bwd_stage(3), K)
+    t_fin_launch = time_launches(lambda: c5.bwd_stage(3), K)
+    t_pre = time_graph(lambda: c5.bwd_stage(1), 10, max(3, K // 4))
+    t_fin = time_graph(lambda: c5.bwd_stage(3), 10, max(3, K // 4))
     t_det = time_launches(lambda: c5.bwd_stage("deterministic"), max(3, K // 4))
     B, S, H, D = c5.w.batch, c5.w.seqlen_q, c5.w.heads_q, c5.w.headdim
     pre_bytes = B * S * H * (2 * D * 2 + D * 4 + 4)   # read O, dO (16-bit); write fp32 acc zeros + Dsum
@@ -392,6 +406,7 @@ def main():
         "bwd_pct_peak": 100 * c5.bwd_flops / (t_pre + t_main + t_fin) / 1e12 / PEAK_TFLOPS,
         "fwd_us": t_fwd * 1e6, "bwd_pre_us": t_pre * 1e6, "bwd_main_us": t_main * 1e6, "bwd_fin_us": t_fin * 1e6,
         "bwd_pre_gbs": pre_bytes / t_pre / 1e9, "bwd_fin_gbs": fin_bytes / t_fin / 1e9,
+        "bwd_pre_us_per_launch": t_pre_launch * 1e6, "bwd_fin_us_per_launch": t_fin_launch * 1e6,
         "bwd_deterministic_us": t_det * 1e6, "bwd_deterministic_tflops": c5.bwd_flops / t_det / 1e12,
         "bwd_main_dq_atomics": n_atomics,
     }
