@@ -110,6 +110,35 @@ def make_inputs(w: Workload, rng: np.random.Generator | None = None) -> dict:
     return out
 
 
+def make_inputs_on_device(w: Workload, device: str = "cuda", chunk_rows: int = 8192) -> dict:
+    """Padded q, k, v (and dO when ``w.backward``) drawn on ``device`` itself, for tensors
+    too large to draw on the host in reasonable time (K/V of several GiB).
+
+    Recipe: one ``torch.Generator(device)`` seeded with ``w.seed``; draw order q, k, v,
+    then dO; each tensor in slices of ``chunk_rows`` sequence positions (all batch
+    entries and heads of a slice at once), each slice ``torch.randn(..., float32)`` cast
+    once to the 16-bit dtype (round to nearest even).  The oracle side reads the same
+    values back from the device."""
+    if w.varlen:
+        raise ValueError("device-side draws are for padded workloads")
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    dt = DTYPES[w.dtype]
+    D = w.headdim
+
+    def draw(S, H):
+        t = torch.empty((w.batch, S, H, D), dtype=dt, device=device)
+        for s0 in range(0, S, chunk_rows):
+            s1 = min(S, s0 + chunk_rows)
+            t[:, s0:s1] = torch.randn((w.batch, s1 - s0, H, D), generator=g, dtype=torch.float32, device=device).to(dt)
+        return t
+
+    out = {"q": draw(w.seqlen_q, w.heads_q), "k": draw(w.seqlen_k, w.heads_kv), "v": draw(w.seqlen_k, w.heads_kv)}
+    if w.backward:
+        out["do"] = draw(w.seqlen_q, w.heads_q)
+    return out
+
+
 def config(n: int) -> Workload:
     """The five reference workloads; workload ``n`` is drawn with seed ``n``."""
     if n == 1:

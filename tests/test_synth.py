@@ -32,3 +32,18 @@ def test_flop_model():
     f, b = synth.flops(synth.config(3))
     assert abs(f - 4 * 2 * 32 * 8192 * 8192 * 128 / 2) < 1
     assert abs(b - 2.5 * f) < 1
+
+
+def test_device_draws_follow_their_recipe():
+    # run on the CPU generator here: same seed -> same values; slices drawn in order, each
+    # a float32 normal rounded once to the 16-bit dtype
+    w = synth.Workload("dev", 2, 4, 2, 10, 13, 8, "bf16", True, backward=True, seed=5)
+    a = synth.make_inputs_on_device(w, "cpu", chunk_rows=4)
+    b = synth.make_inputs_on_device(w, "cpu", chunk_rows=4)
+    assert [a[k].shape for k in ("q", "k", "v", "do")] == [(2, 10, 4, 8), (2, 13, 2, 8), (2, 13, 2, 8), (2, 10, 4, 8)]
+    assert all(a[k].dtype == torch.bfloat16 and torch.equal(a[k], b[k]) for k in a)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(5)
+    q0 = torch.randn((2, 4, 4, 8), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    assert torch.equal(a["q"][:, :4], q0)
+    assert not torch.equal(a["k"][:, :10], a["q"][:, :, :2])
