@@ -257,6 +257,37 @@ def make_kvcache_inputs(w: KVCacheWorkload) -> dict:
     return out
 
 
+def make_kvcache_inputs_on_device(w: KVCacheWorkload, device: str = "cuda", chunk_rows: int = 8192) -> dict:
+    """A contiguous KV cache drawn on ``device`` itself (caches of several GiB): one
+    ``torch.Generator(device)`` seeded with ``w.seed``; draw order q, k_cache, v_cache,
+    the caches in slices of ``chunk_rows`` positions (all entries and heads of a slice at
+    once), each slice ``torch.randn(..., float32)`` cast once to the 16-bit dtype.
+    ``cache_seqlens`` / ``cache_batch_idx`` come from the workload as int32 tensors."""
+    if w.page or w.alibi is not None:
+        raise ValueError("device-side draws are for contiguous caches without ALiBi")
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    dt = DTYPES[w.dtype]
+    D = w.headdim
+    n_entries = w.cache_batch if w.cache_batch is not None else w.batch
+
+    def randn(shape):
+        return torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(dt)
+
+    out = {"q": randn((w.batch, w.seqlen_q, w.heads_q, D))}
+    for name in ("k_cache", "v_cache"):
+        t = torch.empty((n_entries, w.capacity, w.heads_kv, D), dtype=dt, device=device)
+        for s0 in range(0, w.capacity, chunk_rows):
+            s1 = min(w.capacity, s0 + chunk_rows)
+            t[:, s0:s1] = randn((n_entries, s1 - s0, w.heads_kv, D))
+        out[name] = t
+    if w.lengths is not None:
+        out["cache_seqlens"] = torch.tensor(w.lengths, dtype=torch.int32, device=device)
+    if w.batch_idx is not None:
+        out["cache_batch_idx"] = torch.tensor(w.batch_idx, dtype=torch.int32, device=device)
+    return out
+
+
 def decode_workload() -> KVCacheWorkload:
     """Serving-style decode step: 16 sequences, one new token each, GQA 32:8 query/KV
     heads of 128, bf16 cache of 32768 positions per sequence, cache lengths drawn uniformly

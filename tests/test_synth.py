@@ -47,3 +47,18 @@ def test_device_draws_follow_their_recipe():
     q0 = torch.randn((2, 4, 4, 8), generator=g, dtype=torch.float32).to(torch.bfloat16)
     assert torch.equal(a["q"][:, :4], q0)
     assert not torch.equal(a["k"][:, :10], a["q"][:, :, :2])
+
+
+def test_device_kvcache_draws_follow_their_recipe():
+    w = synth.KVCacheWorkload("devkv", 3, 2, 4, 2, 8, "fp16", 20, lengths=[20, 1, 7], batch_idx=[2, 0, 1], seed=9)
+    a = synth.make_kvcache_inputs_on_device(w, "cpu", chunk_rows=8)
+    b = synth.make_kvcache_inputs_on_device(w, "cpu", chunk_rows=8)
+    assert a["q"].shape == (3, 2, 4, 8) and a["k_cache"].shape == (3, 20, 2, 8) and a["v_cache"].dtype == torch.float16
+    assert all(torch.equal(a[k], b[k]) for k in a)
+    assert a["cache_seqlens"].tolist() == [20, 1, 7] and a["cache_seqlens"].dtype == torch.int32
+    assert a["cache_batch_idx"].tolist() == [2, 0, 1]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(9)
+    q = torch.randn((3, 2, 4, 8), generator=g, dtype=torch.float32).to(torch.float16)
+    k0 = torch.randn((3, 8, 2, 8), generator=g, dtype=torch.float32).to(torch.float16)
+    assert torch.equal(a["q"], q) and torch.equal(a["k_cache"][:, :8], k0)
