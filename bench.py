@@ -84,9 +84,10 @@ class Case:
         self.bwd_stage(0)
 
 
-def time_launches(fn, n, pre=None, post=None):
+def time_launches(fn, n, pre=None, post=None, stats=None):
     """Average duration (s) of fn() over n launches, each bracketed by HIP events recorded
-    on torch's current stream -- the stream the library launches on."""
+    on torch's current stream -- the stream the library launches on.  ``stats``, a dict,
+    also receives the median and the minimum."""
     import torch
     total = 0.0
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -100,8 +101,11 @@ def time_launches(fn, n, pre=None, post=None):
         if post:
             post()
     torch.cuda.synchronize()
-    for s, e in zip(starts, ends):
-        total += s.elapsed_time(e) * 1e-3
+    ts = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
+    total = sum(ts)
+    if stats is not None:
+        stats["median"] = ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
+        stats["min"] = ts[0]
     return total / n
 
 
@@ -297,7 +301,8 @@ def main():
         c3 = Case(3, with_bwd=True)
         for _ in range(W):
             c3.fwd()
-        t3 = time_launches(c3.fwd, K)
+        st3 = {}
+        t3 = time_launches(c3.fwd, K, stats=st3)
         n = max(3, K // 4)
         for _ in range(max(1, W // 4)):
             c3.bwd_stage(0)
@@ -308,7 +313,7 @@ def main():
         t3f = time_graph(lambda: c3.bwd_stage(3), 10, n)
         detail[c3.w.name] = {
             "fwd_tflops": c3.fwd_flops / t3 / 1e12, "fwd_pct_peak": 100 * c3.fwd_flops / t3 / 1e12 / PEAK_TFLOPS,
-            "fwd_us": t3 * 1e6,
+            "fwd_us": t3 * 1e6, "fwd_us_median": st3["median"] * 1e6, "fwd_us_min": st3["min"] * 1e6,
             "bwd_tflops": c3.bwd_flops / (t3p + t3m + t3f) / 1e12,
             "bwd_pct_peak": 100 * c3.bwd_flops / (t3p + t3m + t3f) / 1e12 / PEAK_TFLOPS,
             "bwd_pre_us": t3p * 1e6, "bwd_main_us": t3m * 1e6, "bwd_fin_us": t3f * 1e6,
@@ -385,9 +390,11 @@ def main():
 
     # per-kernel durations (HIP events on the launch stream); the preprocess and finalize
     # (~15-25 us) also as device time from a graph of 10 calls, which the backward figure uses
-    t_fwd = time_launches(c5.fwd, K)
+    st_fwd, st_main = {}, {}
+    t_fwd = time_launches(c5.fwd, K, stats=st_fwd)
     t_pre_launch = time_launches(lambda: c5.bwd_stage(1), K)
-    t_main = time_launches(lambda: c5.bwd_stage(2), K, pre=lambda: c5.bwd_stage(1), post=lambda: c5.bwd_stage(3))
+    t_main = time_launches(lambda: c5.bwd_stage(2), K, pre=lambda: c5.bwd_stage(1), post=lambda: c5.bwd_stage(3),
+                           stats=st_main)
     t_fin_launch = time_launches(lambda: c5.bwd_stage(3), K)
     t_pre = time_graph(lambda: c5.bwd_stage(1), 10, max(3, K // 4))
     t_fin = time_graph(lambda: c5.bwd_stage(3), 10, max(3, K // 4))
@@ -405,6 +412,8 @@ def main():
         "bwd_tflops": c5.bwd_flops / (t_pre + t_main + t_fin) / 1e12,
         "bwd_pct_peak": 100 * c5.bwd_flops / (t_pre + t_main + t_fin) / 1e12 / PEAK_TFLOPS,
         "fwd_us": t_fwd * 1e6, "bwd_pre_us": t_pre * 1e6, "bwd_main_us": t_main * 1e6, "bwd_fin_us": t_fin * 1e6,
+        "fwd_us_median": st_fwd["median"] * 1e6, "fwd_us_min": st_fwd["min"] * 1e6,
+        "bwd_main_us_median": st_main["median"] * 1e6, "bwd_main_us_min": st_main["min"] * 1e6,
         "bwd_pre_gbs": pre_bytes / t_pre / 1e9, "bwd_fin_gbs": fin_bytes / t_fin / 1e9,
         "bwd_pre_us_per_launch": t_pre_launch * 1e6, "bwd_fin_us_per_launch": t_fin_launch * 1e6,
         "bwd_deterministic_us": t_det * 1e6, "bwd_deterministic_tflops": c5.bwd_flops / t_det / 1e12,
