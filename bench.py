@@ -32,6 +32,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+# fp32 atomic adds complete at the memory side at ~2.1e10 64-byte requests per second for
+# the whole chip (measured by `--atomic-rate`, whatever the lane layout or issuing XCD)
+ATOMIC_REQ_PER_S = 2.1e10
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 
 
@@ -418,6 +421,9 @@ def main():
         "bwd_pre_us_per_launch": t_pre_launch * 1e6, "bwd_fin_us_per_launch": t_fin_launch * 1e6,
         "bwd_deterministic_us": t_det * 1e6, "bwd_deterministic_tflops": c5.bwd_flops / t_det / 1e12,
         "bwd_main_dq_atomics": n_atomics,
+        # the main loop against the time its atomics need at the chip's rate (16 adds per request)
+        "bwd_main_atomic_floor_us": n_atomics / 16 / ATOMIC_REQ_PER_S * 1e6,
+        "bwd_main_vs_atomic_floor": n_atomics / 16 / ATOMIC_REQ_PER_S / t_main,
     }
     del c5
     torch.cuda.empty_cache()
