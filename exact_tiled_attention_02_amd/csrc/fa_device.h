@@ -143,6 +143,12 @@ __device__ __forceinline__ void lds_buffer_load4(__amdgpu_buffer_rsrc_t r, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds_base, 4, byte_off, 0, 0, 0);
 }
 
+// 16-byte store per lane at buffer offset byte_off; offsets at or past the resource's
+// extent are dropped by the hardware.
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, u32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)byte_off, 0, 0);
+}
+
 // 4 bytes per lane straight into LDS (global_load_lds_dword): lane l writes lds_base + 4*l.
 __device__ __forceinline__ void lds_direct_load4(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void*)lds_base, 4, 0, 0);

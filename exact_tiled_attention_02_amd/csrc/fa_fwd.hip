@@ -929,23 +929,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const float l_tot = pair_sum(l_run);
   const float lr_tot = kLazy ? pair_sum(lr_run) : 0.f;
-  if (row_ok) {
+  {
     // kLazy: O is normalised by the sum of the weights its product used (the rounded P),
     // so that one dominant key yields exactly its value however far the reference lags.
     const float den = kLazy ? lr_tot : l_tot;
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * Dr;
+    // The rows go out whole: through this wavefront's Q region of LDS (no longer read;
+    // 16-byte chunk c of row r at chunk c ^ (r % CH), so that neither the 8-byte writes of a
+    // column group nor the 16-byte row reads pile onto a few banks), then 16 bytes per lane
+    // with CH lanes per row.  Stored directly, a lane's four columns made every store
+    // instruction touch 32 rows; this way one touches 64 / CH.
+    constexpr int CH = D / 8;
+    // lane-derived offsets recomputed here rather than kept live through the loops
+    const int ln = opaque(lane), lr = ln & 31, lc = ln >> 5;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = d * 32 + 8 * g + 4 * lh;
         u32x2 w;
         w.x = pack2<BF16>(acc[d][4 * g + 0] * inv, acc[d][4 * g + 1] * inv);
         w.y = pack2<BF16>(acc[d][4 * g + 2] * inv, acc[d][4 * g + 3] * inv);
-        if (col < Dr) *(u32x2*)(op + col) = w;  // four columns, all inside or all past Dr
+        *(u32x2*)(Qw + lr * D + (((4 * d + g) ^ (lr % CH)) * 8) + 4 * lc) = w;
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const int rows_in = Lq - wave_row0;  // this wavefront's rows inside the sequence
+    const size_t obase = (size_t)(q_start + wave_row0) * q_rs + (size_t)h * Dr;
+    const size_t ototal = (size_t)(VARLEN ? load_uniform(a.cu_q + a.B) : a.B * a.Sq) * q_rs;
+    const auto orr = make_rsrc((const uint16_t*)a.out + obase, bytes_left(ototal, obase, 2u));
+#pragma unroll
+    for (int i = 0; i < 32 * CH / 64; ++i) {
+      const int r = (i * 64 + ln) / CH, c = (i * 64 + ln) % CH;
+      const u32x4 v = load16(Qw + r * D + ((c ^ (r % CH)) * 8));
+      if (r < rows_in && c * 8 < Dr) buffer_store16(orr, (uint32_t)(r * (int)q_rs + c * 8) * 2u, v);
+    }
+  }
+  if (row_ok) {
     if (lh == 0) {
       float lse = INFINITY;
       if (l_tot > 0.f) lse = (ALIBI ? m_run * 0.69314718055994531f : m_run * a.scale) + __logf(l_tot);
@@ -1443,24 +1462,45 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const float l_all = l_tot * a0 + l1 * a1;
   const float lr_all = lr_tot * a0 + lr1 * a1;
-  if (row_ok) {
+  {
     // O is normalised by the sum of the weights its products used (the rounded P).
     const float inv = lr_all > 0.f ? 1.f / lr_all : 0.f;
     const float w0 = a0 * inv, w1 = a1 * inv;
-    uint16_t* op = (uint16_t*)a.out + (size_t)(q_start + my_row) * q_rs + (size_t)h * Dr;
+    u32x2 pk[ND][4];
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
       __builtin_amdgcn_sched_barrier(0);  // one d-block at a time: no hoisted reads
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 o1 = *(const f32x4*)((d < ND / 2 ? xa : xb) + (((d % (ND / 2)) * 4 + g) * 64 + lane) * 4);
-        const int col = d * 32 + 8 * g + 4 * lh;
-        u32x2 w;
-        w.x = pack2<BF16>(acc[d][4 * g + 0] * w0 + o1[0] * w1, acc[d][4 * g + 1] * w0 + o1[1] * w1);
-        w.y = pack2<BF16>(acc[d][4 * g + 2] * w0 + o1[2] * w1, acc[d][4 * g + 3] * w0 + o1[3] * w1);
-        if (col < Dr) *(u32x2*)(op + col) = w;
+        pk[d][g].x = pack2<BF16>(acc[d][4 * g + 0] * w0 + o1[0] * w1, acc[d][4 * g + 1] * w0 + o1[1] * w1);
+        pk[d][g].y = pack2<BF16>(acc[d][4 * g + 2] * w0 + o1[2] * w1, acc[d][4 * g + 3] * w0 + o1[3] * w1);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // The rows go out whole, through xa (the pair's group-1 accumulator there has been
+    // read in full; 16-byte chunk c of row r at chunk c ^ (r % CH)), 16 bytes per lane and
+    // CH lanes per row: stored directly, every store instruction touched 32 rows.
+    constexpr int CH = D / 8;
+    uint16_t* ost = reinterpret_cast<uint16_t*>(xa);
+    const int ln = opaque(lane), lr = ln & 31, lc = ln >> 5;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) *(u32x2*)(ost + lr * D + (((4 * d + g) ^ (lr % CH)) * 8) + 4 * lc) = pk[d][g];
+    __builtin_amdgcn_sched_barrier(0);
+    const int rows_in = Lq - wave_row0;  // this pair's rows inside the sequence
+    const size_t obase = (size_t)(q_start + wave_row0) * q_rs + (size_t)h * Dr;
+    const size_t ototal = (size_t)(VARLEN ? load_uniform(a.cu_q + a.B) : a.B * a.Sq) * q_rs;
+    const auto orr = make_rsrc((const uint16_t*)a.out + obase, bytes_left(ototal, obase, 2u));
+#pragma unroll
+    for (int i = 0; i < 32 * CH / 64; ++i) {
+      const int r = (i * 64 + ln) / CH, c = (i * 64 + ln) % CH;
+      const u32x4 v = load16(ost + r * D + ((c ^ (r % CH)) * 8));
+      if (r < rows_in && c * 8 < Dr) buffer_store16(orr, (uint32_t)(r * (int)q_rs + c * 8) * 2u, v);
+    }
+  }
+  if (row_ok) {
     if (lh == 0) {
       float lse = INFINITY;
       if (l_all > 0.f) lse = (ALIBI ? m * 0.69314718055994531f : m * a.scale) + __logf(l_all);
