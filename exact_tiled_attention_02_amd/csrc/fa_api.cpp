@@ -217,16 +217,37 @@ size_t fa_bwd_workspace_bytes(int B, int Sq, int Hq, int D) {
   return ((acc + 255) & ~(size_t)255) + 2 * ((dsum + 255) & ~(size_t)255) + 256;
 }
 
+size_t fa_bwd_ds_workspace_bytes(int B, int Sq, int Sk, int Hq, int D) {
+  const int tile = fa::tile_headdim(D);
+  if (B <= 0 || Sq <= 0 || Sk <= 0 || Hq <= 0 || tile == 0) return 0;
+  const int kb = fa::bwd_block_keys(tile);
+  const size_t tiles = (size_t)B * Hq * (size_t)((Sq + 31) / 32) * (size_t)((Sk + kb - 1) / kb);
+  const size_t bytes = tiles * 32 * kb * 2;
+  return bytes > FA_BWD_DS_MAX_BYTES ? 0 : (bytes + 255) & ~(size_t)255;
+}
+
 namespace {
 
-// Stages of a whole backward: preprocess (1), then either the main loop with dQ atomics (2)
-// and the finalize (4), or the main loop without dQ followed by the dQ pass (8).  Above a
-// 128-wide tile the atomic route is the slower one (its main loop covers 128 keys per
-// workgroup, so it issues one fp32 atomic per dQ element per 128 keys, and the memory-side
-// atomic rate bounds it: B=1 H=16 S=8192 D=256 causal 5.3 ms against 3.1 ms for the two
-// passes), so there the two-pass route serves the default backward too.
-int full_bwd_stages(int D, bool deterministic) {
-  return deterministic || fa::tile_headdim(D) > 128 ? (1 | 8) : 7;
+// Stages of a whole backward: preprocess, then, when the workspace holds the stored-dS
+// area, the main loop that stores dS followed by dQ from it (no atomics, no second
+// computation of S and dP: the fastest route, and deterministic); otherwise either the main
+// loop with dQ atomics and the finalize, or the main loop without dQ followed by the dQ
+// pass that recomputes S and dP.  Above a 128-wide tile the atomic route is the slower of
+// those two (its main loop covers 128 keys per workgroup, so it issues one fp32 atomic per
+// dQ element per 128 keys, and the memory-side atomic rate bounds it: B=1 H=16 S=8192
+// D=256 causal 5.3 ms against 3.1 ms for the two passes), so there the recompute route
+// serves the default backward too.
+int full_bwd_stages(int D, bool deterministic, bool stored_ds) {
+  if (stored_ds) return fa::kBwdPre | fa::kBwdMainStoreDs | fa::kBwdDqFromDs;
+  return deterministic || fa::tile_headdim(D) > 128 ? (fa::kBwdPre | fa::kBwdRecompute)
+                                                    : (fa::kBwdPre | fa::kBwdMainAtomic | fa::kBwdFinalize);
+}
+
+// Whether a backward with this workspace takes the stored-dS route.
+bool has_ds_area(int B, int Sq, int Sk, int Hq, int D, size_t workspace_bytes) {
+  const size_t ds = fa_bwd_ds_workspace_bytes(B, Sq, Sk, Hq, D);
+  const size_t base = fa_bwd_workspace_bytes(B, Sq, Hq, D);
+  return ds > 0 && base > 0 && workspace_bytes >= ((base + 255) & ~(size_t)255) + ds;
 }
 
 int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, const void* v, const void* out,
@@ -283,7 +304,17 @@ int bwd_impl(int stage_mask, const void* dout, const void* q, const void* k, con
   a.bf16 = dtype == FA_DTYPE_BF16;
   a.scale = scale;
   a.scale_log2 = exp2_scale(scale);
-  a.zero_acc = (stage_mask & 8) == 0;  // only the atomic dQ path uses the accumulator
+  // only the atomic dQ path uses the accumulator
+  a.zero_acc = (stage_mask & (fa::kBwdRecompute | fa::kBwdMainStoreDs | fa::kBwdDqFromDs)) == 0;
+  if (stage_mask & (fa::kBwdMainStoreDs | fa::kBwdDqFromDs)) {
+    if (!has_ds_area(B, Sq, Sk, Hq, D, workspace_bytes))
+      return fail(FA_ERR_WORKSPACE, "the stored-dS stages need %zu + %zu bytes of workspace (got %zu)",
+                  (need + 255) & ~(size_t)255, fa_bwd_ds_workspace_bytes(B, Sq, Sk, Hq, D), workspace_bytes);
+    const int kb = fa::bwd_block_keys(fa::tile_headdim(D));
+    a.ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + ((need + 255) & ~(size_t)255));
+    a.ds_nqs = (Sq + 31) / 32;
+    a.ds_nkb = (Sk + kb - 1) / kb;
+  }
   return hip_status(fa::launch_bwd(a, stage_mask, stream), "fa_bwd launch");
 }
 
@@ -293,27 +324,31 @@ int fa_bwd(const void* dout, const void* q, const void* k, const void* v, const 
            void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv, int D, float scale, int causal,
            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, void* workspace,
            size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(full_bwd_stages(D, false), dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale,
-                  causal, -1, -1, nullptr, 0, cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
+  return bwd_impl(full_bwd_stages(D, false, has_ds_area(B, Sq, Sk, Hq, D, workspace_bytes)), dout, q, k, v, out,
+                  lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1, -1, nullptr, 0, cu_seqlens_q,
+                  cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_deterministic(const void* dout, const void* q, const void* k, const void* v, const void* out,
                          const float* lse, void* dq, void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv,
                          int D, float scale, int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                          int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(1 | 8, dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1, -1, nullptr,
-                  0, cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
+  return bwd_impl(full_bwd_stages(D, true, has_ds_area(B, Sq, Sk, Hq, D, workspace_bytes)), dout, q, k, v, out,
+                  lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1, -1, nullptr, 0, cu_seqlens_q,
+                  cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_stage(int stage, const void* dout, const void* q, const void* k, const void* v, const void* out,
                  const float* lse, void* dq, void* dk, void* dv, int B, int Sq, int Sk, int Hq, int Hkv, int D,
                  float scale, int causal, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype,
                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (stage < 1 || stage > 3) {
+  if (stage < 1 || stage > 5) {
     g_last_error.clear();
-    return fail(FA_ERR_INVALID_ARGUMENT, "stage %d is not 1, 2 or 3", stage);
+    return fail(FA_ERR_INVALID_ARGUMENT, "stage %d is not 1, 2, 3, 4 or 5", stage);
   }
-  return bwd_impl(1 << (stage - 1), dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1,
+  static const int masks[5] = {fa::kBwdPre, fa::kBwdMainAtomic, fa::kBwdFinalize, fa::kBwdMainStoreDs,
+                               fa::kBwdDqFromDs};
+  return bwd_impl(masks[stage - 1], dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale, causal, -1,
                   -1, nullptr, 0, cu_seqlens_q, cu_seqlens_k, dtype, workspace, workspace_bytes, stream);
 }
 
@@ -322,7 +357,7 @@ int fa_bwd_ex(const void* dout, const void* q, const void* k, const void* v, con
               int window_left, int window_right, const float* alibi_slopes, int alibi_batch_stride,
               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, int deterministic,
               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(full_bwd_stages(D, deterministic != 0), dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale,
+  return bwd_impl(full_bwd_stages(D, deterministic != 0, has_ds_area(B, Sq, Sk, Hq, D, workspace_bytes)), dout, q, k, v, out, lse, dq, dk, dv, B, Sq, Sk, Hq, Hkv, D, scale,
                   causal, window_left, window_right, alibi_slopes, alibi_batch_stride, cu_seqlens_q, cu_seqlens_k,
                   dtype, workspace, workspace_bytes, stream);
 }

@@ -40,9 +40,35 @@
 namespace fa {
 namespace {
 
+constexpr int kXcds = 8;  // XCDs of the MI355X; workgroups are dispatched to them round-robin
 constexpr int kBwdWaves = 4;
 constexpr int kBwdBN = 32 * kBwdWaves;  // keys per workgroup
 constexpr int kBwdBQ = 32;              // query rows per inner step
+
+// Query steps (32-row blocks of a sequence) that keep a key of the key block
+// [k0, k0 + nkeys): [begin, end), empty when begin == end.  Bottom-right causal limit and
+// sliding window as in KeyWindow; without a mask every row keeps every key.  The main loops
+// visit exactly these steps, and the dQ pass over stored dS reads exactly the tiles they
+// wrote, so both take the range from here.
+struct StepRange {
+  int begin, end;
+};
+__device__ __forceinline__ StepRange block_steps(int k0, int nkeys, int Lq, int Lk, bool masked, int causal, int wl,
+                                                 int wr) {
+  const int diag = Lk - Lq;
+  const int k_last = min(k0 + nkeys, Lk) - 1;
+  int i_begin = 0, i_end = Lq;
+  if (masked) {
+    if (causal) {
+      i_begin = max(0, k0 - diag);
+    } else if (wr >= 0) {
+      i_begin = max(0, k0 - diag - wr);
+    }
+    if (wl >= 0) i_end = min(Lq, k_last - diag + wl + 1);
+  }
+  const int qb = i_begin / 32;
+  return StepRange{qb, i_end > i_begin ? (i_end + 31) / 32 : qb};
+}
 
 // ---------------------------------------------------------------- 1. preprocess
 
@@ -90,9 +116,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     }
     a.lse2[pair] = a.lse[li] * 1.4426950408889634f;
   }
-  if (blockIdx.x == 0 && tid == 0) {  // the main loop's key-block queue starts empty
-    a.work[0] = 0;
-    a.work[1] = 0;
+  if (blockIdx.x == 0 && tid == 0) {  // the main loop's key-block queues start empty
+    for (int i = 0; i < 2 + kXcds; ++i) a.work[i] = 0;
   }
 }
 
@@ -166,27 +191,21 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     lse_row0 = (size_t)b * a.Hq * a.Sq;
   }
 
-  // Query rows that keep a key of this block, [i_begin, i_end).  The work is the flat
-  // list of (query head of the group, 32-row query block) steps.
-  const int k_last = min(k0 + kBwdBN, Lk) - 1;
-  int i_begin = 0, i_end = Lq;
+  // The work is the flat list of (query head of the group, 32-row query block) steps over
+  // the query blocks that keep a key of this block.
   int rmin = -0x3fffffff, rmax = 0x3fffffff;  // rows that keep this lane's key
   const int my_key = k0 + threadIdx.x / 64 * 32 + (threadIdx.x & 31);
   if constexpr (MASKED) {
     if (a.causal) {
-      i_begin = max(0, k0 - diag);
       rmin = my_key - diag;
     } else if (a.window_right >= 0) {
-      i_begin = max(0, k0 - diag - a.window_right);
       rmin = my_key - diag - a.window_right;
     }
-    if (a.window_left >= 0) {
-      i_end = min(Lq, k_last - diag + a.window_left + 1);
-      rmax = my_key - diag + a.window_left;
-    }
+    if (a.window_left >= 0) rmax = my_key - diag + a.window_left;
   }
-  const int qb_begin = i_begin / kBwdBQ;
-  const int qb_end = i_end > i_begin ? (i_end + kBwdBQ - 1) / kBwdBQ : qb_begin;
+  const StepRange sr = block_steps(k0, kBwdBN, Lq, Lk, MASKED, a.causal, a.window_left, a.window_right);
+  const int qb_begin = sr.begin;
+  const int qb_end = sr.end;
   const int nqs = max(0, qb_end - qb_begin);
   const int nsteps = G * nqs;
   float sl_next = 0.f;  // ALiBi slope (exp2 units) of the step fetched last
@@ -404,6 +423,17 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     }
     wait_all_memory();  // the prefetched step has landed in LDS
     __syncthreads();    // every wavefront is done with this step's tiles and dS
+    if constexpr (!DQ) {
+      // As in the main loop for D <= 128: dS / scale of this wavefront's 32 keys x 32 rows
+      // into the step's stored tile, when the route over stored dS asks for it (after the
+      // wait, so that the stores have a whole step to complete).
+      if (a.ds != nullptr && i0 / kBwdBQ < a.ds_nqs) {  // (the step bound fails only for invalid cu_seqlens)
+        uint16_t* t = a.ds + (((size_t)b * a.Hq + h) * a.ds_nqs + (size_t)(i0 / kBwdBQ)) * a.ds_nkb * (kBwdBQ * kBwdBN) +
+                      (size_t)kb * (kBwdBQ * kBwdBN) + wave * 1024 + li * 32 + lh * 16;
+        store16(t, dsf[0].v);
+        store16(t + 8, dsf[1].v);
+      }
+    }
   };
   for (int it = 0; it < nsteps; ++it) {
     const bool odd = it & 1;
@@ -446,6 +476,8 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
 constexpr int kK2Keys = 256;
 constexpr int kK2Waves = 8;
 constexpr int kK2BQ = 32;
+static_assert(kK2BQ == 32 && kBwdBQ == 32, "block_steps counts 32-row query steps");
+static_assert(kK2Keys == bwd_block_keys(128) && kBwdBN == bwd_block_keys(256), "stored dS tile sizes");
 
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool DQ, bool ALIBI>
 __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) {
@@ -509,17 +541,9 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   KeyWindow kw{Lk, diag, 0, -1, -1};
   if constexpr (MASKED) kw = KeyWindow{Lk, diag, a.causal, a.window_left, a.window_right};
   const int k_last = min(k0 + kK2Keys, Lk) - 1;
-  int i_begin = 0, i_end = Lq;
-  if constexpr (MASKED) {
-    if (a.causal) {
-      i_begin = max(0, k0 - diag);
-    } else if (a.window_right >= 0) {
-      i_begin = max(0, k0 - diag - a.window_right);
-    }
-    if (a.window_left >= 0) i_end = min(Lq, k_last - diag + a.window_left + 1);
-  }
-  const int qb_begin = i_begin / kK2BQ;
-  const int qb_end = i_end > i_begin ? (i_end + kK2BQ - 1) / kK2BQ : qb_begin;
+  const StepRange sr = block_steps(k0, kK2Keys, Lq, Lk, MASKED, a.causal, a.window_left, a.window_right);
+  const int qb_begin = sr.begin;
+  const int qb_end = sr.end;
   const int nqs = max(0, qb_end - qb_begin);
   const int nsteps = G * nqs;
   float sl_next = 0.f;  // ALiBi slope (exp2 units) of the step fetched last
@@ -629,6 +653,8 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   int ktr[2];
 #pragma unroll
   for (int hi = 0; hi < 2; ++hi) ktr[hi] = Swz::elem(8 * lh + ((lane & 15) >> 2) + 4 * hi, (wave % ND) * 32 + tr_col);
+  // this lane's 32 bytes in a stored dS tile: key row wave * 32 + li, positions 16 lh ..
+  const int ds_lane = wave * 1024 + li * 32 + lh * 16;
 
   wait_all_memory();
   __syncthreads();
@@ -814,6 +840,17 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
     } else {
       wait_vmcnt<0>();  // the prefetched step has landed
       lds_barrier();    // everywhere, and every wavefront is done with this step's tiles
+      // Without dQ here, the route over stored dS keeps this wavefront's 32 keys x 32 rows
+      // of dS / scale for the dQ pass: two 16-byte stores per lane, zeros where nothing is
+      // kept (so every tile of the step range is written whole).  Issued after the wait, so
+      // that they have a whole step to complete before the next one (the counter that
+      // wait reads covers stores too).
+      if (a.ds != nullptr && i0 / kK2BQ < a.ds_nqs) {  // (the step bound fails only for invalid cu_seqlens)
+        uint16_t* t = a.ds + (((size_t)b * a.Hq + h) * a.ds_nqs + (size_t)(i0 / kK2BQ)) * a.ds_nkb * (kK2BQ * kK2Keys) +
+                      (size_t)kb * (kK2BQ * kK2Keys);
+        store16(t + ds_lane, dsf[0].v);
+        store16(t + ds_lane + 8, dsf[1].v);
+      }
     }
   };
 
@@ -875,20 +912,32 @@ template <int D, bool BF16, bool MASKED, bool VARLEN, bool DQ, bool ALIBI>
 __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   if (debug_stop(a.dbg)) return;
   __shared__ int next;
-  const int nblocks = (a.Sk + kK2Keys - 1) / kK2Keys * a.B * a.Hkv;
+  const int nbh = a.B * a.Hkv;
+  const int nblocks = (a.Sk + kK2Keys - 1) / kK2Keys * nbh;
+  // XCD-aware queues: workgroups are dispatched to the 8 XCDs round-robin, so workgroup i
+  // runs on XCD i % 8; when the (sequence, KV head) pairs split evenly, that XCD takes the
+  // key blocks of the pairs bh = i % 8 (mod 8) from a queue of its own (work[2 + i % 8]),
+  // so that the Q / dO rows of a pair are fetched into one L2 only.  Otherwise one queue
+  // (work[0]) serves every workgroup.  Either way every key block is taken exactly once.
+  const bool per_xcd = nbh % kXcds == 0 && gridDim.x % kXcds == 0;
+  const int x = per_xcd ? (int)(blockIdx.x % kXcds) : 0;
+  unsigned int* queue = per_xcd ? a.work + 2 + x : a.work;
+  const int units = per_xcd ? nblocks / kXcds : nblocks;
+  const int nbx = nbh / kXcds;
   for (;;) {
     wait_all_memory();  // the previous block's loads into LDS and its atomics are done
-    if (threadIdx.x == 0) next = (int)atomicAdd(a.work, 1u);
+    if (threadIdx.x == 0) next = (int)atomicAdd(queue, 1u);
     __syncthreads();
-    const int lin = next;
+    const int u = next;
     __syncthreads();  // every wavefront has read it before it is overwritten
-    if (lin >= nblocks) break;
+    if (u >= units) break;
+    // key block kb = lin / nbh of pair bh = lin % nbh, ascending key blocks (longest first)
+    const int lin = per_xcd ? (u / nbx) * nbh + x + kXcds * (u % nbx) : u;
     bwd_k256_block<D, BF16, MASKED, VARLEN, DQ, ALIBI>(a, lin);
   }
   if (threadIdx.x == 0 && atomicAdd(a.work + 1, 1u) == gridDim.x - 1) {
-    // Every workgroup is past its last take from the queue.
-    a.work[0] = 0;
-    a.work[1] = 0;
+    // Every workgroup is past its last take from the queues.
+    for (int i = 0; i < 2 + kXcds; ++i) a.work[i] = 0;
   }
 }
 
@@ -1153,6 +1202,248 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_pass_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- 2d. dQ from stored dS
+
+// dQ = scale dS K from the dS tiles the main loop stored (the route with neither dQ
+// atomics nor a second computation of S and dP): one workgroup per (128-row query block,
+// query head, sequence), four wavefronts of one 32-row query step each.  The key blocks
+// of the main loop that reach the workgroup's steps are walked in 64-key stages through an
+// LDS ring (direct loads): the stage's K rows, shared, and each wavefront's slice of its
+// own dS tile.  dQ^T += K^T dS^T accumulates on MFMA with both operands taken by
+// transposed LDS reads (K^T from the swizzled K rows; dS^T from the stored key rows, whose
+// 64 bytes hold the 32 query rows in the order the main loop's products produced them).
+// A wavefront skips the key blocks whose step range does not hold its step (those tiles
+// were never written).  dQ is written once: the same sum in the same order on every run.
+// Every stored dS element is read once; the pass is bound by those reads.
+// Wavefronts (32-row query steps) per workgroup, and keys per LDS stage (two stages,
+// double-buffered, so that two workgroups fit on a CU and one streams while the other
+// multiplies).
+constexpr int ds_waves(int) { return 4; }
+constexpr int ds_stage_keys(int D) { return D == 256 ? 32 : 64; }
+
+// LDS ring slot i of a stage ring held as distinct objects (so that the compiler can tell
+// the reads of one slot from the direct loads in flight into another).
+template <int I, class T>
+__device__ __forceinline__ T* ring_slot(T* s0, T* s1, T* s2, T* s3) {
+  if constexpr (I == 0) return s0;
+  else if constexpr (I == 1) return s1;
+  else if constexpr (I == 2) return s2;
+  else return s3;
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * ds_waves(D), 2) void bwd_dq_ds_kernel(BwdArgs a) {
+  if (debug_stop(a.dbg)) return;
+  constexpr int kDsWaves = ds_waves(D);
+  constexpr int kDsRows = 32 * kDsWaves;  // query rows per workgroup
+  constexpr int kDsSK = ds_stage_keys(D);
+  constexpr int KB = bwd_block_keys(D);  // keys per main-loop block (one stored tile)
+  constexpr int TILE = 32 * KB;          // elements of a stored tile
+  constexpr int SPB = KB / kDsSK;        // stages per key block
+  constexpr int NST = 2;                 // ring depth (LDS: 64 KiB at D = 128, 48 KiB at 64 and 256)
+  constexpr int ND = D / 32;
+  constexpr int KT = kDsSK * D;          // K elements per stage
+  constexpr int STW = kDsSK * 32;        // dS elements per wavefront per stage (key rows of 32)
+  constexpr int NK = KT / 8 / (64 * kDsWaves);  // 16-byte K loads per lane per stage
+  constexpr int NSL = STW / 8 / 64;      // 16-byte dS loads per lane per stage
+  constexpr int L = NK + NSL;            // vector-memory loads per lane per stage, in every wavefront
+  static_assert(KB % kDsSK == 0 && kDsSK % 16 == 0 && NK >= 1 && NSL >= 1 && (NST - 2) * L < 64, "stage shape");
+  using Swz = DualSwizzle<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[KT];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[KT];
+  __shared__ __attribute__((aligned(16))) uint16_t K2[NST > 2 ? KT : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t K3[NST > 3 ? KT : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t S0[kDsWaves * STW];
+  __shared__ __attribute__((aligned(16))) uint16_t S1[kDsWaves * STW];
+  __shared__ __attribute__((aligned(16))) uint16_t S2[NST > 2 ? kDsWaves * STW : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t S3[NST > 3 ? kDsWaves * STW : 8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31;
+  const int lh = lane >> 5;
+
+  const int nqb = (a.Sq + kDsRows - 1) / kDsRows;
+  const int nbh = a.B * a.Hq;
+  const int qb = nqb - 1 - (int)blockIdx.x / nbh;  // causal: the longest key ranges first
+  const int bh = (int)blockIdx.x % nbh;
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+
+  const bool varlen = a.cu_q != nullptr;
+  int q_start, k_start, Lq, Lk;
+  if (varlen) {
+    q_start = load_uniform(a.cu_q + b);
+    Lq = load_uniform(a.cu_q + b + 1) - q_start;
+    k_start = load_uniform(a.cu_k + b);
+    Lk = load_uniform(a.cu_k + b + 1) - k_start;
+  } else {
+    q_start = b * a.Sq;
+    Lq = a.Sq;
+    k_start = b * a.Sk;
+    Lk = a.Sk;
+  }
+  if (qb * kDsRows >= Lq) return;  // uniform
+
+  const bool masked = a.causal || a.window_left >= 0 || a.window_right >= 0;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int Dr = a.D;  // head dimension of the tensors (<= D, the tile width)
+  const int Dc = Dr / 8;
+  const size_t q_rs = (size_t)a.Hq * Dr;
+  const size_t k_rs = (size_t)a.Hkv * Dr;
+  const int step0 = qb * kDsWaves;               // the workgroup's first query step
+  const int my_step = step0 + wave;               // this wavefront's
+  const int nsteps_seq = (Lq + 31) / 32;
+  const int last_step = min(step0 + kDsWaves, nsteps_seq) - 1;
+  const int nkb = Lk > 0 ? (Lk + KB - 1) / KB : 0;
+
+  // Key blocks whose step range reaches one of the workgroup's steps: [kb_lo, kb_hi].
+  // (The ranges move forward with the key block, so these are contiguous.)
+  int kb_lo = nkb, kb_hi = -1;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const StepRange r = block_steps(kb * KB, KB, Lq, Lk, masked, a.causal, a.window_left, a.window_right);
+    if (r.begin <= last_step && r.end > step0) {
+      kb_lo = min(kb_lo, kb);
+      kb_hi = kb;
+    }
+  }
+  const int nst = kb_hi >= kb_lo ? (kb_hi - kb_lo + 1) * SPB : 0;
+
+  // Direct loads of stage s: its 64 K rows (clamped to the sequence; the padding chunks
+  // past the head dimension re-read chunk 0 and only feed dQ columns that are never
+  // stored) into the shared K slot, and this wavefront's 64 key rows of its dS tile into its
+  // part of the dS slot.  A wavefront whose step the block does not reach still loads (from
+  // its step clamped into the array, never used), so that every wavefront issues L loads per
+  // stage and the waits below can count them.
+  const size_t k_rows = varlen ? (size_t)load_uniform(a.cu_k + a.B) : (size_t)a.B * a.Sk;
+  const uint16_t* ds_head = a.ds + ((size_t)b * a.Hq + h) * a.ds_nqs * a.ds_nkb * (size_t)TILE;
+  const size_t my_tiles = (size_t)min(my_step, a.ds_nqs - 1) * a.ds_nkb * (size_t)TILE;
+  auto issue = [&](int s, uint16_t* __restrict__ Kd, uint16_t* __restrict__ Sd) {
+    const int kb = kb_lo + s / SPB;
+    const int kbase = kb * KB;  // < Lk
+    const int k0 = kbase + (s % SPB) * kDsSK;
+    const size_t kfirst = (size_t)(k_start + kbase) * k_rs + (size_t)hk * Dr;
+    const auto kr = make_rsrc((const uint16_t*)a.k + kfirst, min(bytes_left(k_rows * k_rs, kfirst, 2u), 0x7fffffffu));
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int first = (i * kDsWaves + wave) * 64;
+      const int chunk = first + lane;
+      const int r = chunk / Swz::CH;
+      const int g = Swz::chunk(r, chunk % Swz::CH);
+      const int key = min(k0 + r, Lk - 1) - kbase;  // 0 <= key < KB
+      lds_buffer_load16(kr, (uint32_t)(key * (int)k_rs + src_chunk(g, Dc) * 8) * 2u, Kd + first * 8);
+    }
+    // (the clamps of step and key block to the area bind only for invalid cu_seqlens)
+    const auto sr = make_rsrc(ds_head + my_tiles + (size_t)min(kb, a.ds_nkb - 1) * TILE + (s % SPB) * STW, STW * 2u);
+#pragma unroll
+    for (int i = 0; i < NSL; ++i)
+      lds_buffer_load16_stream(sr, (uint32_t)(i * 64 + lane) * 16u, Sd + wave * STW + i * 512);
+  };
+
+  // Transposed-read bases.  K^T (A operand): lane reads key rows 8 lh + (lane & 15) / 4 + 4 hi
+  // of a 16-key step, columns 32 d + tr_col (swizzled: k_base[hi] + 32 (d ^ k_x[hi]));
+  // dS^T (B operand): key rows as for K, positions 16 ((lane >> 4) & 1) + 4 (lane & 3).
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int k_base[2], k_x[2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    const int r = 8 * lh + ((lane & 15) >> 2) + 4 * hi;
+    const int f = Swz::f(r);
+    k_base[hi] = r * D + 8 * ((tr_col >> 3) ^ (f & 3)) + (tr_col & 7);
+    k_x[hi] = f >> 2;
+  }
+  const int s_base = wave * STW + (8 * lh + ((lane & 15) >> 2)) * 32 + tr_col;
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) acc[d] = f32x16{};
+
+  auto compute = [&](const uint16_t* __restrict__ K, const uint16_t* __restrict__ S) {
+    // ops o = (16-key step ks, d-block d); operand reads RA ops ahead in fenced order.
+    constexpr int NO = (kDsSK / 16) * ND, RA = 2;
+    const int kb0 = opaque(k_base[0]), kb1 = opaque(k_base[1]);
+    Frag8 kt[RA], sf[2];
+    auto read = [&](auto o_tag) __attribute__((always_inline)) {
+      constexpr int o = decltype(o_tag)::value, sl = o % RA, ks = o / ND, d = o % ND;
+      const u32x2 lo = lds_read_tr16(K + ks * 16 * D + kb0 + 32 * (d ^ k_x[0]));
+      const u32x2 hi = lds_read_tr16(K + ks * 16 * D + kb1 + 32 * (d ^ k_x[1]));
+      kt[sl].v = u32x4{lo.x, lo.y, hi.x, hi.y};
+      if constexpr (d == 0) {
+        const u32x2 slo = lds_read_tr16(S + s_base + ks * 16 * 32);
+        const u32x2 shi = lds_read_tr16(S + s_base + ks * 16 * 32 + 4 * 32);
+        sf[ks & 1].v = u32x4{slo.x, slo.y, shi.x, shi.y};
+      }
+    };
+    static_for<0, RA>([&](auto o) __attribute__((always_inline)) { read(o); });
+    static_for<0, NO>([&](auto o_tag) __attribute__((always_inline)) {
+      constexpr int o = decltype(o_tag)::value, sl = o % RA, ks = o / ND, d = o % ND;
+      __builtin_amdgcn_sched_barrier(0);
+      acc[d] = mfma32x32x16<BF16>(kt[sl], sf[ks & 1], acc[d]);
+      if constexpr (o + RA < NO) read(Idx<o + RA>{});
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // The whole ring walk in one function that takes the slots as distinct restrict
+  // pointers, so that the compiler can tell the reads of a stage from the direct loads in
+  // flight into the other slots (issued in this or an earlier stage) and does not wait for
+  // those before every read.  Stage s: wait for its loads, barrier, issue the loads of
+  // stage s + NST - 1 into the slot stage s - 1 used, then this wavefront's products.
+  auto walk = [&](uint16_t* __restrict__ k0, uint16_t* __restrict__ k1, uint16_t* __restrict__ k2,
+                  uint16_t* __restrict__ k3, uint16_t* __restrict__ s0p, uint16_t* __restrict__ s1p,
+                  uint16_t* __restrict__ s2p, uint16_t* __restrict__ s3p) __attribute__((always_inline)) {
+    static_for<0, NST - 1>([&](auto j_tag) __attribute__((always_inline)) {
+      constexpr int j = decltype(j_tag)::value;
+      if (j < nst) issue(j, ring_slot<j>(k0, k1, k2, k3), ring_slot<j>(s0p, s1p, s2p, s3p));
+    });
+    for (int s0 = 0; s0 < nst; s0 += NST) {
+      static_for<0, NST>([&](auto j_tag) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_tag)::value;
+        const int s = s0 + j;
+        if (s < nst) {
+          // Stage s has landed once at most the loads of the stages issued after it are in
+          // flight (loads complete in issue order; nothing else is outstanding here).
+          if (s + NST - 2 < nst) {
+            wait_vmcnt<(NST - 2) * L>();
+          } else {
+            wait_vmcnt<0>();
+          }
+          // Every wavefront's loads of stage s are in LDS, and every wavefront is done with
+          // stage s - 1, whose slot the next issue reuses.
+          lds_barrier();
+          if (s + NST - 1 < nst)
+            issue(s + NST - 1, ring_slot<(j + NST - 1) % NST>(k0, k1, k2, k3),
+                  ring_slot<(j + NST - 1) % NST>(s0p, s1p, s2p, s3p));
+          const int kb = kb_lo + s / SPB;
+          const StepRange r = block_steps(kb * KB, KB, Lq, Lk, masked, a.causal, a.window_left, a.window_right);
+          if (r.begin <= my_step && my_step < r.end) compute(ring_slot<j>(k0, k1, k2, k3), ring_slot<j>(s0p, s1p, s2p, s3p));
+        }
+      });
+    }
+  };
+  walk(K0, K1, K2, K3, S0, S1, S2, S3);
+
+  // Lane li holds query row position li of the step (row = the position's bits permuted as
+  // in the stored tile) and, in register r of d-block d, column 32 d + 8 (r / 4) + 4 lh + r % 4.
+  const int row = my_step * 32 + 16 * ((li >> 3) & 1) + 8 * ((li >> 2) & 1) + 4 * (li >> 4) + (li & 3);
+  const size_t q_rows = varlen ? (size_t)load_uniform(a.cu_q + a.B) : (size_t)a.B * a.Sq;
+  if (row < Lq && (size_t)(q_start + row) < q_rows) {
+    uint16_t* gp = (uint16_t*)a.dq + (size_t)(q_start + row) * q_rs + (size_t)h * Dr;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = d * 32 + 8 * g + 4 * lh;
+        u32x2 w;
+        w.x = pack2<BF16>(acc[d][4 * g + 0] * a.scale, acc[d][4 * g + 1] * a.scale);
+        w.y = pack2<BF16>(acc[d][4 * g + 2] * a.scale, acc[d][4 * g + 3] * a.scale);
+        if (col < Dr) *(u32x2*)(gp + col) = w;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- 3. finalize
 
 template <bool BF16, bool VARLEN>
@@ -1191,7 +1482,7 @@ int cu_count() {
 template <int D, bool BF16, bool MASKED, bool VARLEN, bool ALIBI>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   const size_t rows = (size_t)a.B * a.Sq;  // bound on total_q in varlen mode
-  if (stages & 1) {
+  if (stages & kBwdPre) {
     constexpr int PAIRS = 256 / (D / 8);
     const size_t pairs = rows * a.Hq;
     const dim3 grid((unsigned)((pairs + PAIRS - 1) / PAIRS));
@@ -1199,8 +1490,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stages & (2 | 8)) {
-    const bool det = (stages & 8) != 0;
+  if (stages & (kBwdMainAtomic | kBwdRecompute | kBwdMainStoreDs)) {
+    // the main loop without dQ serves the recompute route and, with a.ds set, the
+    // stored-dS route
+    const bool det = (stages & kBwdMainAtomic) == 0;
     if constexpr (D <= 128) {
       const int nkb = (a.Sk + kK2Keys - 1) / kK2Keys;
       const dim3 grid((unsigned)std::min(nkb * a.B * a.Hkv, cu_count()));
@@ -1220,7 +1513,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (det) {
+    if (stages & kBwdRecompute) {
       const int nqb = (a.Sq + kDqBM - 1) / kDqBM;
       const dim3 grid((unsigned)nqb * a.B * a.Hq);
       hipLaunchKernelGGL((bwd_dq_pass_kernel<D, BF16, MASKED, VARLEN, ALIBI>), grid, dim3(256), 0, stream, a);
@@ -1228,7 +1521,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
       if (e != hipSuccess) return e;
     }
   }
-  if (stages & 4) {
+  if (stages & kBwdDqFromDs) {
+    constexpr int rows = 32 * ds_waves(D);
+    const int nqb = (a.Sq + rows - 1) / rows;
+    hipLaunchKernelGGL((bwd_dq_ds_kernel<D, BF16>), dim3((unsigned)nqb * a.B * a.Hq), dim3(64 * ds_waves(D)), 0, stream,
+                       a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kBwdFinalize) {
     const size_t n8 = rows * a.Hq * a.D / 8;
     size_t blocks = (n8 + 255) / 256;
     if (blocks > 65536) blocks = 65536;

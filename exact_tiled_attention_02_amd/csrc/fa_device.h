@@ -137,6 +137,11 @@ __device__ __forceinline__ void lds_buffer_load16(__amdgpu_buffer_rsrc_t r, uint
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds_base, 16, byte_off, (int)uniform_off, 0, 0);
 }
 
+// The same load with the non-temporal (streaming) cache hint, for data read exactly once.
+__device__ __forceinline__ void lds_buffer_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds_base, 16, byte_off, 0, 0, 2);
+}
+
 // The same with 4 bytes per lane (buffer_load_dword with the lds bit): lane l writes
 // lds_base + 4*l.
 __device__ __forceinline__ void lds_buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, void* lds_base) {
@@ -270,5 +275,8 @@ struct KeyWindow {
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void store16(void* p, u32x4 x) { *(u32x4*)p = x; }
+// 16-byte store with the non-temporal (streaming) hint: data written once and read back
+// only much later, which should not displace reused lines from the caches.
+__device__ __forceinline__ void store16_stream(void* p, u32x4 x) { __builtin_nontemporal_store(x, (u32x4*)p); }
 
 }  // namespace fa

@@ -62,7 +62,18 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int zero_acc;  // preprocess also zeroes dq_acc (the atomic path needs it)
-  unsigned int* work;  // [2]: key blocks handed out, workgroups finished (zero between launches)
+  unsigned int* work;  // [10]: key blocks handed out (one queue), workgroups finished, then the
+                       // per-XCD queues (all zero between launches)
+  // Stored dS / scale in the input dtype (the route without dQ atomics), or null: one tile
+  // of 32 query rows x KB keys (KB = keys per main-loop workgroup: 256 up to a 128-wide
+  // tile, 128 above) per (sequence, query head, query step, key block), tile index
+  // ((b * Hq + h) * ds_nqs + step) * ds_nkb + key block.  Inside a tile, the 32 keys of
+  // main-loop wavefront w take bytes [2048 w, 2048 w + 2048): key row j (64 bytes) holds
+  // the 32 rows at positions p, row = 16 ((p >> 3) & 1) + 8 ((p >> 2) & 1) + 4 (p >> 4) + (p & 3)
+  // (the order in which the products leave them in a lane).
+  uint16_t* ds;
+  int ds_nqs;  // ceil(Sq / 32)
+  int ds_nkb;  // ceil(Sk / KB)
 };
 
 // Decode against a read-only KV cache (few query rows, long cache), split over the keys.
@@ -114,7 +125,14 @@ constexpr int tile_headdim(int D) {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // stage_mask bit 0: preprocess, bit 1: main loop with dQ atomics, bit 2: finalize,
-// bit 3: deterministic dQ (main loop without dQ, then a separate dQ pass writing dq).
+// bit 3: deterministic dQ (main loop without dQ, then a separate dQ pass writing dq),
+// bit 4: main loop without dQ that stores dS (a.ds), bit 5: dQ = scale dS K from the
+// stored dS, written to dq.
+constexpr int kBwdPre = 1, kBwdMainAtomic = 2, kBwdFinalize = 4, kBwdRecompute = 8, kBwdMainStoreDs = 16,
+              kBwdDqFromDs = 32;
+// Keys per backward main-loop workgroup for tile width D (the key-block size of the
+// stored dS tiles).
+constexpr int bwd_block_keys(int D) { return D <= 128 ? 256 : 128; }
 hipError_t launch_bwd(const BwdArgs& a, int stage_mask, hipStream_t stream);
 // Split kernel, then (splits > 1) the combine kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

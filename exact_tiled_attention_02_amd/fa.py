@@ -37,6 +37,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.restype = i
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
         L.fa_bwd_workspace_bytes.restype = sz
+        L.fa_bwd_ds_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.fa_bwd_ds_workspace_bytes.restype = sz
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, i, vp, sz, vp]
         L.fa_bwd.restype = i
         L.fa_bwd_deterministic.argtypes = L.fa_bwd.argtypes
@@ -211,12 +213,18 @@ def fa_bwd_workspace_bytes(B: int, Sq: int, Hq: int, D: int) -> int:
     return int(lib().fa_bwd_workspace_bytes(B, Sq, Hq, D))
 
 
+def fa_bwd_ds_workspace_bytes(B: int, Sq: int, Sk: int, Hq: int, D: int) -> int:
+    """Extra workspace of the stored-dS backward route (0: not available at this size)."""
+    return int(lib().fa_bwd_ds_workspace_bytes(B, Sq, Sk, Hq, D))
+
+
 def fa_bwd(dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: bool = False, scale: float | None = None,
            cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None,
            window_size=(-1, -1), alibi_slopes=None) -> None:
     """Enqueue the backward; writes dq, dk, dv.  ``workspace``: a uint8 device tensor of
-    at least fa_bwd_workspace_bytes(B, Sq, Hq, D) bytes.  With a window or ALiBi this is
-    the C ``fa_bwd_ex``."""
+    at least fa_bwd_workspace_bytes(B, Sq, Hq, D) bytes (plus fa_bwd_ds_workspace_bytes
+    for the stored-dS route; :func:`workspace_for`).  With a window or ALiBi this is the
+    C ``fa_bwd_ex``."""
     if _plain(window_size, alibi_slopes):
         fa_bwd_stage(0, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal, scale, cu_seqlens_q, cu_seqlens_k,
                      max_seqlen_q, max_seqlen_k, stream)
@@ -253,8 +261,9 @@ def _bwd_ex(deterministic, dout, q, k, v, out, lse, dq, dk, dv, workspace, causa
 def fa_bwd_stage(stage, dout, q, k, v, out, lse, dq, dk, dv, workspace, causal: bool = False,
                  scale: float | None = None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
                  max_seqlen_k=None, stream=None) -> None:
-    """Enqueue one backward stage (1 preprocess, 2 main loop, 3 finalize); stage 0 runs
-    the whole backward (``fa_bwd``)."""
+    """Enqueue one backward stage (1 preprocess, 2 main loop with dQ atomics, 3 finalize,
+    4 main loop storing dS, 5 dQ from the stored dS); stage 0 runs the whole backward
+    (``fa_bwd``)."""
     B, Sq, Sk, Hq, Hkv, D, dt = _bwd_args(dout, q, k, v, out, lse, dq, dk, dv, workspace, cu_seqlens_q,
                                           cu_seqlens_k, max_seqlen_q, max_seqlen_k)
     if scale is None:
@@ -299,23 +308,34 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, cu_seqlen
     return out, lse
 
 
-def workspace_for(q, cu_seqlens_q=None, max_seqlen_q=None):
+def workspace_for(q, cu_seqlens_q=None, max_seqlen_q=None, k=None, max_seqlen_k=None, stored_ds: bool = False):
+    """Backward workspace for q; with ``stored_ds`` (and k) also the stored-dS area when
+    that route is available at this size (fa_bwd then takes it)."""
     if cu_seqlens_q is None:
         B, Sq, Hq, D = q.shape
     else:
         # every sequence is at most max_seqlen_q long, so B * max_seqlen_q >= total_q
         B, Sq, Hq, D = cu_seqlens_q.numel() - 1, int(max_seqlen_q), q.shape[1], q.shape[2]
     n = fa_bwd_workspace_bytes(B, Sq, Hq, D)
+    if stored_ds:
+        if k is None:
+            raise ValueError("the stored-dS area needs k (its key length)")
+        Sk = k.shape[1] if cu_seqlens_q is None else int(max_seqlen_k)
+        ds = fa_bwd_ds_workspace_bytes(B, Sq, Sk, Hq, D)
+        if ds:
+            n = (n + 255) // 256 * 256 + ds
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
 def backward(dout, q, k, v, out, lse, causal: bool = False, scale: float | None = None, cu_seqlens_q=None,
              cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, stream=None, deterministic: bool = False,
-             window_size=(-1, -1), alibi_slopes=None):
+             window_size=(-1, -1), alibi_slopes=None, stored_ds: bool = True):
     """Allocate (dq, dk, dv) and the workspace, and run :func:`fa_bwd` (or
-    :func:`fa_bwd_deterministic`)."""
+    :func:`fa_bwd_deterministic`).  ``stored_ds`` gives the workspace the stored-dS area
+    (the fastest route, deterministic) when it is available at this size; without it the
+    backward takes the atomic route (or, deterministic or D > 128, the recompute route)."""
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = workspace_for(q, cu_seqlens_q, max_seqlen_q)
+    ws = workspace_for(q, cu_seqlens_q, max_seqlen_q, k, max_seqlen_k, stored_ds)
     run = fa_bwd_deterministic if deterministic else fa_bwd
     run(dout, q, k, v, out, lse, dq, dk, dv, ws, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
         max_seqlen_k, stream, window_size, alibi_slopes)

@@ -111,6 +111,22 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse
  */
 size_t fa_bwd_workspace_bytes(int B, int Sq, int Hq, int D);
 
+/* Largest stored-dS area fa_bwd_ds_workspace_bytes offers (32 GiB). */
+#define FA_BWD_DS_MAX_BYTES ((size_t)32 << 30)
+
+/*
+ * Extra workspace bytes, beyond fa_bwd_workspace_bytes(B, Sq, Hq, D), of the backward's
+ * stored-dS route: the main loop writes dS / scale (the input dtype, rounded exactly as
+ * the dQ product would take it) for every query step and key block it visits, and a
+ * second, memory-bound pass forms dQ = scale dS K from them, with no atomics and no second
+ * computation of S and dP.  The area is B * Hq * ceil(Sq / 32) * ceil(Sk / KB) tiles of
+ * 32 * KB 16-bit values, KB = 256 keys for D <= 128 and 128 above (Sq, Sk the padded or
+ * maximum lengths); only the tiles a mask keeps are written and read.  Returns 0 for
+ * invalid sizes and when the area would exceed FA_BWD_DS_MAX_BYTES (the route is then not
+ * available).
+ */
+size_t fa_bwd_ds_workspace_bytes(int B, int Sq, int Sk, int Hq, int D);
+
 /*
  * Backward: given dout = dL/dO and the forward's own out and lse, writes
  * dq = dL/dQ, dk = dL/dK, dv = dL/dV (input dtype).  The method is the recompute-from-LSE
@@ -124,9 +140,13 @@ size_t fa_bwd_workspace_bytes(int B, int Sq, int Hq, int D);
  * stored).  Other arguments as for fa_fwd.  `workspace` (16-byte aligned) must hold
  * fa_bwd_workspace_bytes(B, Sq, Hq, D) bytes; its contents on entry do not matter.
  * dq, dk, dv are fully overwritten (rows beyond a varlen sequence are not touched).
- * For D <= 128, dq is accumulated with fp32 atomics, so the result may differ in the last
- * bits from run to run; for D > 128 fa_bwd runs the scheme of fa_bwd_deterministic, which
- * is the faster one there.  The forward is bitwise deterministic.
+ * Route: when fa_bwd_ds_workspace_bytes(B, Sq, Sk, Hq, D) is nonzero and the workspace
+ * holds both sizes, dQ is formed from the stored dS (the fastest route, and bitwise
+ * repeatable; the dS area follows the first fa_bwd_workspace_bytes bytes, rounded up to
+ * 256).  Otherwise, for D <= 128, dq is accumulated with fp32 atomics, so the result may
+ * differ in the last bits from run to run, and for D > 128 fa_bwd runs the recompute
+ * scheme of fa_bwd_deterministic, which is the faster one there.  The forward is bitwise
+ * deterministic.
  */
 int fa_bwd(const void* dout, const void* q, const void* k, const void* v,
            const void* out, const float* lse, void* dq, void* dk, void* dv,
@@ -139,8 +159,10 @@ int fa_bwd(const void* dout, const void* q, const void* k, const void* v,
  * formed by a separate pass over the key blocks of each query block instead of fp32
  * atomics, so dq, dk and dv are bitwise identical from run to run (the pages' README
  * offers a deterministic backward: changelog entry 2.4 and the `deterministic`
- * argument of the flash_attn_func docstring).  It recomputes the scores and dP once more,
- * so for D <= 128 it is slower than fa_bwd; for D > 128 the two calls run the same kernels.
+ * argument of the flash_attn_func docstring).  With a workspace large enough for the
+ * stored-dS route (see fa_bwd) it runs that route, the same kernels as fa_bwd; otherwise
+ * it recomputes the scores and dP once more in the dQ pass, which for D <= 128 is slower
+ * than fa_bwd's atomic route.
  */
 int fa_bwd_deterministic(const void* dout, const void* q, const void* k, const void* v,
                          const void* out, const float* lse, void* dq, void* dk, void* dv,
@@ -170,12 +192,16 @@ int fa_bwd_ex(const void* dout, const void* q, const void* k, const void* v,
  * stage 2: main loop -- dk, dv written, dQ / scale added into the accumulator
  *          (its key-block queue is emptied by stage 1 and again at its own end, so it
  *          may be repeated on its own after a complete stage 1 or stage 2);
- * stage 3: finalize -- dq = scale * accumulator, in the input dtype.
- * For D <= 128, fa_bwd is stages 1, 2, 3 in this order on one stream; a stage reads what
- * the earlier stages left in the workspace.  (For D > 128 fa_bwd takes the atomic-free
- * route of fa_bwd_deterministic instead; stages 1, 2, 3 still compute the same gradients
- * there, with atomics.)  Arguments, checks and errors as for fa_bwd; a stage outside 1..3
- * returns FA_ERR_INVALID_ARGUMENT.
+ * stage 3: finalize -- dq = scale * accumulator, in the input dtype;
+ * stage 4: main loop of the stored-dS route -- dk, dv written, dS / scale stored in the
+ *          workspace's dS area (needs the workspace of that route, see fa_bwd);
+ * stage 5: dQ of the stored-dS route -- dq = scale dS K from the stored dS.
+ * Stages 1, 4, 5 in this order are fa_bwd's stored-dS route; stages 1, 2, 3 its atomic
+ * route (for D > 128 without the dS area fa_bwd takes the recompute route of
+ * fa_bwd_deterministic instead; stages 1, 2, 3 still compute the same gradients there,
+ * with atomics).  A stage reads what the earlier stages left in the workspace.  Arguments,
+ * checks and errors as for fa_bwd; a stage outside 1..5 returns FA_ERR_INVALID_ARGUMENT,
+ * and stage 4 or 5 without the dS area FA_ERR_WORKSPACE.
  */
 int fa_bwd_stage(int stage, const void* dout, const void* q, const void* k, const void* v,
                  const void* out, const float* lse, void* dq, void* dk, void* dv,

@@ -124,10 +124,36 @@ def test_binding_rejects_host_tensors(L):
         fa.fa_fwd(q, q, q, q.clone(), torch.zeros(1, 2, 8), causal=False)
 
 
-@pytest.mark.parametrize("stage", [0, 4, -1])
+@pytest.mark.parametrize("stage", [0, 6, -1])
 def test_bwd_stage_rejects_bad_stage(L, stage):
     args = [P] * 9 + [1, 128, 128, 4, 2, 128, 0.1, 1, None, None, 1, P, 1 << 40, None]
     assert L.fa_bwd_stage(stage, *args) == 1
+
+
+def test_ds_workspace_bytes(L):
+    """The stored-dS area: B * Hq * ceil(Sq / 32) * ceil(Sk / KB) tiles of 32 x KB 16-bit
+    values (KB = 256 keys up to a 128-wide tile, 128 above), 256-byte rounded; 0 for invalid
+    sizes and above the 32 GiB cap."""
+    for B, Sq, Sk, H, D, kb in ((2, 4096, 4096, 16, 128, 256), (3, 77, 500, 6, 64, 256), (1, 1, 1, 1, 256, 128),
+                                (2, 300, 333, 4, 192, 128), (16, 2048, 2048, 8, 40, 256)):
+        n = B * H * -(-Sq // 32) * -(-Sk // kb) * 32 * kb * 2
+        assert L.fa_bwd_ds_workspace_bytes(B, Sq, Sk, H, D) == (n + 255) // 256 * 256
+    assert L.fa_bwd_ds_workspace_bytes(2, 4096, 4096, 16, 128) == 2 * 16 * 4096 * 4096 * 2
+    assert L.fa_bwd_ds_workspace_bytes(0, 1, 1, 1, 128) == 0
+    assert L.fa_bwd_ds_workspace_bytes(1, 1, 0, 1, 128) == 0
+    assert L.fa_bwd_ds_workspace_bytes(1, 1, 1, 1, 100) == 0
+    # 1 x 32 x 32768^2 x 2 bytes = 64 GiB: beyond the cap, the route is not offered
+    assert L.fa_bwd_ds_workspace_bytes(1, 32768, 32768, 32, 128) == 0
+    assert L.fa_bwd_ds_workspace_bytes(1, 32768, 32768, 16, 128) == 32 << 30
+
+
+@pytest.mark.parametrize("stage", [4, 5])
+def test_stored_ds_stages_need_the_area(L, stage):
+    """Stages 4 and 5 with only the base workspace return FA_ERR_WORKSPACE before any launch."""
+    base = L.fa_bwd_workspace_bytes(1, 128, 4, 128)
+    args = [P] * 9 + [1, 128, 128, 4, 2, 128, 0.1, 1, None, None, 1, P, base, None]
+    assert L.fa_bwd_stage(stage, *args) == 3
+    assert b"stored-dS" in L.fa_last_error()
 
 
 def test_bwd_stage_validates_like_fa_bwd(L):

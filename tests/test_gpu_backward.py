@@ -17,7 +17,10 @@ def rel_fro(got, ref):
     return float(np.linalg.norm(got - ref) / n) if n > 0 else float(np.linalg.norm(got))
 
 
-def run_fwd_bwd(w, x, poison=True, deterministic=False):
+def run_fwd_bwd(w, x, poison=True, deterministic=False, stored_ds=False):
+    """Forward, then the backward through the C ABI: with ``stored_ds`` the workspace holds
+    the stored-dS area (fa_bwd takes that route), without it only the base workspace (the
+    atomic route, or the recompute route when deterministic or above a 128-wide tile)."""
     d = dev(x)
     kw = {}
     if w.varlen:
@@ -31,8 +34,12 @@ def run_fwd_bwd(w, x, poison=True, deterministic=False):
         dv = torch.full_like(d["v"], float("nan"))
     else:
         dq, dk, dv = torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])
-    ws = fa.workspace_for(d["q"], d.get("cu_seqlens_q"), w.seqlen_q if w.varlen else None)
-    ws.fill_(0xFF)  # the workspace's contents on entry must not matter
+    ws = fa.workspace_for(d["q"], d.get("cu_seqlens_q"), w.seqlen_q if w.varlen else None, d["k"],
+                          w.seqlen_k if w.varlen else None, stored_ds)
+    if stored_ds:
+        B = len(w.lengths_q) if w.varlen else w.batch
+        assert ws.numel() > fa.fa_bwd_workspace_bytes(B, w.seqlen_q, w.heads_q, w.headdim), "no stored-dS area"
+    ws.fill_(0xFF)  # the workspace's contents on entry must not matter (16-bit NaN in the dS area)
     run = fa.fa_bwd_deterministic if deterministic else fa.fa_bwd
     run(d["do"], d["q"], d["k"], d["v"], out, lse, dq, dk, dv, ws, causal=w.causal, scale=w.softmax_scale, **mk,
         **kw)
@@ -77,22 +84,29 @@ def W(name, B, Hq, Hkv, Sq, Sk, D, dtype, causal, seed=0, lengths=None, scale=No
                           window=window, alibi=alibi)
 
 
-def _full(w, deterministic=False):
+def _full(w, deterministic=False, stored_ds=False):
     x = synth.make_inputs(w)
-    say(f"bwd{' det' if deterministic else ''} {w.name} B={w.batch} Hq={w.heads_q} Hkv={w.heads_kv} Sq={w.seqlen_q} "
-        f"Sk={w.seqlen_k} D={w.headdim} {w.dtype} causal={w.causal} varlen={w.varlen}")
-    _, _, dq, dk, dv = run_fwd_bwd(w, x, deterministic=deterministic)
+    say(f"bwd{' det' if deterministic else ''}{' ds' if stored_ds else ''} {w.name} B={w.batch} Hq={w.heads_q} "
+        f"Hkv={w.heads_kv} Sq={w.seqlen_q} Sk={w.seqlen_k} D={w.headdim} {w.dtype} causal={w.causal} "
+        f"varlen={w.varlen}")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x, deterministic=deterministic, stored_ds=stored_ds)
     return check_grads(w, x, dq, dk, dv)
 
 
-def test_workload5_full():
+# the two routes of fa_bwd: the workspace with the stored-dS area, and the base workspace
+ROUTES = ["ds", "base"]
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_workload5_full(route):
     """Workload 5 at full size: dQ, dK and dV of all 32 (sequence, head) pairs against the
-    oracle's gradients, from the GPU's own forward outputs."""
+    oracle's gradients, from the GPU's own forward outputs, on both routes."""
     w, x = synth.draw_config(5)
-    say(f"bwd {w.name} (full tensor)")
-    _, _, dq, dk, dv = run_fwd_bwd(w, x)
+    say(f"bwd {w.name} (full tensor, route {route})")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x, stored_ds=route == "ds")
     errs = check_grads(w, x, dq, dk, dv)
-    msg = f"workload 5 ({w.name}) backward: rel-Frobenius (dq, dk, dv) = " + ", ".join(f"{e:.3e}" for e in errs)
+    msg = (f"workload 5 ({w.name}) backward, {'stored-dS' if route == 'ds' else 'atomic'} route: "
+           f"rel-Frobenius (dq, dk, dv) = " + ", ".join(f"{e:.3e}" for e in errs))
     print(msg)
     REPORT.append(msg)
 
@@ -106,52 +120,91 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_sweep(D, dtype, causal, shape):
+def test_sweep(D, dtype, causal, shape, route):
     B, Hq, Hkv, Sq, Sk = shape
-    print(_full(W(f"bwd_{dtype}_d{D}_c{int(causal)}", B, Hq, Hkv, Sq, Sk, D, dtype, causal, seed=D + Sq + 1)))
+    print(_full(W(f"bwd_{dtype}_d{D}_c{int(causal)}", B, Hq, Hkv, Sq, Sk, D, dtype, causal, seed=D + Sq + 1),
+                stored_ds=route == "ds"))
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen_ragged(D, causal):
+def test_varlen_ragged(D, causal, route):
     lq = [1, 129, 0, 300, 64, 17]
     lk = [5, 129, 3, 250, 64, 200]
     print(_full(W(f"bwd_varlen_d{D}_c{int(causal)}", None, 4, 2, None, None, D, "bf16", causal, seed=8,
-                  lengths=(lq, lk))))
+                  lengths=(lq, lk)), stored_ds=route == "ds"))
 
 
-def test_gqa_long():
-    print(_full(W("bwd_gqa_1k", 1, 8, 2, 1024, 1024, 128, "bf16", True, seed=9)))
+@pytest.mark.parametrize("route", ROUTES)
+def test_gqa_long(route):
+    print(_full(W("bwd_gqa_1k", 1, 8, 2, 1024, 1024, 128, "bf16", True, seed=9), stored_ds=route == "ds"))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_stored_ds_long_noncausal(D):
+    """Several query blocks per workgroup row range and many key blocks per query block
+    (S = 1100: five 256-key blocks, nine 128-row dQ workgroups, a ragged tail)."""
+    print(_full(W(f"bwd_ds_long_d{D}", 1, 4, 4, 1100, 1100, D, "bf16", False, seed=D + 40), stored_ds=True))
+
+
+def test_stored_ds_bitwise_repeatable_and_stages():
+    """The stored-dS route has no atomics: two runs give bitwise the same gradients, and
+    stages 1, 4, 5 through fa_bwd_stage give exactly what fa_bwd gives."""
+    w = W("bwd_ds_repeat", 2, 8, 2, 1500, 1500, 128, "bf16", True, seed=34)
+    x = synth.make_inputs(w)
+    say("bwd ds bitwise repeat and stages 1, 4, 5")
+    out, lse, dq, dk, dv = run_fwd_bwd(w, x, stored_ds=True)
+    _, _, dq2, dk2, dv2 = run_fwd_bwd(w, x, stored_ds=True)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    check_grads(w, x, dq, dk, dv)
+    d = dev(x)
+    grads = [torch.full_like(d[k], float("nan")) for k in ("q", "k", "v")]
+    ws = fa.workspace_for(d["q"], k=d["k"], stored_ds=True)
+    ws.fill_(0xFF)
+    args = (d["do"], d["q"], d["k"], d["v"], out, lse, *grads, ws)
+    for stage in (1, 4, 5):
+        fa.fa_bwd_stage(stage, *args, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(grads[0], dq) and torch.equal(grads[1], dk) and torch.equal(grads[2], dv)
+    # stages 4 and 5 refuse a workspace without the dS area
+    small = fa.workspace_for(d["q"])
+    with pytest.raises(RuntimeError, match="stored-dS"):
+        fa.fa_bwd_stage(4, *args[:-1], small, causal=True)
 
 
 # ---------------------------------------------------------------- deterministic backward
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES[:3], ids=lambda s: "x".join(map(str, s)))
-def test_deterministic_sweep(D, causal, shape):
+def test_deterministic_sweep(D, causal, shape, route):
     B, Hq, Hkv, Sq, Sk = shape
     print(_full(W(f"bwd_det_d{D}_c{int(causal)}", B, Hq, Hkv, Sq, Sk, D, "bf16", causal, seed=D + Sq + 2),
-                deterministic=True))
+                deterministic=True, stored_ds=route == "ds"))
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("causal", [False, True])
-def test_deterministic_varlen_fp16(causal):
+def test_deterministic_varlen_fp16(causal, route):
     lq = [1, 129, 0, 300, 64, 17]
     lk = [5, 129, 3, 250, 64, 200]
     print(_full(W(f"bwd_det_varlen_c{int(causal)}", None, 4, 2, None, None, 128, "fp16", causal, seed=9,
-                  lengths=(lq, lk)), deterministic=True))
+                  lengths=(lq, lk)), deterministic=True, stored_ds=route == "ds"))
 
 
-def test_deterministic_is_bitwise_repeatable_and_matches_workload5():
+@pytest.mark.parametrize("route", ROUTES)
+def test_deterministic_is_bitwise_repeatable_and_matches_workload5(route):
     w, x = synth.draw_config(5)
-    say(f"bwd det {w.name}")
-    _, _, dq, dk, dv = run_fwd_bwd(w, x, deterministic=True)
-    _, _, dq2, dk2, dv2 = run_fwd_bwd(w, x, deterministic=True)
+    say(f"bwd det {w.name} route {route}")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x, deterministic=True, stored_ds=route == "ds")
+    _, _, dq2, dk2, dv2 = run_fwd_bwd(w, x, deterministic=True, stored_ds=route == "ds")
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
     print("workload 5 deterministic full-tensor rel-Frobenius:", check_grads(w, x, dq, dk, dv))
 
@@ -167,12 +220,12 @@ def test_sweep_point_d64_s2048_sampled_heads():
 
 # ---------------------------------------------------------------- the main loop's key-block queue
 
-def _setup(w):
+def _setup(w, stored_ds=False):
     x = synth.make_inputs(w)
     d = dev(x)
     out, lse = fa.forward(d["q"], d["k"], d["v"], causal=w.causal, scale=w.softmax_scale)
     grads = [torch.full_like(d[k], float("nan")) for k in ("q", "k", "v")]
-    ws = fa.workspace_for(d["q"])
+    ws = fa.workspace_for(d["q"], k=d["k"], stored_ds=stored_ds)
     ws.fill_(0xFF)
     args = (d["do"], d["q"], d["k"], d["v"], out, lse, *grads, ws)
     return x, d, grads, args
@@ -215,13 +268,14 @@ def test_staged_atomic_route_wide_heads(D):
     print(check_grads(w, x, dq, dk, dv))
 
 
-def test_backward_graph_replays():
+@pytest.mark.parametrize("route", ROUTES)
+def test_backward_graph_replays(route):
     """The whole backward captured in a HIP graph (no memset nodes; the queue counters are
     reset by the kernels themselves) and replayed several times, with eager work between
     the replays: every replay matches the eager result."""
     w = W("graph_bwd", 2, 8, 2, 1500, 1500, 128, "bf16", True, seed=32)
-    say("bwd graph capture and replays")
-    x, d, (dq, dk, dv), args = _setup(w)
+    say(f"bwd graph capture and replays, route {route}")
+    x, d, (dq, dk, dv), args = _setup(w, stored_ds=route == "ds")
     fa.fa_bwd(*args, causal=True)
     torch.cuda.synchronize()
     ref = [t.clone() for t in (dq, dk, dv)]

@@ -34,20 +34,23 @@ def test_forward_varlen(D):
     tf._full_check(tf.W(f"hd_fwd_varlen_d{D}", None, 4, 2, None, None, D, "bf16", True, seed=D + 3, lengths=(lq, lk)))
 
 
+@pytest.mark.parametrize("route", tb.ROUTES)
 @pytest.mark.parametrize("D", DIMS)
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward(D, causal):
+def test_backward(D, causal, route):
     dtype = "fp16" if D % 16 else "bf16"
-    print(tb._full(tb.W(f"hd_bwd_d{D}_c{int(causal)}", 2, 4, 2, 300, 300, D, dtype, causal, seed=D * 11)))
+    print(tb._full(tb.W(f"hd_bwd_d{D}_c{int(causal)}", 2, 4, 2, 300, 300, D, dtype, causal, seed=D * 11),
+                   stored_ds=route == "ds"))
 
 
+@pytest.mark.parametrize("route", tb.ROUTES)
 @pytest.mark.parametrize("D", [32, 96, 160, 192])
 @pytest.mark.parametrize("causal", [False, True])
-def test_backward_varlen_gqa(D, causal):
+def test_backward_varlen_gqa(D, causal, route):
     lq = [1, 129, 0, 300, 64, 17]
     lk = [5, 129, 3, 250, 64, 200]
     print(tb._full(tb.W(f"hd_bwd_varlen_d{D}_c{int(causal)}", None, 6, 2, None, None, D, "bf16", causal, seed=D + 5,
-                        lengths=(lq, lk))))
+                        lengths=(lq, lk)), stored_ds=route == "ds"))
 
 
 @pytest.mark.parametrize("D", [32, 96, 160, 192])
@@ -60,6 +63,7 @@ def test_window_alibi(D):
     w = tb.W(f"hd_local_d{D}", 2, 4, 2, 300, 280, D, "bf16", True, seed=D + 13, window=(70, 0), alibi="head")
     print(tb._full(w))
     print(tb._full(w, deterministic=True))
+    print(tb._full(w, stored_ds=True))
 
 
 @pytest.mark.parametrize("D", [32, 96, 160, 192])

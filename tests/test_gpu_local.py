@@ -31,12 +31,12 @@ def _fwd(w):
     return compare_forward(w, o, lse, o_ref, lse_ref, where=w.name), o, lse
 
 
-def _bwd(w, deterministic=False):
+def _bwd(w, deterministic=False, stored_ds=False):
     x = synth.make_inputs(w)
-    say(f"bwd{' det' if deterministic else ''} {w.name} B={w.batch} Hq={w.heads_q} Hkv={w.heads_kv} "
-        f"Sq={w.seqlen_q} Sk={w.seqlen_k} D={w.headdim} {w.dtype} causal={w.causal} window={w.window} "
-        f"alibi={w.alibi} varlen={w.varlen}")
-    _, _, dq, dk, dv = run_fwd_bwd(w, x, deterministic=deterministic)
+    say(f"bwd{' det' if deterministic else ''}{' ds' if stored_ds else ''} {w.name} B={w.batch} Hq={w.heads_q} "
+        f"Hkv={w.heads_kv} Sq={w.seqlen_q} Sk={w.seqlen_k} D={w.headdim} {w.dtype} causal={w.causal} "
+        f"window={w.window} alibi={w.alibi} varlen={w.varlen}")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x, deterministic=deterministic, stored_ds=stored_ds)
     return check_grads(w, x, dq, dk, dv)
 
 
@@ -111,35 +111,40 @@ def test_fwd_long_window_sampled():
 
 # ---------------------------------------------------------------- backward
 
+@pytest.mark.parametrize("route", ["ds", "base"])
 @pytest.mark.parametrize("window", WINDOWS, ids=lambda w: f"w{w[0]}_{w[1]}")
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_bwd_window(window, causal, shape):
+def test_bwd_window(window, causal, shape, route):
     B, Hq, Hkv, Sq, Sk = shape
     print(_bwd(WB(f"bwd_win{window}_c{int(causal)}", B, Hq, Hkv, Sq, Sk, 128, "bf16", causal, seed=Sq + window[1],
-                  window=window)))
+                  window=window), stored_ds=route == "ds"))
 
 
+@pytest.mark.parametrize("route", ["ds", "base"])
 @pytest.mark.parametrize("D", [64, 256])
-def test_bwd_window_headdims(D):
-    print(_bwd(WB(f"bwd_win_d{D}", 2, 4, 2, 333, 333, D, "bf16", True, seed=D + 3, window=(70, -1))))
-    print(_bwd(WB(f"bwd_win2_d{D}", 1, 4, 4, 200, 260, D, "fp16", False, seed=D + 4, window=(33, 17))))
+def test_bwd_window_headdims(D, route):
+    ds = route == "ds"
+    print(_bwd(WB(f"bwd_win_d{D}", 2, 4, 2, 333, 333, D, "bf16", True, seed=D + 3, window=(70, -1)), stored_ds=ds))
+    print(_bwd(WB(f"bwd_win2_d{D}", 1, 4, 4, 200, 260, D, "fp16", False, seed=D + 4, window=(33, 17)), stored_ds=ds))
 
 
+@pytest.mark.parametrize("route", ["ds", "base"])
 @pytest.mark.parametrize("alibi", ["head", "batch_head"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("D", [64, 128, 256])
-def test_bwd_alibi(alibi, causal, D):
+def test_bwd_alibi(alibi, causal, D, route):
     print(_bwd(WB(f"bwd_alibi_{alibi}_c{int(causal)}_d{D}", 2, 4, 2, 300, 280, D, "bf16", causal, seed=D + 9,
-                  alibi=alibi)))
+                  alibi=alibi), stored_ds=route == "ds"))
 
 
+@pytest.mark.parametrize("route", ["ds", "base"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_alibi_with_window_varlen(causal):
+def test_bwd_alibi_with_window_varlen(causal, route):
     lq = [1, 129, 0, 300, 64, 17]
     lk = [5, 129, 3, 250, 64, 200]
     print(_bwd(WB(f"bwd_alibi_win_varlen_c{int(causal)}", None, 4, 2, None, None, 128, "bf16", causal, seed=25,
-                  lengths=(lq, lk), window=(48, 16), alibi="head")))
+                  lengths=(lq, lk), window=(48, 16), alibi="head"), stored_ds=route == "ds"))
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
