@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the exact-attention hot path on one MI355X.
 
-A step is one forward (fa_fwd) plus one backward (fa_bwd: preprocess, dK/dV main loop
-with dQ accumulation, dQ finalize) over the causal MHA workload B=2, H=16, S=4096,
-D=128, bf16 -- the reference workload that includes the backward.  Inputs are seeded
-synthetic N(0,1) draws, resident in HBM before timing starts.
+A step is one forward (fa_fwd) plus one backward (fa_bwd with the workspace the binding
+allocates by default, which holds the stored-dS area: preprocess, dK/dV main loop that
+stores dS, dQ from the stored dS) over the causal MHA workload B=2, H=16, S=4096, D=128,
+bf16 -- the reference workload that includes the backward.  Inputs are seeded synthetic
+N(0,1) draws, resident in HBM before timing starts.
 
 Prints ONE JSON line: throughput in algorithmic TFLOPS (forward 4*B*H*S*S*D/2 for causal,
 backward 2.5x that; masked work and recomputation are not counted), the roofline of the
@@ -64,7 +65,9 @@ class Case:
         self.lse = torch.empty(fa.lse_shape(d["q"], d.get("cu_seqlens_q")), dtype=torch.float32, device="cuda")
         if with_bwd:
             self.dq, self.dk, self.dv = (torch.empty_like(d[k]) for k in ("q", "k", "v"))
-            self.ws = fa.workspace_for(d["q"])
+            # the binding's default workspace: with the stored-dS area (fa_bwd's fastest
+            # route); its first fa_bwd_workspace_bytes serve the atomic route's stages too
+            self.ws = fa.workspace_for(d["q"], k=d["k"], stored_ds=True)
         self.fwd_flops, self.bwd_flops = synth.flops(self.w)
 
     def fwd(self):
@@ -183,7 +186,7 @@ def sweep(steps: int, warmup: int):
                 out = torch.empty_like(x["q"])
                 lse = torch.empty(fa.lse_shape(x["q"]), dtype=torch.float32, device="cuda")
                 dq, dk, dv = (torch.empty_like(x[k]) for k in ("q", "k", "v"))
-                ws = fa.workspace_for(x["q"])
+                ws = fa.workspace_for(x["q"], k=x["k"], stored_ds=True)  # the binding's default route
                 fwd = lambda: fa.fa_fwd(x["q"], x["k"], x["v"], out, lse, causal=causal)
                 bwd = lambda: fa.fa_bwd(x["do"], x["q"], x["k"], x["v"], out, lse, dq, dk, dv, ws, causal=causal)
                 for _ in range(warmup):
@@ -309,20 +312,23 @@ def main():
         n = max(3, K // 4)
         for _ in range(max(1, W // 4)):
             c3.bwd_stage(0)
-        # preprocess and finalize: device time from a graph of 10 calls; the main loop
-        # (milliseconds) per launch, each after a preprocess that resets its key-block queue
-        t3p = time_graph(lambda: c3.bwd_stage(1), 10, n)
-        t3m = time_launches(lambda: c3.bwd_stage(2), n, pre=lambda: c3.bwd_stage(1))
-        t3f = time_graph(lambda: c3.bwd_stage(3), 10, n)
+        # the whole backward (fa_bwd, stored-dS route) per launch; its stages, and those of the
+        # atomic route, per launch (milliseconds each; the main loops after a preprocess
+        # that resets the key-block queue)
+        t3b = time_launches(lambda: c3.bwd_stage(0), n)
+        t3m = time_launches(lambda: c3.bwd_stage(4), n, pre=lambda: c3.bwd_stage(1))
+        t3q = time_launches(lambda: c3.bwd_stage(5), n)
+        t3a = time_launches(lambda: c3.bwd_stage(2), n, pre=lambda: c3.bwd_stage(1))
         detail[c3.w.name] = {
             "fwd_tflops": c3.fwd_flops / t3 / 1e12, "fwd_pct_peak": 100 * c3.fwd_flops / t3 / 1e12 / PEAK_TFLOPS,
             "fwd_us": t3 * 1e6, "fwd_us_median": st3["median"] * 1e6, "fwd_us_min": st3["min"] * 1e6,
-            "bwd_tflops": c3.bwd_flops / (t3p + t3m + t3f) / 1e12,
-            "bwd_pct_peak": 100 * c3.bwd_flops / (t3p + t3m + t3f) / 1e12 / PEAK_TFLOPS,
-            "bwd_pre_us": t3p * 1e6, "bwd_main_us": t3m * 1e6, "bwd_fin_us": t3f * 1e6,
+            "bwd_tflops": c3.bwd_flops / t3b / 1e12, "bwd_pct_peak": 100 * c3.bwd_flops / t3b / 1e12 / PEAK_TFLOPS,
+            "bwd_us": t3b * 1e6, "bwd_main_store_ds_us": t3m * 1e6, "bwd_dq_from_ds_us": t3q * 1e6,
+            "bwd_main_atomic_route_us": t3a * 1e6,
         }
         log(f"[bench] GQA S=8192 forward {t3 * 1e6:.1f} us -> {detail[c3.w.name]['fwd_tflops']:.1f} TFLOPS; "
-            f"backward {(t3p + t3m + t3f) * 1e6:.1f} us -> {detail[c3.w.name]['bwd_tflops']:.1f} TFLOPS")
+            f"backward {t3b * 1e6:.1f} us -> {detail[c3.w.name]['bwd_tflops']:.1f} TFLOPS "
+            f"(main loop {t3m * 1e6:.1f} us, dQ from dS {t3q * 1e6:.1f} us; atomic main loop {t3a * 1e6:.1f} us)")
         del c3
         torch.cuda.empty_cache()
 
@@ -391,40 +397,56 @@ def main():
     value = step_flops / (ms * 1e-3) / 1e12
     log(f"[bench] step {ms:.3f} ms -> {value:.1f} TFLOPS")
 
-    # per-kernel durations (HIP events on the launch stream); the preprocess and finalize
-    # (~15-25 us) also as device time from a graph of 10 calls, which the backward figure uses
+    # per-kernel durations (HIP events on the launch stream).  The stored-dS route that the
+    # step runs: preprocess (device time from a graph of 10 calls, ~15 us), the main loop
+    # that stores dS (the dominant kernel), dQ from the stored dS.  Then the atomic route's
+    # stages and the deterministic call with only the base workspace (recompute route).
     st_fwd, st_main = {}, {}
     t_fwd = time_launches(c5.fwd, K, stats=st_fwd)
-    t_pre_launch = time_launches(lambda: c5.bwd_stage(1), K)
-    t_main = time_launches(lambda: c5.bwd_stage(2), K, pre=lambda: c5.bwd_stage(1), post=lambda: c5.bwd_stage(3),
+    t_bwd = time_launches(lambda: c5.bwd_stage(0), K)
+    t_main = time_launches(lambda: c5.bwd_stage(4), K, pre=lambda: c5.bwd_stage(1), post=lambda: c5.bwd_stage(5),
                            stats=st_main)
-    t_fin_launch = time_launches(lambda: c5.bwd_stage(3), K)
+    t_dq = time_launches(lambda: c5.bwd_stage(5), K)
     t_pre = time_graph(lambda: c5.bwd_stage(1), 10, max(3, K // 4))
+    t_amain = time_launches(lambda: c5.bwd_stage(2), K, pre=lambda: c5.bwd_stage(1), post=lambda: c5.bwd_stage(3))
     t_fin = time_graph(lambda: c5.bwd_stage(3), 10, max(3, K // 4))
+    ws_full = c5.ws
+    c5.ws = fa.workspace_for(c5.d["q"])  # base workspace only: fa_bwd takes the atomic route
+    t_atomic = time_launches(lambda: c5.bwd_stage(0), max(3, K // 4))
     t_det = time_launches(lambda: c5.bwd_stage("deterministic"), max(3, K // 4))
+    c5.ws = ws_full
     B, S, H, D = c5.w.batch, c5.w.seqlen_q, c5.w.heads_q, c5.w.headdim
-    pre_bytes = B * S * H * (2 * D * 2 + D * 4 + 4)   # read O, dO (16-bit); write fp32 acc zeros + Dsum
     fin_bytes = B * S * H * D * (4 + 2)               # read fp32 acc, write dQ
-    main_tflops = c5.bwd_flops / t_main / 1e12
-    # fp32 dQ atomics of the main loop: one per (query row, head, column, 256-key block the row sees)
+    # the main loop of the stored-dS route does 4 of the 5 products (the dQ product is the
+    # dQ pass's): its algorithmic FLOPs are 4/5 of the backward's
+    main_flops = 0.8 * c5.bwd_flops
+    main_tflops = main_flops / t_main / 1e12
+    # stored dS: one 16-bit value per (query row, key) pair a 256-key block's step range
+    # covers, written once by the main loop and read once by the dQ pass
     kb = 256
+    ds_pairs = B * H * sum(S - min(S, j * kb) for j in range((S + kb - 1) // kb)) * kb
+    # fp32 dQ atomics of the atomic route: one per (query row, head, column, 256-key block)
     n_atomics = B * H * D * sum(S - min(S, j * kb) for j in range((S + kb - 1) // kb))
     detail[c5.w.name] = {
         "fwd_tflops": c5.fwd_flops / t_fwd / 1e12,
         "fwd_pct_peak": 100 * c5.fwd_flops / t_fwd / 1e12 / PEAK_TFLOPS,
-        "bwd_tflops": c5.bwd_flops / (t_pre + t_main + t_fin) / 1e12,
-        "bwd_pct_peak": 100 * c5.bwd_flops / (t_pre + t_main + t_fin) / 1e12 / PEAK_TFLOPS,
-        "fwd_us": t_fwd * 1e6, "bwd_pre_us": t_pre * 1e6, "bwd_main_us": t_main * 1e6, "bwd_fin_us": t_fin * 1e6,
+        "bwd_tflops": c5.bwd_flops / t_bwd / 1e12,
+        "bwd_pct_peak": 100 * c5.bwd_flops / t_bwd / 1e12 / PEAK_TFLOPS,
+        "fwd_us": t_fwd * 1e6, "bwd_us": t_bwd * 1e6,
+        "bwd_pre_us": t_pre * 1e6, "bwd_main_us": t_main * 1e6, "bwd_dq_from_ds_us": t_dq * 1e6,
         "fwd_us_median": st_fwd["median"] * 1e6, "fwd_us_min": st_fwd["min"] * 1e6,
         "bwd_main_us_median": st_main["median"] * 1e6, "bwd_main_us_min": st_main["min"] * 1e6,
-        "bwd_pre_gbs": pre_bytes / t_pre / 1e9, "bwd_fin_gbs": fin_bytes / t_fin / 1e9,
-        "bwd_pre_us_per_launch": t_pre_launch * 1e6, "bwd_fin_us_per_launch": t_fin_launch * 1e6,
-        "bwd_deterministic_us": t_det * 1e6, "bwd_deterministic_tflops": c5.bwd_flops / t_det / 1e12,
-        "bwd_main_dq_atomics": n_atomics,
-        # the main loop against the time its atomics need at the chip's rate (16 adds per request)
-        "bwd_main_atomic_floor_us": n_atomics / 16 / ATOMIC_REQ_PER_S * 1e6,
-        "bwd_main_vs_atomic_floor": n_atomics / 16 / ATOMIC_REQ_PER_S / t_main,
+        "bwd_dq_from_ds_gbs": 2 * ds_pairs / t_dq / 1e9, "bwd_ds_bytes": 2 * ds_pairs,
+        "bwd_atomic_route_us": t_atomic * 1e6, "bwd_atomic_route_tflops": c5.bwd_flops / t_atomic / 1e12,
+        "bwd_atomic_main_us": t_amain * 1e6, "bwd_fin_us": t_fin * 1e6, "bwd_fin_gbs": fin_bytes / t_fin / 1e9,
+        "bwd_deterministic_recompute_us": t_det * 1e6,
+        "bwd_atomic_main_dq_atomics": n_atomics,
+        # the atomic main loop against the time its atomics need at the chip's rate (16 adds per request)
+        "bwd_atomic_main_floor_us": n_atomics / 16 / ATOMIC_REQ_PER_S * 1e6,
+        "bwd_atomic_main_vs_floor": n_atomics / 16 / ATOMIC_REQ_PER_S / t_amain,
     }
+    log(f"[bench] backward {t_bwd * 1e6:.1f} us (pre {t_pre * 1e6:.1f}, main {t_main * 1e6:.1f}, dQ from dS "
+        f"{t_dq * 1e6:.1f}); atomic route {t_atomic * 1e6:.1f} us (main {t_amain * 1e6:.1f})")
     del c5
     torch.cuda.empty_cache()
 
@@ -455,7 +477,8 @@ def main():
                      "traffic_note": ("HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE counter "
                                       "summary of this kernel source, scaled by a 512 MiB copy; not measured in "
                                       "this run") if traffic is not None else "no counter summary for this source",
-                     "kernel": "bwd_main_k256_kernel<D=128, bf16, causal, padded, dQ atomics>"},
+                     "kernel": "bwd_main_k256_kernel<D=128, bf16, causal, padded, no dQ> storing dS "
+                               "(4 of the backward's 5 products)"},
         "cpu_baseline": cpu,
         "detail": detail,
     }

@@ -275,8 +275,5 @@ struct KeyWindow {
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void store16(void* p, u32x4 x) { *(u32x4*)p = x; }
-// 16-byte store with the non-temporal (streaming) hint: data written once and read back
-// only much later, which should not displace reused lines from the caches.
-__device__ __forceinline__ void store16_stream(void* p, u32x4 x) { __builtin_nontemporal_store(x, (u32x4*)p); }
 
 }  // namespace fa
