@@ -22,9 +22,14 @@
 //      keys per workgroup (8 wavefronts of 32 keys); D = 256 uses 128 keys (4
 //      wavefronts), which its register footprint requires;
 //   3. finalize: scale * fp32 accumulator -> dQ in the input dtype.
+// Two routes form dQ without atomics.  The stored-dS route (fa_bwd's when the workspace
+// holds the area): the main loop without the dQ product stores each step's dS / scale in
+// the input dtype -- the values the dQ product would have taken -- and a memory-bound pass
+// (2d) forms dQ = scale dS K once per query row from them.  The recompute route (2c, no
+// extra workspace): a forward-shaped pass computes S and dP a second time.
 // The main loops form dS / scale (one multiply less per score) and apply the softmax scale
-// once to dK at its store and to dQ in the finalize; the preprocess also writes
-// LSE * log2(e) per (row, head), the exp2 offset of P in the D <= 128 main loop.
+// once to dK at its store and to dQ in the finalize or the dQ passes; the preprocess also
+// writes LSE * log2(e) per (row, head), the exp2 offset of P in the D <= 128 main loop.
 // Sliding window and ALiBi (flash_attn_func docstring, window_size and alibi_slopes): the
 // kept keys of query i are [lo(i), hi(i)] as in the forward (KeyWindow); the main loops
 // visit only the query rows that keep a key of their block, and the ALiBi bias
