@@ -45,7 +45,6 @@
 namespace fa {
 namespace {
 
-constexpr int kXcds = 8;  // XCDs of the MI355X; workgroups are dispatched to them round-robin
 constexpr int kBwdWaves = 4;
 constexpr int kBwdBN = 32 * kBwdWaves;  // keys per workgroup
 constexpr int kBwdBQ = 32;              // query rows per inner step
@@ -121,8 +120,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     }
     a.lse2[pair] = a.lse[li] * 1.4426950408889634f;
   }
-  if (blockIdx.x == 0 && tid == 0) {  // the main loop's key-block queues start empty
-    for (int i = 0; i < 2 + kXcds; ++i) a.work[i] = 0;
+  if (blockIdx.x == 0 && tid == 0) {  // the main loop's key-block queue starts empty
+    a.work[0] = 0;
+    a.work[1] = 0;
   }
 }
 
@@ -917,32 +917,20 @@ template <int D, bool BF16, bool MASKED, bool VARLEN, bool DQ, bool ALIBI>
 __global__ __launch_bounds__(512, 1) void bwd_main_k256_kernel(BwdArgs a) {
   if (debug_stop(a.dbg)) return;
   __shared__ int next;
-  const int nbh = a.B * a.Hkv;
-  const int nblocks = (a.Sk + kK2Keys - 1) / kK2Keys * nbh;
-  // XCD-aware queues: workgroups are dispatched to the 8 XCDs round-robin, so workgroup i
-  // runs on XCD i % 8; when the (sequence, KV head) pairs split evenly, that XCD takes the
-  // key blocks of the pairs bh = i % 8 (mod 8) from a queue of its own (work[2 + i % 8]),
-  // so that the Q / dO rows of a pair are fetched into one L2 only.  Otherwise one queue
-  // (work[0]) serves every workgroup.  Either way every key block is taken exactly once.
-  const bool per_xcd = nbh % kXcds == 0 && gridDim.x % kXcds == 0;
-  const int x = per_xcd ? (int)(blockIdx.x % kXcds) : 0;
-  unsigned int* queue = per_xcd ? a.work + 2 + x : a.work;
-  const int units = per_xcd ? nblocks / kXcds : nblocks;
-  const int nbx = nbh / kXcds;
+  const int nblocks = (a.Sk + kK2Keys - 1) / kK2Keys * a.B * a.Hkv;
   for (;;) {
     wait_all_memory();  // the previous block's loads into LDS and its atomics are done
-    if (threadIdx.x == 0) next = (int)atomicAdd(queue, 1u);
+    if (threadIdx.x == 0) next = (int)atomicAdd(a.work, 1u);
     __syncthreads();
-    const int u = next;
+    const int lin = next;
     __syncthreads();  // every wavefront has read it before it is overwritten
-    if (u >= units) break;
-    // key block kb = lin / nbh of pair bh = lin % nbh, ascending key blocks (longest first)
-    const int lin = per_xcd ? (u / nbx) * nbh + x + kXcds * (u % nbx) : u;
+    if (lin >= nblocks) break;
     bwd_k256_block<D, BF16, MASKED, VARLEN, DQ, ALIBI>(a, lin);
   }
   if (threadIdx.x == 0 && atomicAdd(a.work + 1, 1u) == gridDim.x - 1) {
-    // Every workgroup is past its last take from the queues.
-    for (int i = 0; i < 2 + kXcds; ++i) a.work[i] = 0;
+    // Every workgroup is past its last take from the queue.
+    a.work[0] = 0;
+    a.work[1] = 0;
   }
 }
 

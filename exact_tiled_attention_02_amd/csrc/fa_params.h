@@ -62,8 +62,7 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int zero_acc;  // preprocess also zeroes dq_acc (the atomic path needs it)
-  unsigned int* work;  // [10]: key blocks handed out (one queue), workgroups finished, then the
-                       // per-XCD queues (all zero between launches)
+  unsigned int* work;  // [2]: key blocks handed out, workgroups finished (zero between launches)
   // Stored dS / scale in the input dtype (the route without dQ atomics), or null: one tile
   // of 32 query rows x KB keys (KB = keys per main-loop workgroup: 256 up to a 128-wide
   // tile, 128 above) per (sequence, query head, query step, key block), tile index
