@@ -187,13 +187,17 @@ def sweep(steps: int, warmup: int):
                 lse = torch.empty(fa.lse_shape(x["q"]), dtype=torch.float32, device="cuda")
                 dq, dk, dv = (torch.empty_like(x[k]) for k in ("q", "k", "v"))
                 ws = fa.workspace_for(x["q"], k=x["k"], stored_ds=True)  # the binding's default route
+                ws_base = fa.workspace_for(x["q"])                         # atomic route, for comparison
                 fwd = lambda: fa.fa_fwd(x["q"], x["k"], x["v"], out, lse, causal=causal)
                 bwd = lambda: fa.fa_bwd(x["do"], x["q"], x["k"], x["v"], out, lse, dq, dk, dv, ws, causal=causal)
+                bwd_a = lambda: fa.fa_bwd(x["do"], x["q"], x["k"], x["v"], out, lse, dq, dk, dv, ws_base,
+                                          causal=causal)
                 for _ in range(warmup):
                     fwd()
                     bwd()
                 tf = time_launches(fwd, steps)
                 tb = time_launches(bwd, steps)
+                ta = time_launches(bwd_a, steps)
                 ff, fb = synth.flops(w)
                 rec = {"workload": w.name, "batch": B, "heads": H, "seqlen": S, "headdim": D, "causal": causal,
                        "fwd_tflops": ff / tf / 1e12, "bwd_tflops": fb / tb / 1e12,
@@ -201,9 +205,9 @@ def sweep(steps: int, warmup: int):
                        "fwd_pct_peak": 100 * ff / tf / 1e12 / PEAK_TFLOPS,
                        "bwd_pct_peak": 100 * fb / tb / 1e12 / PEAK_TFLOPS,
                        "fwdbwd_pct_peak": 100 * (ff + fb) / (tf + tb) / 1e12 / PEAK_TFLOPS,
-                       "fwd_us": tf * 1e6, "bwd_us": tb * 1e6}
+                       "fwd_us": tf * 1e6, "bwd_us": tb * 1e6, "bwd_atomic_route_us": ta * 1e6}
                 print(json.dumps(rec), flush=True)
-                del x, out, lse, dq, dk, dv, ws
+                del x, out, lse, dq, dk, dv, ws, ws_base
                 torch.cuda.empty_cache()
 
 

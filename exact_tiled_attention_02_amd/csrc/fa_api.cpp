@@ -237,8 +237,15 @@ namespace {
 // dQ element per 128 keys, and the memory-side atomic rate bounds it: B=1 H=16 S=8192
 // D=256 causal 5.3 ms against 3.1 ms for the two passes), so there the recompute route
 // serves the default backward too.
+// At tile width 64 the stored-dS route moves the same 4 bytes of dS per (row, key) pair as at
+// 128 for half the products, and the atomic route issues half the atomics per pair: there
+// the atomic route is the faster one (hidden 2048 as 32 heads of 64, S = 16k: 7.2 ms
+// against 10.3 ms), so fa_bwd keeps it even when the workspace holds the dS area; the
+// deterministic call still takes the stored-dS route, which avoids the second computation
+// of S and dP.
 int full_bwd_stages(int D, bool deterministic, bool stored_ds) {
-  if (stored_ds) return fa::kBwdPre | fa::kBwdMainStoreDs | fa::kBwdDqFromDs;
+  if (stored_ds && (deterministic || fa::tile_headdim(D) >= 128))
+    return fa::kBwdPre | fa::kBwdMainStoreDs | fa::kBwdDqFromDs;
   return deterministic || fa::tile_headdim(D) > 128 ? (fa::kBwdPre | fa::kBwdRecompute)
                                                     : (fa::kBwdPre | fa::kBwdMainAtomic | fa::kBwdFinalize);
 }

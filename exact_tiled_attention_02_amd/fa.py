@@ -332,10 +332,12 @@ def backward(dout, q, k, v, out, lse, causal: bool = False, scale: float | None 
              window_size=(-1, -1), alibi_slopes=None, stored_ds: bool = True):
     """Allocate (dq, dk, dv) and the workspace, and run :func:`fa_bwd` (or
     :func:`fa_bwd_deterministic`).  ``stored_ds`` gives the workspace the stored-dS area
-    (the fastest route, deterministic) when it is available at this size; without it the
-    backward takes the atomic route (or, deterministic or D > 128, the recompute route)."""
+    when the call will take that route (D > 64, or deterministic) and it is available at
+    this size: the fastest route there, and deterministic; without it the backward takes
+    the atomic route (or, deterministic or D > 128, the recompute route)."""
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = workspace_for(q, cu_seqlens_q, max_seqlen_q, k, max_seqlen_k, stored_ds)
+    use_ds = stored_ds and (deterministic or q.shape[-1] > 64)
+    ws = workspace_for(q, cu_seqlens_q, max_seqlen_q, k, max_seqlen_k, use_ds)
     run = fa_bwd_deterministic if deterministic else fa_bwd
     run(dout, q, k, v, out, lse, dq, dk, dv, ws, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
         max_seqlen_k, stream, window_size, alibi_slopes)

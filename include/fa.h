@@ -140,13 +140,13 @@ size_t fa_bwd_ds_workspace_bytes(int B, int Sq, int Sk, int Hq, int D);
  * stored).  Other arguments as for fa_fwd.  `workspace` (16-byte aligned) must hold
  * fa_bwd_workspace_bytes(B, Sq, Hq, D) bytes; its contents on entry do not matter.
  * dq, dk, dv are fully overwritten (rows beyond a varlen sequence are not touched).
- * Route: when fa_bwd_ds_workspace_bytes(B, Sq, Sk, Hq, D) is nonzero and the workspace
- * holds both sizes, dQ is formed from the stored dS (the fastest route, and bitwise
- * repeatable; the dS area follows the first fa_bwd_workspace_bytes bytes, rounded up to
- * 256).  Otherwise, for D <= 128, dq is accumulated with fp32 atomics, so the result may
- * differ in the last bits from run to run, and for D > 128 fa_bwd runs the recompute
- * scheme of fa_bwd_deterministic, which is the faster one there.  The forward is bitwise
- * deterministic.
+ * Route: for D > 64, when fa_bwd_ds_workspace_bytes(B, Sq, Sk, Hq, D) is nonzero and the
+ * workspace holds both sizes, dQ is formed from the stored dS (the fastest route there, and
+ * bitwise repeatable; the dS area follows the first fa_bwd_workspace_bytes bytes, rounded
+ * up to 256).  Otherwise, for D <= 128, dq is accumulated with fp32 atomics, so the result
+ * may differ in the last bits from run to run (for D <= 64 this route is the faster one),
+ * and for D > 128 fa_bwd runs the recompute scheme of fa_bwd_deterministic.  The forward is
+ * bitwise deterministic.
  */
 int fa_bwd(const void* dout, const void* q, const void* k, const void* v,
            const void* out, const float* lse, void* dq, void* dk, void* dv,
@@ -160,9 +160,9 @@ int fa_bwd(const void* dout, const void* q, const void* k, const void* v,
  * atomics, so dq, dk and dv are bitwise identical from run to run (the pages' README
  * offers a deterministic backward: changelog entry 2.4 and the `deterministic`
  * argument of the flash_attn_func docstring).  With a workspace large enough for the
- * stored-dS route (see fa_bwd) it runs that route, the same kernels as fa_bwd; otherwise
- * it recomputes the scores and dP once more in the dQ pass, which for D <= 128 is slower
- * than fa_bwd's atomic route.
+ * stored-dS route (see fa_bwd) it runs that route at every D; otherwise it recomputes the
+ * scores and dP once more in the dQ pass, which for D <= 128 is slower than fa_bwd's
+ * atomic route.
  */
 int fa_bwd_deterministic(const void* dout, const void* q, const void* k, const void* v,
                          const void* out, const float* lse, void* dq, void* dk, void* dv,

@@ -149,8 +149,11 @@ def test_gqa_long(route):
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_stored_ds_long_noncausal(D):
     """Several query blocks per workgroup row range and many key blocks per query block
-    (S = 1100: five 256-key blocks, nine 128-row dQ workgroups, a ragged tail)."""
-    print(_full(W(f"bwd_ds_long_d{D}", 1, 4, 4, 1100, 1100, D, "bf16", False, seed=D + 40), stored_ds=True))
+    (S = 1100: five 256-key blocks, nine 128-row dQ workgroups, a ragged tail); the
+    deterministic call, which takes the stored-dS route at every head dimension (fa_bwd
+    keeps the atomic route at D <= 64)."""
+    print(_full(W(f"bwd_ds_long_d{D}", 1, 4, 4, 1100, 1100, D, "bf16", False, seed=D + 40), deterministic=True,
+                stored_ds=True))
 
 
 def test_stored_ds_bitwise_repeatable_and_stages():
