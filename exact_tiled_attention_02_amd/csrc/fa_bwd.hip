@@ -185,6 +185,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
   const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * Dr;
   const int diag = Lk - Lq;
   const float c = a.scale_log2;
+  const float inv_c = 1.0f / c;  // (as in the main loop for D <= 128)
   constexpr float kLog2e = 1.4426950408889634f;
   size_t lse_row0;  // index of row 0 of this sequence in the LSE of head 0
   size_t lse_hs;    // LSE stride between heads
@@ -312,7 +313,20 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
     // row reads run RA k-steps ahead of their products, in fenced order (left to itself
     // the scheduler sinks each read down to its product); with the dQ product (the staged
     // atomic route) one step ahead, as more registers would spill.
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // The accumulators start from -LSE log2(e) / c and -Dsum (register r = 4 g4 + j holds
+    // row 8 g4 + 4 lh + j; both come as vectors), so that the products leave S - LSE / scale
+    // and dP - Dsum, and no LSE or Dsum read waits after them.
+    f32x16 s, dp;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 l4 = *(const f32x4*)(lse_c + 8 * g4 + 4 * lh);
+      const f32x4 d4 = *(const f32x4*)(dsum_c + 8 * g4 + 4 * lh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[4 * g4 + j] = -l4[j] * (kLog2e * inv_c);
+        dp[4 * g4 + j] = d4[j];
+      }
+    }
     {
       constexpr int RA = DQ ? 1 : 2;
       Frag8 qa[RA], ga[RA], kf[RA];
@@ -334,22 +348,19 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     // P and dS / scale (the scale is applied to dK at its store and to dQ in the finalize).
-    // Register r = 4 g4 + j holds row 8 g4 + 4 lh + j: its LSE and -Dsum come as vectors.
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 l4 = *(const f32x4*)(lse_c + 8 * g4 + 4 * lh);
-      const f32x4 d4 = *(const f32x4*)(dsum_c + 8 * g4 + 4 * lh);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g4 + j;
         const int row = i0 + 8 * g4 + 4 * lh + j;
         bool keep = key_ok && row < Lq;
         if constexpr (MASKED) keep = keep && row >= rmin && row <= rmax;
-        float bias = -l4[j] * kLog2e;
-        if constexpr (ALIBI) bias = fmaf(-sl, fabsf((float)(row + diag - my_key)), bias);
-        const float p = keep ? fast_exp2(fmaf(s[r], c, bias)) : 0.f;
+        float e = s[r] * c;
+        if constexpr (ALIBI) e = fmaf(s[r], c, -sl * fabsf((float)(row + diag - my_key)));
+        const float p = keep ? fast_exp2(e) : 0.f;
         s[r] = p;
-        dp[r] = p * (dp[r] + d4[j]);  // dS / scale (the workspace holds -Dsum)
+        dp[r] = p * dp[r];  // dS / scale = P (dP - Dsum)
       }
     }
     Frag8 pf[2], dsf[2];
@@ -539,6 +550,11 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
   const uint16_t* vp = (const uint16_t*)a.v + (size_t)k_start * k_rs + (size_t)hk * Dr;
   const int diag = Lk - Lq;
   const float c = a.scale_log2;
+  // 1 / c: the S accumulator starts from -LSE log2(e) / c = -LSE / scale.  c >= 1e-30 (host
+  // clamp), and LSE / scale <= max q.k + ln(keys) / scale stays far inside the fp32 range;
+  // the exponent c S then carries an absolute error of about 2^-24 |LSE log2(e)|, far
+  // below the 16-bit rounding of P.  (A dead row's LSE of +inf gives -inf, and P = 0.)
+  const float inv_c = 1.0f / c;
   constexpr float kLog2e = 1.4426950408889634f;
 
   // Query rows that keep a key of this block, [i_begin, i_end), and the kept range of
@@ -677,13 +693,18 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
       live = !mask || (kw0 <= kw.hi(min(i0 + kK2BQ, Lq) - 1) && kw0 + 31 >= kw.lo(i0));
     }
     // dP starts from -Dsum of the step's rows (register r holds row 8 (r / 4) + 4 lh + r % 4),
-    // so that the products leave dP - Dsum.
-    f32x16 s = f32x16{}, dp;
+    // so that the products leave dP - Dsum, and S from -LSE log2(e) / c, so that they leave
+    // S - LSE / scale and P = exp2(c S) needs no LSE read after them.
+    f32x16 s, dp;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x4 d4 = *(const f32x4*)(dsum_c + 8 * g4 + 4 * lh);
+      const f32x4 l4 = *(const f32x4*)(lse_c + 8 * g4 + 4 * lh);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dp[4 * g4 + j] = d4[j];
+      for (int j = 0; j < 4; ++j) {
+        dp[4 * g4 + j] = d4[j];
+        s[4 * g4 + j] = -l4[j] * inv_c;
+      }
     }
     if (live) {
       // The row reads run SPD k-steps ahead of their products, written out in that order
@@ -722,13 +743,15 @@ __device__ __forceinline__ void bwd_k256_block(const BwdArgs& a, const int lin) 
     const float abase = (float)(i0 + 4 * lh + diag - my_key);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 l4 = *(const f32x4*)(lse_c + 8 * g4 + 4 * lh);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 4 * g4 + j;
-        float bias = -l4[j];  // LSE * log2(e), from the preprocess
-        if constexpr (ALIBI) bias = fmaf(-sl, fabsf(abase + (float)(8 * g4 + j)), bias);
-        const float p = fast_exp2(fmaf(s[r], c, bias));
+        float p;
+        if constexpr (ALIBI) {
+          p = fast_exp2(fmaf(s[r], c, -sl * fabsf(abase + (float)(8 * g4 + j))));
+        } else {
+          p = fast_exp2(s[r] * c);
+        }
         s[r] = p;
         dp[r] = p * dp[r];  // dS / scale = P (dP - Dsum)
       }
