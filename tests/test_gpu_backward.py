@@ -111,6 +111,40 @@ def test_workload5_full(route):
     REPORT.append(msg)
 
 
+def test_workload3_backward_full():
+    """The GQA workload at full size (B=2, Hq=32, Hkv=8, S=8192, causal, bf16) through the
+    stored-dS route (8 GiB of dS tiles): dQ of all 64 (sequence, query head) pairs and dK,
+    dV of all 16 (sequence, KV head) pairs, each summed over its four query heads, against
+    the oracle's gradients, from the GPU's own forward outputs."""
+    w = synth.config(3)
+    w.backward = True  # the same q, k, v draws as the forward workload, then dO
+    x = synth.make_inputs(w)
+    say(f"bwd {w.name} (full tensor, stored-dS route)")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x, stored_ds=True)
+    errs = check_grads(w, x, dq, dk, dv)
+    msg = (f"workload 3 ({w.name}) backward, stored-dS route: rel-Frobenius (dq, dk, dv) = "
+           + ", ".join(f"{e:.3e}" for e in errs))
+    print(msg)
+    REPORT.append(msg)
+
+
+def test_workload4_backward_full():
+    """The packed variable-length workload at full size (16 sequences of 128..4096 tokens,
+    H=8, D=256, fp16, causal) through the stored-dS route, whose D = 256 main loop holds 128
+    keys per workgroup: dQ, dK, dV of every token and head against the oracle."""
+    w, x = synth.draw_config(4)
+    w.backward = True
+    rng = np.random.default_rng(4000 + w.seed)  # dO, drawn after the workload's q, k, v
+    x["do"] = synth._cast(rng.standard_normal(tuple(x["q"].shape), dtype=np.float32), w.dtype)
+    say(f"bwd {w.name} (full tensor, stored-dS route)")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x, stored_ds=True)
+    errs = check_grads(w, x, dq, dk, dv)
+    msg = (f"workload 4 ({w.name}) backward, stored-dS route: rel-Frobenius (dq, dk, dv) = "
+           + ", ".join(f"{e:.3e}" for e in errs))
+    print(msg)
+    REPORT.append(msg)
+
+
 SHAPES = [
     (2, 2, 2, 300, 300),
     (1, 6, 2, 77, 500),
