@@ -1222,15 +1222,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_pass_kernel(BwdArgs a) {
 
 // dQ = scale dS K from the dS tiles the main loop stored (the route with neither dQ
 // atomics nor a second computation of S and dP): one workgroup per (128-row query block,
-// query head, sequence), four wavefronts of one 32-row query step each.  The key blocks
-// of the main loop that reach the workgroup's steps are walked in 64-key stages through an
-// LDS ring (direct loads): the stage's K rows, shared, and each wavefront's slice of its
-// own dS tile.  dQ^T += K^T dS^T accumulates on MFMA with both operands taken by
+// query head, sequence), four wavefronts of one 32-row query step each, two workgroups per
+// CU.  The key blocks of the main loop that reach the workgroup's steps are walked in
+// stages of 64 keys (32 at D = 256) through a double-buffered LDS ring filled by direct
+// loads: the stage's K rows, shared, and each wavefront's slice of its own dS tile.  (The
+// ring takes up to four slots; deeper rings measured slower: the compiler then waits for
+// the direct loads of the previous stage before every LDS read, as it cannot tell the
+// slots apart across stages.)  dQ^T += K^T dS^T accumulates on MFMA with both operands taken by
 // transposed LDS reads (K^T from the swizzled K rows; dS^T from the stored key rows, whose
 // 64 bytes hold the 32 query rows in the order the main loop's products produced them).
 // A wavefront skips the key blocks whose step range does not hold its step (those tiles
 // were never written).  dQ is written once: the same sum in the same order on every run.
 // Every stored dS element is read once; the pass is bound by those reads.
+
 // Wavefronts (32-row query steps) per workgroup, and keys per LDS stage (two stages,
 // double-buffered, so that two workgroups fit on a CU and one streams while the other
 // multiplies).
