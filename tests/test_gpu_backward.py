@@ -145,6 +145,21 @@ def test_workload4_backward_full():
     REPORT.append(msg)
 
 
+def test_d256_s8192_backward_full():
+    """The head-dimension-256 workload the benchmark times beside the five (B=1, H=16,
+    S=8192, D=256, bf16, causal) at full size through the stored-dS route: dQ, dK, dV of
+    every head against the oracle."""
+    w = W("fwdbwd_causal_b1_h16_s8192_d256_bf16", 1, 16, 16, 8192, 8192, 256, "bf16", True, seed=6)
+    x = synth.make_inputs(w)
+    say(f"bwd {w.name} (full tensor, stored-dS route)")
+    _, _, dq, dk, dv = run_fwd_bwd(w, x, stored_ds=True)
+    errs = check_grads(w, x, dq, dk, dv)
+    msg = (f"D=256 S=8192 ({w.name}) backward, stored-dS route: rel-Frobenius (dq, dk, dv) = "
+           + ", ".join(f"{e:.3e}" for e in errs))
+    print(msg)
+    REPORT.append(msg)
+
+
 SHAPES = [
     (2, 2, 2, 300, 300),
     (1, 6, 2, 77, 500),
